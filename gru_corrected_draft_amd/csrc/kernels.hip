@@ -1,0 +1,835 @@
+// Step kernels of the Domino draft-block rollout for gfx950.
+//
+// Method (cited by page title and section):
+//  * "Add correctness-first Domino support to DFlash V2" (sglang PR #31328),
+//    "Design": first proposal = full-vocabulary argmax of the base logits;
+//    bias-free GRU over [verified, first proposal]; one block-shared pool of
+//    K ids per request (K = 0: full vocabulary); each realised proposal is
+//    fed back before the next correction step.
+//  * "[Spec] Add Domino projector support to DFlash speculative decoding
+//    (V2)" (sglang PR #28998), "Implementation": fused SiLU(z+s)·fc2ᵀ + bias +
+//    base_logits followed by the argmax; a fused GRU cell.
+//  * "feat: support tensor-parallel Domino rollout" (sglang PR #32018),
+//    "Implementation" / "Validation and limitations": the pool is a TopK of
+//    the block's base logits whose cutoff ties the page leaves open (here:
+//    lower id wins).
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+
+template <bool BF>
+using W_t = typename std::conditional<BF, bf16_t, float>::type;
+
+// ---------------------------------------------------------------- fragments
+// Weight-side (A operand) fragment: 8 consecutive elements of one row.
+template <bool BF>
+struct WFrag;
+template <>
+struct WFrag<true> {
+  v8s f;
+  __device__ __forceinline__ void load(const bf16_t* p) { f = load_frag_bf16(p); }
+};
+template <>
+struct WFrag<false> {
+  F8 f;
+  __device__ __forceinline__ void load(const float* p) { f = load8_f32(p); }
+};
+
+// Activation (B operand) fragment of values exactly representable in the
+// weight type (embedding rows, draft hiddens).
+template <bool BF>
+struct XFrag;
+template <>
+struct XFrag<true> {
+  v8s f;
+  __device__ __forceinline__ void load(const bf16_t* p, bool ok) { f = ok ? load_frag_bf16(p) : zero_frag(); }
+};
+template <>
+struct XFrag<false> {
+  F8 f;
+  __device__ __forceinline__ void load(const float* p, bool ok) { f = ok ? load8_f32(p) : zero8(); }
+};
+
+// Activation fragment of fp32 values (GRU state, projector output).
+template <bool BF>
+struct HFrag;
+template <>
+struct HFrag<true> {
+  v8s hi, lo;
+  __device__ __forceinline__ void load(const float* p, bool ok) {
+    if (ok) {
+      split_hi_lo(load8_f32(p), hi, lo);
+    } else {
+      hi = zero_frag();
+      lo = zero_frag();
+    }
+  }
+};
+template <>
+struct HFrag<false> {
+  F8 f;
+  __device__ __forceinline__ void load(const float* p, bool ok) { f = ok ? load8_f32(p) : zero8(); }
+};
+
+__device__ __forceinline__ v4f mma(const WFrag<true>& a, const XFrag<true>& x, v4f c) {
+  return mfma_bf16(a.f, x.f, c);
+}
+__device__ __forceinline__ v4f mma(const WFrag<false>& a, const XFrag<false>& x, v4f c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c = mfma_f32(a.f.v[i], x.f.v[i], c);
+  return c;
+}
+__device__ __forceinline__ v4f mma(const WFrag<true>& a, const HFrag<true>& x, v4f c) {
+  c = mfma_bf16(a.f, x.hi, c);
+  return mfma_bf16(a.f, x.lo, c);
+}
+__device__ __forceinline__ v4f mma(const WFrag<false>& a, const HFrag<false>& x, v4f c) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c = mfma_f32(a.f.v[i], x.f.v[i], c);
+  return c;
+}
+
+template <bool BF>
+__device__ __forceinline__ float load_w(const W_t<BF>* p) {
+  if constexpr (BF) {
+    return bf16_to_f32(*p);
+  } else {
+    return *p;
+  }
+}
+
+// ---------------------------------------------------------------- reset
+__global__ void reset_kernel(uint64_t* slots, int nslots, uint32_t* hist, int nhist,
+                             uint32_t* state, int32_t* bad, int B, int K) {
+  const int stride = gridDim.x * blockDim.x;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < nhist; j += stride) hist[j] = 0;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < nslots; j += stride) slots[j] = 0;
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < B; j += stride) {
+    state[2 * j] = 0;
+    state[2 * j + 1] = (uint32_t)K;
+    bad[j] = 0;
+  }
+}
+
+void launch_reset(const Workspace& ws, int B, int K, hipStream_t st) {
+  const int nslots = DOMINO_T * B, nhist = B * 3 * 2048;
+  hipLaunchKernelGGL(reset_kernel, dim3(64), dim3(256), 0, st, ws.slots, nslots, ws.hist, nhist,
+                     ws.state, ws.bad, B, K);
+}
+
+// ------------------------------------------------------- first proposal (p1)
+// argmax over the full vocabulary of base row 0 (t = 0), one word per request
+__global__ __launch_bounds__(256) void row0_argmax_kernel(const float* __restrict__ base, int V,
+                                                          uint64_t* __restrict__ slots) {
+  const int b = blockIdx.y;
+  const float* row = base + (size_t)b * V;
+  const int v_end = min(V, (int)(blockIdx.x + 1) * 2048);
+  uint64_t best = 0;
+  for (int v = blockIdx.x * 2048 + threadIdx.x; v < v_end; v += 256)
+    best = umax64(best, pack_key(row[v], (uint32_t)v));
+  best = wave_max_u64(best);
+  __shared__ uint64_t wb[4];
+  if ((threadIdx.x & 63) == 0) wb[threadIdx.x >> 6] = best;
+  __syncthreads();
+  if (threadIdx.x == 0) publish_max(&slots[b], umax64(umax64(wb[0], wb[1]), umax64(wb[2], wb[3])));
+}
+
+void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st) {
+  hipLaunchKernelGGL(row0_argmax_kernel, dim3((s.V + 2047) / 2048, B), dim3(256), 0, st, base, s.V,
+                     slots);
+}
+
+// ---------------------------------------------------------------- pool build
+// Radix select of the K largest per-id scores score[v] = max_t base[t,b,v]
+// (as order-preserving uint32 keys) with 11 + 11 + 10 bit passes, then a
+// stable compaction in id order that takes every key above the threshold and
+// the lowest ids among keys equal to it.
+
+__device__ __forceinline__ int block_excl_scan_256(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) lds[w] = x;
+  __syncthreads();
+  int off = 0;
+  for (int i = 0; i < w; ++i) off += lds[i];
+  if (total) *total = lds[0] + lds[1] + lds[2] + lds[3];
+  __syncthreads();
+  return off + x - v;
+}
+
+__device__ __forceinline__ int block_sum_256(int v, int* lds) {
+  int t;
+  block_excl_scan_256(v, lds, &t);
+  return t;
+}
+
+__global__ __launch_bounds__(256) void pool_score_hist_kernel(const float* __restrict__ base, int V,
+                                                              int B, uint32_t* __restrict__ keys,
+                                                              uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[2048];
+  const int b = blockIdx.y;
+  for (int i = threadIdx.x; i < 2048; i += 256) h[i] = 0;
+  __syncthreads();
+  const int v0 = blockIdx.x * kPoolChunk;
+#pragma unroll
+  for (int j = 0; j < kPoolChunk / 256; ++j) {
+    const int v = v0 + j * 256 + threadIdx.x;
+    if (v < V) {
+      float sc = base[(size_t)b * V + v];
+      for (int t = 1; t < DOMINO_T; ++t) sc = fmaxf(sc, base[((size_t)t * B + b) * V + v]);
+      const uint32_t key = orderable(sc);
+      keys[(size_t)b * V + v] = key;
+      atomicAdd(&h[key >> 21], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* hh = hist + (size_t)b * 3 * 2048;
+  for (int i = threadIdx.x; i < 2048; i += 256)
+    if (h[i]) atomicAdd(&hh[i], h[i]);
+}
+
+template <int PASS>
+__global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restrict__ keys, int V,
+                                                        const uint32_t* __restrict__ state,
+                                                        uint32_t* __restrict__ hist) {
+  constexpr int NBINS = PASS == 1 ? 2048 : 1024;
+  __shared__ uint32_t h[NBINS];
+  const int b = blockIdx.y;
+  const uint32_t prefix = state[2 * b];
+  for (int i = threadIdx.x; i < NBINS; i += 256) h[i] = 0;
+  __syncthreads();
+  const int v0 = blockIdx.x * kPoolChunk;
+#pragma unroll
+  for (int j = 0; j < kPoolChunk / 256; ++j) {
+    const int v = v0 + j * 256 + threadIdx.x;
+    if (v < V) {
+      const uint32_t key = keys[(size_t)b * V + v];
+      if (PASS == 1) {
+        if ((key >> 21) == prefix) atomicAdd(&h[(key >> 10) & 2047u], 1u);
+      } else {
+        if ((key >> 10) == prefix) atomicAdd(&h[key & 1023u], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* hh = hist + ((size_t)b * 3 + PASS) * 2048;
+  for (int i = threadIdx.x; i < NBINS; i += 256)
+    if (h[i]) atomicAdd(&hh[i], h[i]);
+}
+
+// One workgroup per request: find the bin holding the remaining-th largest
+// key, extend the prefix by the bin and subtract the keys in higher bins.
+template <int PASS>
+__global__ __launch_bounds__(256) void pool_select_kernel(const uint32_t* __restrict__ hist,
+                                                          uint32_t* __restrict__ state) {
+  constexpr int NBINS = PASS < 2 ? 2048 : 1024;
+  constexpr int PER = NBINS / 256;
+  constexpr int BITS = PASS < 2 ? 11 : 10;
+  __shared__ int lds[4];
+  const int b = blockIdx.x;
+  const uint32_t prefix = state[2 * b];
+  const uint32_t need = state[2 * b + 1];
+  const uint32_t* hh = hist + ((size_t)b * 3 + PASS) * 2048;
+  // thread 0 holds the highest PER bins, thread 255 the lowest
+  const int lo_bin = NBINS - (threadIdx.x + 1) * PER;
+  uint32_t c[PER];
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    c[j] = hh[lo_bin + j];
+    tot += (int)c[j];
+  }
+  uint32_t above = (uint32_t)block_excl_scan_256(tot, lds, nullptr);
+#pragma unroll
+  for (int j = PER - 1; j >= 0; --j) {
+    if (above < need && above + c[j] >= need) {
+      state[2 * b] = (prefix << BITS) | (uint32_t)(lo_bin + j);
+      state[2 * b + 1] = need - above;
+    }
+    above += c[j];
+  }
+}
+
+__global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restrict__ keys, int V,
+                                                         const uint32_t* __restrict__ state,
+                                                         uint32_t* __restrict__ counts, int nch) {
+  __shared__ int lds[4];
+  const int b = blockIdx.y;
+  const uint32_t T = state[2 * b];
+  const int v0 = blockIdx.x * kPoolChunk;
+  int gt = 0, eq = 0;
+#pragma unroll
+  for (int j = 0; j < kPoolChunk / 256; ++j) {
+    const int v = v0 + j * 256 + threadIdx.x;
+    if (v < V) {
+      const uint32_t key = keys[(size_t)b * V + v];
+      gt += key > T;
+      eq += key == T;
+    }
+  }
+  gt = block_sum_256(gt, lds);
+  eq = block_sum_256(eq, lds);
+  if (threadIdx.x == 0) {
+    counts[((size_t)b * nch + blockIdx.x) * 2] = (uint32_t)gt;
+    counts[((size_t)b * nch + blockIdx.x) * 2 + 1] = (uint32_t)eq;
+  }
+}
+
+__global__ __launch_bounds__(256) void pool_compact_kernel(
+    const uint32_t* __restrict__ keys, const float* __restrict__ base, int V, int B, int K,
+    const uint32_t* __restrict__ state, const uint32_t* __restrict__ counts, int nch,
+    int32_t* __restrict__ pool_ids, float* __restrict__ pool_base) {
+  __shared__ int lds[4];
+  const int b = blockIdx.y, chunk = blockIdx.x;
+  const uint32_t T = state[2 * b];
+  const int need = (int)state[2 * b + 1];
+  int gt_b = 0, eq_b = 0;
+  for (int c = threadIdx.x; c < chunk; c += 256) {
+    gt_b += (int)counts[((size_t)b * nch + c) * 2];
+    eq_b += (int)counts[((size_t)b * nch + c) * 2 + 1];
+  }
+  gt_b = block_sum_256(gt_b, lds);
+  eq_b = block_sum_256(eq_b, lds);
+  // four consecutive ids per thread keep the scan order equal to id order
+  const int v0 = chunk * kPoolChunk + threadIdx.x * 4;
+  bool isgt[4], iseq[4];
+  int my_eq = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int v = v0 + j;
+    uint32_t key = 0;
+    const bool ok = v < V;
+    if (ok) key = keys[(size_t)b * V + v];
+    isgt[j] = ok && key > T;
+    iseq[j] = ok && key == T;
+    my_eq += iseq[j];
+  }
+  const int eq_before = eq_b + block_excl_scan_256(my_eq, lds, nullptr);
+  bool sel[4];
+  int my_sel = 0, e = eq_before;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    sel[j] = isgt[j] || (iseq[j] && e < need);
+    e += iseq[j];
+    my_sel += sel[j];
+  }
+  int pos = gt_b + min(eq_b, need) + block_excl_scan_256(my_sel, lds, nullptr);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (!sel[j]) continue;
+    const int v = v0 + j;
+    if (pos < K) {
+      pool_ids[(size_t)b * K + pos] = v;
+      for (int t = 1; t < DOMINO_T; ++t)
+        pool_base[((size_t)(t - 1) * B + b) * K + pos] = base[((size_t)t * B + b) * V + v];
+    }
+    ++pos;
+  }
+}
+
+void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, hipStream_t st) {
+  const int nch = (s.V + kPoolChunk - 1) / kPoolChunk;
+  const dim3 grid(nch, B), blk(256);
+  hipLaunchKernelGGL(pool_score_hist_kernel, grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
+  hipLaunchKernelGGL(pool_select_kernel<0>, dim3(B), blk, 0, st, ws.hist, ws.state);
+  hipLaunchKernelGGL(pool_hist_kernel<1>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+  hipLaunchKernelGGL(pool_select_kernel<1>, dim3(B), blk, 0, st, ws.hist, ws.state);
+  hipLaunchKernelGGL(pool_hist_kernel<2>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+  hipLaunchKernelGGL(pool_select_kernel<2>, dim3(B), blk, 0, st, ws.hist, ws.state);
+  hipLaunchKernelGGL(pool_count_kernel, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.counts, nch);
+  hipLaunchKernelGGL(pool_compact_kernel, grid, blk, 0, st, ws.keys, ws.base, s.V, B, K, ws.state,
+                     ws.counts, nch, ws.pool_ids, ws.pool_base);
+}
+
+// ---------------------------------------------------------------- GRU cell
+// One workgroup owns 16 hidden units j0..j0+15 and all B requests.  Its four
+// waves split the reduction dimension (32-wide slices, round robin); the
+// r and z gates accumulate W_ih·x and W_hh·h into one register tile, the n
+// gate keeps a_n and c_n apart.  The partial tiles meet in LDS in a fixed
+// order, so the result does not depend on scheduling.
+template <bool BF>
+struct GruArgs {
+  const W_t<BF>* E;
+  const W_t<BF>* w_ih;
+  const W_t<BF>* w_hh;
+  const float* h_in;       // nullptr: h = 0
+  float* h_out;
+  const int32_t* tok_i32;  // token of request b at tok_i32[b * tok_stride]
+  int tok_stride;
+  const uint64_t* tok_key; // or the argmax word of request b
+  int32_t* bad;
+  int B, V, e, g;
+};
+
+template <bool BF, int NB>
+__global__ __launch_bounds__(256) void gru_kernel(GruArgs<BF> a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, q = lane >> 4;
+  const int j0 = blockIdx.x * 16;
+  const int e = a.e, g = a.g;
+
+  const W_t<BF>* xrow[NB];
+  bool cv[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    const int b = cb * 16 + row;
+    cv[cb] = b < a.B;
+    int tok = 0;
+    if (cv[cb]) {
+      tok = a.tok_key ? key_id(a.tok_key[b]) : a.tok_i32[(size_t)b * a.tok_stride];
+      if (tok < 0 || tok >= a.V) {
+        a.bad[b] = 1;
+        tok = 0;
+      }
+    }
+    xrow[cb] = a.E + (size_t)tok * e + q * 8;
+  }
+
+  v4f ar[NB], az[NB], an[NB], cn[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) ar[cb] = az[cb] = an[cb] = cn[cb] = zero4();
+
+  {
+    const W_t<BF>* pr = a.w_ih + (size_t)(j0 + row) * e + q * 8;
+    const W_t<BF>* pz = pr + (size_t)g * e;
+    const W_t<BF>* pn = pz + (size_t)g * e;
+    for (int c = wave; c < e / 32; c += 4) {
+      const int k = c * 32;
+      WFrag<BF> A_r, A_z, A_n;
+      A_r.load(pr + k);
+      A_z.load(pz + k);
+      A_n.load(pn + k);
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        XFrag<BF> x;
+        x.load(xrow[cb] + k, cv[cb]);
+        ar[cb] = mma(A_r, x, ar[cb]);
+        az[cb] = mma(A_z, x, az[cb]);
+        an[cb] = mma(A_n, x, an[cb]);
+      }
+    }
+  }
+  if (a.h_in) {
+    const W_t<BF>* pr = a.w_hh + (size_t)(j0 + row) * g + q * 8;
+    const W_t<BF>* pz = pr + (size_t)g * g;
+    const W_t<BF>* pn = pz + (size_t)g * g;
+    for (int c = wave; c < g / 32; c += 4) {
+      const int k = c * 32;
+      WFrag<BF> A_r, A_z, A_n;
+      A_r.load(pr + k);
+      A_z.load(pz + k);
+      A_n.load(pn + k);
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        HFrag<BF> hf;
+        hf.load(a.h_in + (size_t)(cb * 16 + row) * g + q * 8 + k, cv[cb]);
+        ar[cb] = mma(A_r, hf, ar[cb]);
+        az[cb] = mma(A_z, hf, az[cb]);
+        cn[cb] = mma(A_n, hf, cn[cb]);
+      }
+    }
+  }
+
+  __shared__ float red[4][4][NB][256];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[wave][0][cb][i * 64 + lane] = ar[cb][i];
+      red[wave][1][cb][i * 64 + lane] = az[cb][i];
+      red[wave][2][cb][i * 64 + lane] = an[cb][i];
+      red[wave][3][cb][i * 64 + lane] = cn[cb][i];
+    }
+  __syncthreads();
+  // thread t finishes register i = t / 64 of lane l = t % 64 of every tile
+  const int l = threadIdx.x & 63, i = threadIdx.x >> 6;
+  const int j = j0 + 4 * (l >> 4) + i;
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    const int b = cb * 16 + (l & 15);
+    if (b >= a.B) continue;
+    float S[4];
+#pragma unroll
+    for (int gt = 0; gt < 4; ++gt)
+      S[gt] = ((red[0][gt][cb][threadIdx.x] + red[1][gt][cb][threadIdx.x]) +
+               red[2][gt][cb][threadIdx.x]) + red[3][gt][cb][threadIdx.x];
+    const float hold = a.h_in ? a.h_in[(size_t)b * g + j] : 0.0f;
+    const float rg = sigmoidf_(S[0]);
+    const float zg = sigmoidf_(S[1]);
+    const float ng = tanhf(S[2] + rg * S[3]);
+    a.h_out[(size_t)b * g + j] = (1.0f - zg) * ng + zg * hold;
+  }
+}
+
+template <bool BF, int NB>
+static void gru_launch(const GruArgs<BF>& a, hipStream_t st) {
+  hipLaunchKernelGGL((gru_kernel<BF, NB>), dim3(a.g / 16), dim3(256), 0, st, a);
+}
+
+template <bool BF>
+static void gru_dispatch(const GruArgs<BF>& a, hipStream_t st) {
+  switch ((a.B + 15) / 16) {
+    case 1: gru_launch<BF, 1>(a, st); break;
+    case 2: gru_launch<BF, 2>(a, st); break;
+    case 3: gru_launch<BF, 3>(a, st); break;
+    default: gru_launch<BF, 4>(a, st); break;
+  }
+}
+
+void launch_gru(const Shape& s, const DeviceWeights& w, const float* h_in, float* h_out,
+                const int32_t* tok_i32, int tok_stride, const uint64_t* tok_key, int32_t* bad,
+                int B, hipStream_t st) {
+  if (s.bf16) {
+    GruArgs<true> a{(const bf16_t*)w.embed, (const bf16_t*)w.w_ih, (const bf16_t*)w.w_hh, h_in,
+                    h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g};
+    gru_dispatch<true>(a, st);
+  } else {
+    GruArgs<false> a{(const float*)w.embed, (const float*)w.w_ih, (const float*)w.w_hh, h_in,
+                     h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g};
+    gru_dispatch<false>(a, st);
+  }
+}
+
+// ---------------------------------------------------------------- fc1 + SiLU
+// u = SiLU(fc1·h + s_step).  One workgroup per 16 projector units, waves split
+// the GRU width; bf16 models also store u as a hi/lo bf16 pair for fc2.
+template <bool BF>
+struct Fc1Args {
+  const W_t<BF>* F1;
+  const float* h;
+  const float* s;  // [B, 14, r]
+  int step;        // s row (k - 1)
+  float* u;
+  uint16_t* u_hi;
+  uint16_t* u_lo;
+  int B, g, r;
+};
+
+template <bool BF, int NB>
+__global__ __launch_bounds__(256) void fc1_kernel(Fc1Args<BF> a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, q = lane >> 4;
+  const int i0 = blockIdx.x * 16;
+  const int g = a.g, r = a.r;
+  v4f acc[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) acc[cb] = zero4();
+  const W_t<BF>* pw = a.F1 + (size_t)(i0 + row) * g + q * 8;
+  for (int c = wave; c < g / 32; c += 4) {
+    const int k = c * 32;
+    WFrag<BF> A;
+    A.load(pw + k);
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      const int b = cb * 16 + row;
+      HFrag<BF> hf;
+      hf.load(a.h + (size_t)b * g + q * 8 + k, b < a.B);
+      acc[cb] = mma(A, hf, acc[cb]);
+    }
+  }
+  __shared__ float red[4][NB][256];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][cb][i * 64 + lane] = acc[cb][i];
+  __syncthreads();
+  const int l = threadIdx.x & 63, i = threadIdx.x >> 6;
+  const int iu = i0 + 4 * (l >> 4) + i;
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    const int b = cb * 16 + (l & 15);
+    if (b >= a.B) continue;
+    const float z = ((red[0][cb][threadIdx.x] + red[1][cb][threadIdx.x]) + red[2][cb][threadIdx.x]) +
+                    red[3][cb][threadIdx.x];
+    const float v = z + a.s[((size_t)b * DOMINO_S + a.step) * r + iu];
+    const float uu = v * sigmoidf_(v);
+    a.u[(size_t)b * r + iu] = uu;
+    if (BF) {
+      const uint32_t hi = f32_to_bf16(uu);
+      a.u_hi[(size_t)b * r + iu] = (uint16_t)hi;
+      a.u_lo[(size_t)b * r + iu] = (uint16_t)f32_to_bf16(uu - bf16_to_f32(hi));
+    }
+  }
+}
+
+template <bool BF, int NB>
+static void fc1_launch(const Fc1Args<BF>& a, hipStream_t st) {
+  hipLaunchKernelGGL((fc1_kernel<BF, NB>), dim3(a.r / 16), dim3(256), 0, st, a);
+}
+template <bool BF>
+static void fc1_dispatch(const Fc1Args<BF>& a, hipStream_t st) {
+  switch ((a.B + 15) / 16) {
+    case 1: fc1_launch<BF, 1>(a, st); break;
+    case 2: fc1_launch<BF, 2>(a, st); break;
+    case 3: fc1_launch<BF, 3>(a, st); break;
+    default: fc1_launch<BF, 4>(a, st); break;
+  }
+}
+
+void launch_fc1(const Shape& s, const DeviceWeights& w, const float* h, const float* step_s,
+                int step, const Workspace& ws, int B, hipStream_t st) {
+  if (s.bf16) {
+    Fc1Args<true> a{(const bf16_t*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r};
+    fc1_dispatch<true>(a, st);
+  } else {
+    Fc1Args<false> a{(const float*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r};
+    fc1_dispatch<false>(a, st);
+  }
+}
+
+// ------------------------------------------------- correction, full vocabulary
+// y[b,c] = base[k,b,c] + (fc2[c]·u_b + b2[c]) for every vocabulary id c,
+// then the argmax per request.  Each wave streams RT tiles of 16 fc2 rows
+// once and multiplies them with all B requests' u (NB column blocks of 16).
+template <bool BF>
+struct CorrArgs {
+  const W_t<BF>* F2;
+  const W_t<BF>* b2;
+  const float* base_k;   // base row k: [B, V]
+  const float* u;
+  const uint16_t* u_hi;
+  const uint16_t* u_lo;
+  uint64_t* slot_k;      // [B]
+  int B, V, r;
+};
+
+template <bool BF>
+__device__ __forceinline__ void load_u_frag(const CorrArgs<BF>& a, int b, int k, bool ok,
+                                            HFrag<BF>& f) {
+  if constexpr (BF) {
+    const size_t off = (size_t)b * a.r + k;
+    f.hi = ok ? load_frag_bf16(a.u_hi + off) : zero_frag();
+    f.lo = ok ? load_frag_bf16(a.u_lo + off) : zero_frag();
+  } else {
+    f.f = ok ? load8_f32(a.u + (size_t)b * a.r + k) : zero8();
+  }
+}
+
+template <bool BF, int NB, int RT>
+__global__ __launch_bounds__(256) void correct_full_kernel(CorrArgs<BF> a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, q = lane >> 4;
+  const int tile0 = (blockIdx.x * 4 + wave) * RT;
+  const int V = a.V, r = a.r;
+  const bool active = tile0 * 16 < V;
+
+  uint64_t best[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) best[cb] = 0;
+
+  if (active) {
+    const W_t<BF>* pa[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int c = (tile0 + t) * 16 + row;
+      pa[t] = a.F2 + (size_t)min(c, V - 1) * r + q * 8;
+    }
+    v4f acc[RT][NB];
+#pragma unroll
+    for (int t = 0; t < RT; ++t)
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) acc[t][cb] = zero4();
+    for (int k = 0; k < r; k += 32) {
+      WFrag<BF> A[RT];
+#pragma unroll
+      for (int t = 0; t < RT; ++t) A[t].load(pa[t] + k);
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int b = cb * 16 + row;
+        HFrag<BF> uf;
+        load_u_frag<BF>(a, b, k + q * 8, b < a.B, uf);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) acc[t][cb] = mma(A[t], uf, acc[t][cb]);
+      }
+    }
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      const int b = cb * 16 + row;
+      if (b >= a.B) continue;
+      const float* brow = a.base_k + (size_t)b * V;
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = (tile0 + t) * 16 + 4 * q + i;
+          if (c < V) {
+            const float y = brow[c] + (acc[t][cb][i] + load_w<BF>(a.b2 + c));
+            best[cb] = umax64(best[cb], pack_key(y, (uint32_t)c));
+          }
+        }
+    }
+  }
+  // lanes row, row+16, row+32, row+48 hold the same column
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 16));
+    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 32));
+  }
+  __shared__ uint64_t wb[4][NB][16];
+  if (q == 0)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) wb[wave][cb][row] = best[cb];
+  __syncthreads();
+  if (threadIdx.x < NB * 16) {
+    const int cb = threadIdx.x >> 4, n = threadIdx.x & 15;
+    const int b = cb * 16 + n;
+    if (b < a.B) {
+      const uint64_t m = umax64(umax64(wb[0][cb][n], wb[1][cb][n]), umax64(wb[2][cb][n], wb[3][cb][n]));
+      publish_max(&a.slot_k[b], m);
+    }
+  }
+}
+
+constexpr int kCorrRT = 4;
+
+template <bool BF, int NB>
+static void correct_full_launch(const CorrArgs<BF>& a, hipStream_t st) {
+  const int tiles = (a.V + 15) / 16;
+  const int units = (tiles + kCorrRT - 1) / kCorrRT;
+  hipLaunchKernelGGL((correct_full_kernel<BF, NB, kCorrRT>), dim3((units + 3) / 4), dim3(256), 0,
+                     st, a);
+}
+template <bool BF>
+static void correct_full_dispatch(const CorrArgs<BF>& a, hipStream_t st) {
+  switch ((a.B + 15) / 16) {
+    case 1: correct_full_launch<BF, 1>(a, st); break;
+    case 2: correct_full_launch<BF, 2>(a, st); break;
+    case 3: correct_full_launch<BF, 3>(a, st); break;
+    default: correct_full_launch<BF, 4>(a, st); break;
+  }
+}
+
+void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
+                         hipStream_t st) {
+  const float* base_k = ws.base + (size_t)k * B * s.V;
+  uint64_t* slot_k = ws.slots + (size_t)k * B;
+  if (s.bf16) {
+    CorrArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, base_k, ws.u, ws.u_hi, ws.u_lo,
+                     slot_k, B, s.V, s.r};
+    correct_full_dispatch<true>(a, st);
+  } else {
+    CorrArgs<false> a{(const float*)w.fc2, (const float*)w.fc2_b, base_k, ws.u, ws.u_hi, ws.u_lo,
+                      slot_k, B, s.V, s.r};
+    correct_full_dispatch<false>(a, st);
+  }
+}
+
+// ------------------------------------------------------ correction, pool
+// Per request, 16 gathered fc2 rows form the A tile; u_b sits in column 0
+// (bf16 models: hi in column 0, lo in column 1) of the B tile.
+template <bool BF>
+struct PoolArgs {
+  const W_t<BF>* F2;
+  const W_t<BF>* b2;
+  const float* pool_base_k;  // [B, K] base logits of step k at the pool ids
+  const int32_t* pool_ids;   // [B, K]
+  const float* u;
+  const uint16_t* u_hi;
+  const uint16_t* u_lo;
+  uint64_t* slot_k;
+  int B, K, r, V, units_per_req;
+};
+
+template <bool BF, int RT>
+__global__ __launch_bounds__(256) void correct_pool_kernel(PoolArgs<BF> a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, q = lane >> 4;
+  const int unit = blockIdx.x * 4 + wave;
+  const int b = unit / a.units_per_req;
+  if (b >= a.B) return;  // no workgroup barrier below
+  const int tile0 = (unit % a.units_per_req) * RT;
+  const int K = a.K, r = a.r;
+  const int32_t* ids = a.pool_ids + (size_t)b * K;
+
+  const W_t<BF>* pa[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) {
+    const int i = (tile0 + t) * 16 + row;
+    const int id = min(max(ids[min(i, K - 1)], 0), a.V - 1);  // ids are in range by construction
+    pa[t] = a.F2 + (size_t)id * r + q * 8;
+  }
+  v4f acc[RT];
+#pragma unroll
+  for (int t = 0; t < RT; ++t) acc[t] = zero4();
+  for (int k = 0; k < r; k += 32) {
+    WFrag<BF> A[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) A[t].load(pa[t] + k);
+    HFrag<BF> uf;
+    if constexpr (BF) {
+      const size_t off = (size_t)b * r + k + q * 8;
+      uf.hi = row == 0 ? load_frag_bf16(a.u_hi + off) : (row == 1 ? load_frag_bf16(a.u_lo + off) : zero_frag());
+      uf.lo = zero_frag();
+      // one product per tile: the lo half rides in column 1
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t] = mfma_bf16(A[t].f, uf.hi, acc[t]);
+    } else {
+      uf.f = row == 0 ? load8_f32(a.u + (size_t)b * r + k + q * 8) : zero8();
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t] = mma(A[t], uf, acc[t]);
+    }
+  }
+  uint64_t best = 0;
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float dot = acc[t][i];
+      if (BF) dot += __shfl_down(acc[t][i], 1, 64);  // column 1 (lo) of the same row
+      const int idx = (tile0 + t) * 16 + 4 * q + i;
+      if (row == 0 && idx < K) {
+        const int id = min(max(ids[idx], 0), a.V - 1);
+        const float y = a.pool_base_k[(size_t)b * K + idx] + (dot + load_w<BF>(a.b2 + id));
+        best = umax64(best, pack_key(y, (uint32_t)id));
+      }
+    }
+  best = wave_max_u64(best);
+  if (lane == 0) publish_max(&a.slot_k[b], best);
+}
+
+constexpr int kPoolRT = 2;
+
+void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
+                         int K, hipStream_t st) {
+  const int tiles = (K + 15) / 16;
+  const int upr = (tiles + kPoolRT - 1) / kPoolRT;
+  const int units = upr * B;
+  const dim3 grid((units + 3) / 4);
+  const float* pb = ws.pool_base + (size_t)(k - 1) * B * K;
+  uint64_t* slot_k = ws.slots + (size_t)k * B;
+  if (s.bf16) {
+    PoolArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,
+                     ws.u_lo, slot_k, B, K, s.r, s.V, upr};
+    hipLaunchKernelGGL((correct_pool_kernel<true, kPoolRT>), grid, dim3(256), 0, st, a);
+  } else {
+    PoolArgs<false> a{(const float*)w.fc2, (const float*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,
+                      ws.u_lo, slot_k, B, K, s.r, s.V, upr};
+    hipLaunchKernelGGL((correct_pool_kernel<false, kPoolRT>), grid, dim3(256), 0, st, a);
+  }
+}
+
+// ---------------------------------------------------------------- outputs
+__global__ void writeout_kernel(const uint64_t* __restrict__ slots, const int32_t* __restrict__ bad,
+                                int B, int32_t* __restrict__ out_tokens,
+                                float* __restrict__ out_top1) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * DOMINO_T) return;
+  const int b = idx / DOMINO_T, k = idx % DOMINO_T;
+  const uint64_t key = slots[(size_t)k * B + b];
+  const bool invalid = bad[b] != 0 || key == 0;
+  out_tokens[idx] = invalid ? -1 : key_id(key);
+  if (out_top1) out_top1[idx] = invalid ? __builtin_nanf("") : key_value(key);
+}
+
+void launch_writeout(const Workspace& ws, int B, int32_t* out_tokens, float* out_top1,
+                     hipStream_t st) {
+  const int n = B * DOMINO_T;
+  hipLaunchKernelGGL(writeout_kernel, dim3((n + 255) / 256), dim3(256), 0, st, ws.slots, ws.bad, B,
+                     out_tokens, out_top1);
+}

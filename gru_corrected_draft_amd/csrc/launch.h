@@ -1,0 +1,57 @@
+// Host-side launchers of the rollout kernels (internal interface between the
+// orchestration in rollout.hip and the kernels in kernels.hip / lmhead.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+struct DeviceWeights {
+  const void* lm_head;
+  const void* embed;
+  const void* w_ih;
+  const void* w_hh;
+  const void* fc1;
+  const void* fc2;
+  const void* fc2_b;
+};
+
+struct Shape {
+  int V, H, e, g, r;
+  bool bf16;
+};
+
+// workspace buffers of one handle
+struct Workspace {
+  float* base;         // [15, Bmax, V] step-major base logits
+  uint32_t* keys;      // [Bmax, V] orderable pool scores
+  uint32_t* hist;      // [Bmax, 3, 2048] radix histograms
+  uint32_t* state;     // [Bmax, 2] (prefix, remaining count)
+  uint32_t* counts;    // [Bmax, nchunks, 2] (greater, equal) per chunk
+  int32_t* pool_ids;   // [Bmax, Kmax]
+  float* pool_base;    // [14, Bmax, Kmax]
+  float* h[2];         // [Bmax, g] ping-pong GRU state
+  float* u;            // [Bmax, r]
+  uint16_t* u_hi;      // [Bmax, r]
+  uint16_t* u_lo;      // [Bmax, r]
+  uint64_t* slots;     // [15, Bmax] argmax words
+  int32_t* bad;        // [Bmax]
+};
+
+constexpr int kPoolChunk = 1024;
+
+void lmhead_prepare();  // once per process: raise the tiled kernel's LDS limit
+void launch_reset(const Workspace& ws, int B, int K, hipStream_t st);
+void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int B, hipStream_t st);
+void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st);
+void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, hipStream_t st);
+// token source: exactly one of tok_i32 (element b*stride) or tok_key (argmax word b)
+void launch_gru(const Shape& s, const DeviceWeights& w, const float* h_in, float* h_out,
+                const int32_t* tok_i32, int tok_stride, const uint64_t* tok_key, int32_t* bad,
+                int B, hipStream_t st);
+void launch_fc1(const Shape& s, const DeviceWeights& w, const float* h, const float* step_s,
+                int step, const Workspace& ws, int B, hipStream_t st);
+void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
+                         hipStream_t st);
+void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
+                         int K, hipStream_t st);
+void launch_writeout(const Workspace& ws, int B, int32_t* out_tokens, float* out_top1,
+                     hipStream_t st);

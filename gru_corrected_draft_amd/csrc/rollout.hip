@@ -1,0 +1,380 @@
+// C ABI of the Domino draft-block rollout: validation, workspace, launch
+// order, graph cache.  The order of work follows "Add correctness-first
+// Domino support to DFlash V2" (sglang PR #31328), "Design":
+//   base logits (once per block) -> p1 = full-vocabulary argmax
+//   -> [pool of K ids]  -> GRU(verified) -> GRU(p1)
+//   -> 14 x { u = SiLU(fc1 h + s) ; corrected argmax ; GRU(new token) }
+// with no GRU update after the last step (2 prefix + 13 feedback updates).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/domino_rollout.h"
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+std::mutex g_err_mu;
+std::string g_err;  // last create() failure
+
+void set_global_err(const std::string& s) {
+  std::lock_guard<std::mutex> lk(g_err_mu);
+  g_err = s;
+}
+
+struct GraphKey {
+  int B, K, forced;
+  const void* p[6];
+  bool operator==(const GraphKey& o) const {
+    if (B != o.B || K != o.K || forced != o.forced) return false;
+    for (int i = 0; i < 6; ++i)
+      if (p[i] != o.p[i]) return false;
+    return true;
+  }
+};
+
+struct GraphEntry {
+  GraphKey key;
+  hipGraphExec_t exec;
+};
+
+}  // namespace
+
+struct domino_rollout {
+  domino_config_t cfg;
+  DeviceWeights w;
+  Shape shape;
+  int device;
+  Workspace ws;
+  std::vector<void*> allocations;
+  std::vector<GraphEntry> graphs;
+  hipStream_t capture_stream = nullptr;
+  int last_B = 0, last_K = 0;  // shape of the last enqueued run
+  std::string err;
+
+  domino_status_t fail(domino_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    err = buf;
+    return st;
+  }
+};
+
+static domino_status_t validate_config(const domino_config_t* c, std::string& why) {
+  char buf[256];
+  auto bad = [&](const char* msg) {
+    why = msg;
+    return DOMINO_ERR_INVALID_CONFIG;
+  };
+  if (c->vocab <= 0 || c->hidden <= 0 || c->emb_dim <= 0 || c->gru_hidden <= 0 || c->proj_dim <= 0)
+    return bad("vocab, hidden, emb_dim, gru_hidden and proj_dim must be positive");
+  if (c->block_size != 16) {
+    snprintf(buf, sizeof buf, "block_size must be 16 (got %d)", c->block_size);
+    return bad(buf);
+  }
+  if (c->pure_draft_prefix_len != 1) {
+    snprintf(buf, sizeof buf, "pure_draft_prefix_len must be 1 (got %d)", c->pure_draft_prefix_len);
+    return bad(buf);
+  }
+  if (c->max_batch < 1 || c->max_batch > 64) return bad("max_batch must be in [1, 64]");
+  if (c->max_k < 0) return bad("max_k must be >= 0");
+  if (c->dtype != DOMINO_DTYPE_BF16 && c->dtype != DOMINO_DTYPE_FP32)
+    return bad("dtype must be DOMINO_DTYPE_BF16 or DOMINO_DTYPE_FP32");
+  if (c->hidden % 64 || c->emb_dim % 32 || c->gru_hidden % 32 || c->proj_dim % 32) {
+    why = "hidden must be a multiple of 64 and emb_dim, gru_hidden, proj_dim multiples of 32";
+    return DOMINO_ERR_UNSUPPORTED;
+  }
+  if ((long long)DOMINO_T * c->max_batch * (long long)c->vocab > (1LL << 31) - 1 ||
+      (long long)c->vocab * c->hidden > (1LL << 40)) {
+    why = "shape too large";
+    return DOMINO_ERR_UNSUPPORTED;
+  }
+  return DOMINO_OK;
+}
+
+extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
+                                                 const domino_weights_t* w,
+                                                 domino_rollout_t** out) {
+  if (!out) {
+    set_global_err("create: out is NULL");
+    return DOMINO_ERR_INVALID_ARG;
+  }
+  *out = nullptr;
+  if (!cfg || !w) {
+    set_global_err("create: cfg or weights is NULL");
+    return DOMINO_ERR_INVALID_ARG;
+  }
+  std::string why;
+  domino_status_t st = validate_config(cfg, why);
+  if (st != DOMINO_OK) {
+    set_global_err("create: " + why);
+    return st;
+  }
+  const void* wp[7] = {w->lm_head, w->embed, w->gru_w_ih, w->gru_w_hh, w->fc1_w, w->fc2_w, w->fc2_b};
+  for (int i = 0; i < 7; ++i) {
+    if (!wp[i]) {
+      set_global_err("create: a weight pointer is NULL");
+      return DOMINO_ERR_INVALID_ARG;
+    }
+    if (i < 6 && ((uintptr_t)wp[i] & 15)) {
+      set_global_err("create: weight matrices must be 16-byte aligned");
+      return DOMINO_ERR_INVALID_ARG;
+    }
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    set_global_err("create: no HIP device");
+    return DOMINO_ERR_UNSUPPORTED;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+    set_global_err("create: hipGetDeviceProperties failed");
+    return DOMINO_ERR_HIP;
+  }
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    set_global_err(std::string("create: device is ") + prop.gcnArchName + ", this build needs gfx950");
+    return DOMINO_ERR_UNSUPPORTED;
+  }
+
+  domino_rollout* h = new domino_rollout();
+  h->cfg = *cfg;
+  h->w = DeviceWeights{w->lm_head, w->embed, w->gru_w_ih, w->gru_w_hh, w->fc1_w, w->fc2_w, w->fc2_b};
+  h->shape = Shape{cfg->vocab, cfg->hidden, cfg->emb_dim, cfg->gru_hidden, cfg->proj_dim,
+                   cfg->dtype == DOMINO_DTYPE_BF16};
+  h->device = dev;
+
+  const size_t V = cfg->vocab, Bm = cfg->max_batch, Km = cfg->max_k > 0 ? cfg->max_k : 1;
+  const size_t g = cfg->gru_hidden, r = cfg->proj_dim;
+  const size_t nch = (V + kPoolChunk - 1) / kPoolChunk;
+  auto alloc = [&](size_t bytes) -> void* {
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes < 256 ? 256 : bytes) != hipSuccess) return nullptr;
+    h->allocations.push_back(p);
+    return p;
+  };
+  Workspace& ws = h->ws;
+  ws.base = (float*)alloc(DOMINO_T * Bm * V * 4);
+  ws.keys = (uint32_t*)alloc(Bm * V * 4);
+  ws.hist = (uint32_t*)alloc(Bm * 3 * 2048 * 4);
+  ws.state = (uint32_t*)alloc(Bm * 2 * 4);
+  ws.counts = (uint32_t*)alloc(Bm * nch * 2 * 4);
+  ws.pool_ids = (int32_t*)alloc(Bm * Km * 4);
+  ws.pool_base = (float*)alloc(DOMINO_S * Bm * Km * 4);
+  ws.h[0] = (float*)alloc(Bm * g * 4);
+  ws.h[1] = (float*)alloc(Bm * g * 4);
+  ws.u = (float*)alloc(Bm * r * 4);
+  ws.u_hi = (uint16_t*)alloc(Bm * r * 2);
+  ws.u_lo = (uint16_t*)alloc(Bm * r * 2);
+  ws.slots = (uint64_t*)alloc(DOMINO_T * Bm * 8);
+  ws.bad = (int32_t*)alloc(Bm * 4);
+  for (void* p : {(void*)ws.base, (void*)ws.keys, (void*)ws.hist, (void*)ws.state, (void*)ws.counts,
+                  (void*)ws.pool_ids, (void*)ws.pool_base, (void*)ws.h[0], (void*)ws.h[1],
+                  (void*)ws.u, (void*)ws.u_hi, (void*)ws.u_lo, (void*)ws.slots, (void*)ws.bad}) {
+    if (!p) {
+      set_global_err("create: workspace allocation failed");
+      domino_rollout_destroy(h);
+      return DOMINO_ERR_OUT_OF_MEMORY;
+    }
+  }
+  // every buffer starts defined; the pool ids in particular are always valid rows
+  for (size_t i = 0; i < h->allocations.size(); ++i) {
+    if (hipMemset(h->allocations[i], 0, 256) != hipSuccess) break;
+  }
+  if (hipMemset(ws.pool_ids, 0, Bm * Km * 4) != hipSuccess ||
+      hipMemset(ws.base, 0, DOMINO_T * Bm * V * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    set_global_err("create: workspace initialisation failed");
+    domino_rollout_destroy(h);
+    return DOMINO_ERR_HIP;
+  }
+  static std::once_flag once;
+  std::call_once(once, lmhead_prepare);
+  *out = h;
+  return DOMINO_OK;
+}
+
+extern "C" void domino_rollout_destroy(domino_rollout_t* h) {
+  if (!h) return;
+  for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);
+  if (h->capture_stream) (void)hipStreamDestroy(h->capture_stream);
+  for (void* p : h->allocations) (void)hipFree(p);
+  delete h;
+}
+
+extern "C" const char* domino_rollout_last_error(const domino_rollout_t* h) {
+  if (h) return h->err.c_str();
+  std::lock_guard<std::mutex> lk(g_err_mu);
+  static thread_local std::string copy;
+  copy = g_err;
+  return copy.c_str();
+}
+
+// Host-side checks only: nothing is read from the device.
+static domino_status_t check_run_args(domino_rollout_t* h, const void* hidden, const float* s,
+                                      const int32_t* ver, int32_t B, int32_t K, int32_t* out_tokens) {
+  if (!h) return DOMINO_ERR_INVALID_ARG;
+  if (!hidden || !s || !ver || !out_tokens)
+    return h->fail(DOMINO_ERR_INVALID_ARG, "run: hidden, step_s, verified_tokens and out_tokens must be non-NULL");
+  if (((uintptr_t)hidden & 15) || ((uintptr_t)s & 3))
+    return h->fail(DOMINO_ERR_INVALID_ARG, "run: base_hidden must be 16-byte aligned");
+  if (B < 1 || B > h->cfg.max_batch)
+    return h->fail(DOMINO_ERR_INVALID_ARG, "run: batch %d outside [1, %d]", B, h->cfg.max_batch);
+  if (K < 0) return h->fail(DOMINO_ERR_INVALID_ARG, "run: K must be >= 0 (got %d)", K);
+  if (K > 0 && K < h->cfg.vocab && K > h->cfg.max_k)
+    return h->fail(DOMINO_ERR_INVALID_ARG, "run: pool size K=%d exceeds max_k=%d", K, h->cfg.max_k);
+  return DOMINO_OK;
+}
+
+static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, const int32_t* ver,
+                    const int32_t* forced, int B, int K, int32_t* out_tokens, float* out_top1,
+                    hipStream_t st) {
+  const Shape& sh = h->shape;
+  const Workspace& ws = h->ws;
+  const bool pool = K > 0 && K < sh.V;
+  h->last_B = B;
+  h->last_K = pool ? K : 0;
+  launch_reset(ws, B, pool ? K : 0, st);
+  launch_lmhead(sh, h->w.lm_head, hidden, ws.base, B, st);
+  launch_row0_argmax(sh, ws.base, B, ws.slots, st);
+  if (pool) launch_pool_build(sh, ws, B, K, st);
+  // two-token prefix: h = GRU(E[verified], 0); h = GRU(E[p1], h)
+  launch_gru(sh, h->w, nullptr, ws.h[0], ver, 1, nullptr, ws.bad, B, st);
+  if (forced)
+    launch_gru(sh, h->w, ws.h[0], ws.h[1], forced, DOMINO_T, nullptr, ws.bad, B, st);
+  else
+    launch_gru(sh, h->w, ws.h[0], ws.h[1], nullptr, 0, ws.slots, ws.bad, B, st);
+  int cur = 1;
+  for (int k = 1; k <= DOMINO_S; ++k) {
+    launch_fc1(sh, h->w, ws.h[cur], s, k - 1, ws, B, st);
+    if (pool)
+      launch_correct_pool(sh, h->w, ws, k, B, K, st);
+    else
+      launch_correct_full(sh, h->w, ws, k, B, st);
+    if (k < DOMINO_S) {
+      if (forced)
+        launch_gru(sh, h->w, ws.h[cur], ws.h[cur ^ 1], forced + k, DOMINO_T, nullptr, ws.bad, B, st);
+      else
+        launch_gru(sh, h->w, ws.h[cur], ws.h[cur ^ 1], nullptr, 0, ws.slots + (size_t)k * B, ws.bad,
+                   B, st);
+      cur ^= 1;
+    }
+  }
+  launch_writeout(ws, B, out_tokens, out_top1, st);
+}
+
+namespace {
+struct DeviceGuard {
+  int prev = -1, want;
+  explicit DeviceGuard(int d) : want(d) {
+    if (hipGetDevice(&prev) == hipSuccess && prev != want) (void)hipSetDevice(want);
+  }
+  ~DeviceGuard() {
+    if (prev >= 0 && prev != want) (void)hipSetDevice(prev);
+  }
+};
+}  // namespace
+
+static domino_status_t run_common(domino_rollout_t* h, const void* hidden, const float* s,
+                                  const int32_t* ver, const int32_t* forced, int32_t B, int32_t K,
+                                  int32_t* out_tokens, float* out_top1, void* stream) {
+  domino_status_t st = check_run_args(h, hidden, s, ver, B, K, out_tokens);
+  if (st != DOMINO_OK) return st;
+  DeviceGuard dg(h->device);
+  (void)hipGetLastError();  // clear a stale error of an unrelated call
+  enqueue(h, hidden, s, ver, forced, B, K, out_tokens, out_top1, (hipStream_t)stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return h->fail(DOMINO_ERR_HIP, "run: kernel launch failed: %s", hipGetErrorString(e));
+  h->err.clear();
+  return DOMINO_OK;
+}
+
+extern "C" domino_status_t domino_rollout_run(domino_rollout_t* h, const void* base_hidden,
+                                              const float* step_s, const int32_t* verified_tokens,
+                                              int32_t batch, int32_t K, int32_t* out_tokens,
+                                              float* out_top1_logit, void* stream) {
+  return run_common(h, base_hidden, step_s, verified_tokens, nullptr, batch, K, out_tokens,
+                    out_top1_logit, stream);
+}
+
+extern "C" domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const void* base_hidden,
+                                                     const float* step_s,
+                                                     const int32_t* verified_tokens,
+                                                     const int32_t* forced_tokens, int32_t batch,
+                                                     int32_t K, int32_t* out_tokens,
+                                                     float* out_top1_logit, void* stream) {
+  if (h && !forced_tokens) return h->fail(DOMINO_ERR_INVALID_ARG, "run_forced: forced_tokens is NULL");
+  return run_common(h, base_hidden, step_s, verified_tokens, forced_tokens, batch, K, out_tokens,
+                    out_top1_logit, stream);
+}
+
+extern "C" domino_status_t domino_rollout_run_graph(domino_rollout_t* h, const void* base_hidden,
+                                                    const float* step_s,
+                                                    const int32_t* verified_tokens, int32_t batch,
+                                                    int32_t K, int32_t* out_tokens,
+                                                    float* out_top1_logit, void* stream) {
+  domino_status_t st = check_run_args(h, base_hidden, step_s, verified_tokens, batch, K, out_tokens);
+  if (st != DOMINO_OK) return st;
+  DeviceGuard dg(h->device);
+  const int kmode = (K > 0 && K < h->cfg.vocab) ? K : 0;
+  GraphKey key{batch, kmode, 0, {base_hidden, step_s, verified_tokens, out_tokens, out_top1_logit, nullptr}};
+  hipGraphExec_t exec = nullptr;
+  for (auto& g : h->graphs)
+    if (g.key == key) exec = g.exec;
+  if (!exec) {
+    if (!h->capture_stream &&
+        hipStreamCreateWithFlags(&h->capture_stream, hipStreamNonBlocking) != hipSuccess)
+      return h->fail(DOMINO_ERR_HIP, "run_graph: stream creation failed");
+    (void)hipGetLastError();
+    hipGraph_t graph = nullptr;
+    if (hipStreamBeginCapture(h->capture_stream, hipStreamCaptureModeRelaxed) != hipSuccess)
+      return h->fail(DOMINO_ERR_HIP, "run_graph: begin capture failed");
+    enqueue(h, base_hidden, step_s, verified_tokens, nullptr, batch, kmode, out_tokens,
+            out_top1_logit, h->capture_stream);
+    hipError_t e1 = hipGetLastError();
+    hipError_t e2 = hipStreamEndCapture(h->capture_stream, &graph);
+    if (e1 != hipSuccess || e2 != hipSuccess || !graph) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return h->fail(DOMINO_ERR_HIP, "run_graph: capture failed: %s",
+                     hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+    }
+    hipError_t e3 = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (e3 != hipSuccess) return h->fail(DOMINO_ERR_HIP, "run_graph: instantiate failed: %s", hipGetErrorString(e3));
+    h->graphs.push_back(GraphEntry{key, exec});
+  }
+  hipError_t e = hipGraphLaunch(exec, (hipStream_t)stream);
+  if (e != hipSuccess) return h->fail(DOMINO_ERR_HIP, "run_graph: launch failed: %s", hipGetErrorString(e));
+  h->err.clear();
+  return DOMINO_OK;
+}
+
+extern "C" domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t which,
+                                                         void* dst, size_t dst_bytes, size_t* bytes,
+                                                         void* stream) {
+  if (!h || !bytes || h->last_B <= 0) return DOMINO_ERR_INVALID_ARG;
+  const void* src = nullptr;
+  size_t n = 0;
+  if (which == 0) {
+    src = h->ws.base;
+    n = (size_t)DOMINO_T * h->last_B * h->cfg.vocab * 4;
+  } else if (which == 1 && h->last_K > 0) {
+    src = h->ws.pool_ids;
+    n = (size_t)h->last_B * h->last_K * 4;
+  } else {
+    return DOMINO_ERR_INVALID_ARG;
+  }
+  *bytes = n;
+  if (!dst) return DOMINO_OK;
+  if (dst_bytes < n) return DOMINO_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  if (hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, (hipStream_t)stream) != hipSuccess)
+    return DOMINO_ERR_HIP;
+  return DOMINO_OK;
+}

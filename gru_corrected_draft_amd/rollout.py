@@ -1,0 +1,222 @@
+"""Thin ctypes binding of ``libdomino_rollout.so``.
+
+Argument marshalling only: every step of the rollout runs in the library's
+HIP kernels.  PyTorch supplies device memory (``tensor.data_ptr()``) and the
+stream (``torch.cuda.current_stream().cuda_stream``).  The library must be
+built (``python -m gru_corrected_draft_amd.build``); importing this module
+without it raises, there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdomino_rollout.so")
+
+DOMINO_OK = 0
+DOMINO_ERR_INVALID_ARG = -1
+DOMINO_ERR_INVALID_CONFIG = -2
+DOMINO_ERR_UNSUPPORTED = -3
+DOMINO_ERR_OUT_OF_MEMORY = -4
+DOMINO_ERR_HIP = -5
+DTYPE_BF16, DTYPE_FP32 = 0, 1
+
+BLOCK_SIZE = 16
+N_PROPOSALS = 15
+N_STEPS = 14
+
+EXPORTED = ("domino_rollout_create", "domino_rollout_run", "domino_rollout_run_graph",
+            "domino_rollout_run_forced", "domino_rollout_read_workspace", "domino_rollout_destroy",
+            "domino_rollout_last_error")
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("vocab", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("emb_dim", ctypes.c_int32), ("gru_hidden", ctypes.c_int32),
+                ("proj_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("pure_draft_prefix_len", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("max_k", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class WeightPtrs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("lm_head", "embed", "gru_w_ih", "gru_w_hh", "fc1_w", "fc2_w", "fc2_b")]
+
+
+WEIGHT_NAMES = [n for n, _ in WeightPtrs._fields_]
+
+_lib = None
+
+
+def load_library():
+    """Load the in-tree library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    # torch first: its bundled HIP runtime carries the same soname, so the
+    # library binds to that one copy instead of loading a second runtime
+    import torch  # noqa: F401
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m gru_corrected_draft_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i32p, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p
+    lib.domino_rollout_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(WeightPtrs),
+                                          ctypes.POINTER(vp)]
+    lib.domino_rollout_create.restype = ctypes.c_int
+    run_args = [vp, vp, f32p, i32p, i32, i32, i32p, f32p, vp]
+    lib.domino_rollout_run.argtypes = run_args
+    lib.domino_rollout_run.restype = ctypes.c_int
+    lib.domino_rollout_run_graph.argtypes = run_args
+    lib.domino_rollout_run_graph.restype = ctypes.c_int
+    lib.domino_rollout_run_forced.argtypes = [vp, vp, f32p, i32p, i32p, i32, i32, i32p, f32p, vp]
+    lib.domino_rollout_run_forced.restype = ctypes.c_int
+    lib.domino_rollout_read_workspace.argtypes = [vp, i32, vp, ctypes.c_size_t,
+                                                  ctypes.POINTER(ctypes.c_size_t), vp]
+    lib.domino_rollout_read_workspace.restype = ctypes.c_int
+    lib.domino_rollout_destroy.argtypes = [vp]
+    lib.domino_rollout_destroy.restype = None
+    lib.domino_rollout_last_error.argtypes = [vp]
+    lib.domino_rollout_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+class DominoError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"status {status}: {msg}")
+        self.status = status
+
+
+def make_config(vocab, hidden, emb_dim, gru_hidden, proj_dim, max_batch, max_k, dtype,
+                block_size=BLOCK_SIZE, pure_draft_prefix_len=1):
+    return Config(vocab, hidden, emb_dim, gru_hidden, proj_dim, block_size,
+                  pure_draft_prefix_len, max_batch, max_k, dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+class DominoRollout:
+    """Handle over ``domino_rollout_t``.  ``weights`` maps the names of
+    ``WEIGHT_NAMES`` to contiguous device tensors (bfloat16 or float32); the
+    tensors are kept alive by this object because the library borrows them."""
+
+    def __init__(self, weights: dict, max_batch: int, max_k: int):
+        import torch
+        self.lib = load_library()
+        lm = weights["lm_head"]
+        dt = lm.dtype
+        if dt not in (torch.bfloat16, torch.float32):
+            raise TypeError("weights must be bfloat16 or float32")
+        for n in WEIGHT_NAMES:
+            t = weights[n]
+            if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
+                raise TypeError(f"weight {n} must be a contiguous {dt} device tensor")
+        V, H = lm.shape
+        e = weights["embed"].shape[1]
+        g = weights["gru_w_hh"].shape[1]
+        r = weights["fc1_w"].shape[0]
+        self.dtype = dt
+        self.shape = (V, H, e, g, r)
+        self.cfg = make_config(V, H, e, g, r, max_batch, max_k,
+                               DTYPE_BF16 if dt == torch.bfloat16 else DTYPE_FP32)
+        self._weights = dict(weights)
+        wp = WeightPtrs(*[weights[n].data_ptr() for n in WEIGHT_NAMES])
+        h = ctypes.c_void_p()
+        st = self.lib.domino_rollout_create(ctypes.byref(self.cfg), ctypes.byref(wp), ctypes.byref(h))
+        if st != DOMINO_OK:
+            raise DominoError(st, self.lib.domino_rollout_last_error(None).decode())
+        self.handle = h
+
+    def _check(self, st):
+        if st != DOMINO_OK:
+            raise DominoError(st, self.lib.domino_rollout_last_error(self.handle).decode())
+
+    def run(self, hidden, step_s, verified, K, out_tokens=None, out_top1=None, graph=False,
+            forced=None, stream=None):
+        """Enqueue one rollout; returns (out_tokens [B,15] int32, out_top1 [B,15] fp32)."""
+        import torch
+        B = hidden.shape[0]
+        V, H, e, g, r = self.shape
+        if hidden.shape != (B, N_PROPOSALS, H) or hidden.dtype != self.dtype:
+            raise ValueError("hidden must be [B, 15, H] in the weights' dtype")
+        if step_s.shape != (B, N_STEPS, r) or step_s.dtype != torch.float32:
+            raise ValueError("step_s must be [B, 14, r] float32")
+        if verified.shape != (B,) or verified.dtype != torch.int32:
+            raise ValueError("verified must be [B] int32")
+        for t in (hidden, step_s, verified):
+            if not t.is_cuda or not t.is_contiguous():
+                raise ValueError("inputs must be contiguous device tensors")
+        dev = hidden.device
+        if out_tokens is None:
+            out_tokens = torch.empty((B, N_PROPOSALS), dtype=torch.int32, device=dev)
+        if out_top1 is None:
+            out_top1 = torch.empty((B, N_PROPOSALS), dtype=torch.float32, device=dev)
+        st_ptr = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream if stream is None
+                                 else stream)
+        if forced is not None:
+            if forced.shape != (B, N_PROPOSALS) or forced.dtype != torch.int32 or not forced.is_cuda:
+                raise ValueError("forced must be [B, 15] int32 on the device")
+            st = self.lib.domino_rollout_run_forced(self.handle, _ptr(hidden), _ptr(step_s),
+                                                    _ptr(verified), _ptr(forced), B, K,
+                                                    _ptr(out_tokens), _ptr(out_top1), st_ptr)
+        else:
+            fn = self.lib.domino_rollout_run_graph if graph else self.lib.domino_rollout_run
+            st = fn(self.handle, _ptr(hidden), _ptr(step_s), _ptr(verified), B, K,
+                    _ptr(out_tokens), _ptr(out_top1), st_ptr)
+        self._check(st)
+        return out_tokens, out_top1
+
+    def read_workspace(self, which):
+        """Copy of a workspace buffer of the last run: 0 = base logits
+        [15, B, V] fp32 (step-major), 1 = pool ids [B, K] int32."""
+        import torch
+        n = ctypes.c_size_t()
+        self._check(self.lib.domino_rollout_read_workspace(self.handle, which, None, 0,
+                                                           ctypes.byref(n), None))
+        dt = torch.float32 if which == 0 else torch.int32
+        out = torch.empty(n.value // 4, dtype=dt, device="cuda")
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self._check(self.lib.domino_rollout_read_workspace(self.handle, which, _ptr(out), n.value,
+                                                           ctypes.byref(n), st))
+        return out
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.domino_rollout_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def device_weights(w, device="cuda"):
+    """Upload a ``synth.Weights`` set: bf16 bit patterns -> torch.bfloat16."""
+    import numpy as np
+    import torch
+    out = {}
+    for n in WEIGHT_NAMES:
+        a = w.raw[n]
+        if a.dtype == np.uint16:
+            t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(np.ascontiguousarray(a, np.float32))
+        out[n] = t.to(device).contiguous()
+    return out
+
+
+def device_inputs(inp, device="cuda"):
+    import numpy as np
+    import torch
+    h = inp.hidden
+    if h.dtype == np.uint16:
+        hid = torch.from_numpy(h.view(np.int16)).view(torch.bfloat16)
+    else:
+        hid = torch.from_numpy(h)
+    return (hid.to(device).contiguous(), torch.from_numpy(inp.step_s).to(device).contiguous(),
+            torch.from_numpy(inp.verified).to(device).contiguous())

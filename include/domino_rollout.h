@@ -1,0 +1,160 @@
+/*
+ * domino_rollout.h — C ABI of the MI355X (gfx950) Domino draft-block rollout.
+ *
+ * What is computed (sources cited by page title and section):
+ *   "Add correctness-first Domino support to DFlash V2" (sglang PR #31328),
+ *   section "Design": for a draft block of 16 positions the rollout emits 15
+ *   proposals per request.  Proposal 1 is the full-vocabulary argmax of the
+ *   base LM-head logits; a bias-free GRU is seeded with
+ *   [verified_token, proposal 1]; each later proposal is the argmax of
+ *   base logits plus a per-step correction, taken over the full vocabulary
+ *   (K = 0) or over one per-request, block-shared pool of the K best ids;
+ *   every chosen token is fed back into the GRU before the next step.
+ *   "[Spec] Add Domino projector support to DFlash speculative decoding (V2)"
+ *   (sglang PR #28998), sections "Motivation" and "Implementation": the
+ *   correction is SiLU(z + s)·fc2ᵀ + bias added to the lm_head logits.
+ *   "feat: support tensor-parallel Domino rollout" (sglang PR #32018),
+ *   section "Implementation": proposal 1 stays a full-vocabulary argmax; the
+ *   lm_head is the target model's, shared rather than copied.
+ *
+ * Exact arithmetic of one run (all accumulation in fp32):
+ *   base[t,b,v] = sum_i hidden[b,t,i] * lm_head[v,i]              t = 0..14
+ *   p[b,1]      = argmax_v base[0,b,v]
+ *   pool C_b    = all ids                      if K == 0 or K >= V
+ *               = K ids with the largest max_t base[t,b,v], ties to the
+ *                 lower id                     if 0 < K < V
+ *   h = 0;  h = GRU(E[verified[b]], h);  h = GRU(E[p[b,1]], h)
+ *   for k = 1..14:
+ *     u = SiLU(fc1_w · h + step_s[b,k-1,:])
+ *     y_c = base[k,b,c] + (fc2_w[c,:] · u + fc2_b[c])      for c in C_b
+ *     p[b,k+1] = argmax_c y_c  (ties to the lower id; -0.0 == +0.0)
+ *     if k < 14: h = GRU(E[p[b,k+1]], h)
+ *   GRU(x, h): a = W_ih x, c = W_hh h, rows ordered (r, z, n), no biases;
+ *     r = sigmoid(a_r + c_r), z = sigmoid(a_z + c_z),
+ *     n = tanh(a_n + r * c_n), h' = (1 - z) * n + z * h.
+ *
+ * Threading / streams: a handle is not re-entrant (one run in flight per
+ * handle).  Every run enqueues its kernels on the caller's stream and
+ * returns without a host synchronisation.  domino_rollout_run never
+ * allocates device memory, so a caller may capture it into its own graph.
+ */
+#ifndef DOMINO_ROLLOUT_H
+#define DOMINO_ROLLOUT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DOMINO_OK = 0,
+  DOMINO_ERR_INVALID_ARG = -1,     /* bad scalar or NULL pointer; nothing launched */
+  DOMINO_ERR_INVALID_CONFIG = -2,  /* create(): inconsistent configuration        */
+  DOMINO_ERR_UNSUPPORTED = -3,     /* device is not gfx950, or a shape this build
+                                      does not handle (see domino_config_t)       */
+  DOMINO_ERR_OUT_OF_MEMORY = -4,   /* workspace allocation failed in create()      */
+  DOMINO_ERR_HIP = -5              /* a HIP runtime call failed                    */
+} domino_status_t;
+
+typedef enum { DOMINO_DTYPE_BF16 = 0, DOMINO_DTYPE_FP32 = 1 } domino_dtype_t;
+
+/* Mirrors the Domino fields of the draft configuration ("[Spec] Add Domino
+ * projector support ..." section "Implementation": gru_hidden_dim, emb_dim,
+ * pure_draft_prefix_len; block size 16 per "Add correctness-first Domino
+ * support ..." section "Supported and numerical scope").  Validated by
+ * domino_rollout_create. */
+typedef struct {
+  int32_t vocab;        /* V  > 0                                              */
+  int32_t hidden;       /* H  > 0, multiple of 64                              */
+  int32_t emb_dim;      /* e  > 0, multiple of 32                              */
+  int32_t gru_hidden;   /* g  > 0, multiple of 32                              */
+  int32_t proj_dim;     /* r  > 0, multiple of 32                              */
+  int32_t block_size;   /* must be 16: 15 proposals, 14 correction steps       */
+  int32_t pure_draft_prefix_len; /* must be 1                                  */
+  int32_t max_batch;    /* 1..64: workspace is sized for this many requests    */
+  int32_t max_k;        /* >= 0: largest pool size run() accepts (0 = no pool) */
+  int32_t dtype;        /* domino_dtype_t of weights and hiddens               */
+} domino_config_t;
+
+/* BORROWED device pointers (row-major, dtype of the config) that must stay
+ * valid and unchanged for the life of the handle. */
+typedef struct {
+  const void* lm_head;   /* [V, H]  the target model's LM head                 */
+  const void* embed;     /* [V, e]  token embedding feeding the GRU            */
+  const void* gru_w_ih;  /* [3g, e] rows ordered (r, z, n), bias-free          */
+  const void* gru_w_hh;  /* [3g, g] rows ordered (r, z, n), bias-free          */
+  const void* fc1_w;     /* [r, g]  projector layer 1 (GRU half)               */
+  const void* fc2_w;     /* [V, r]  projector layer 2                          */
+  const void* fc2_b;     /* [V]     projector layer 2 bias                     */
+} domino_weights_t;
+
+typedef struct domino_rollout domino_rollout_t;
+
+/* Validates the configuration, checks that the current HIP device is gfx950,
+ * records the borrowed weights and allocates the workspace (base logits
+ * [15, max_batch, V] fp32, pool buffers, GRU / projector state).  On success
+ * *out owns the handle; on failure *out is NULL and the status says why
+ * (domino_rollout_last_error(NULL) holds the message). */
+domino_status_t domino_rollout_create(const domino_config_t* cfg, const domino_weights_t* w,
+                                      domino_rollout_t** out);
+
+/* One rollout for `batch` requests, enqueued on `stream` (hipStream_t; NULL
+ * = the default stream).  Device pointers, caller-owned:
+ *   base_hidden     [batch, 15, H]  dtype of the config: the block's draft hiddens
+ *   step_s          [batch, 14, r]  fp32: the backbone-hidden half of the
+ *                                   projector input plus the fc1 bias, per step
+ *   verified_tokens [batch]         int32 in [0, V)
+ *   out_tokens      [batch, 15]     int32: proposals 1..15
+ *   out_top1_logit  [batch, 15]     fp32 or NULL: the winning logit of each
+ *                                   proposal (column 0: base logit of p1)
+ * K == 0 or K >= V selects the full vocabulary; 0 < K < V a pool of K ids
+ * (K <= max_k).  Returns DOMINO_ERR_INVALID_ARG without launching anything
+ * for batch outside [1, max_batch], K < 0, K > max_k with K < V, or a NULL
+ * pointer.  A verified token outside [0, V) is not read; that request's
+ * outputs become -1 (tokens) and NaN (logits). */
+domino_status_t domino_rollout_run(domino_rollout_t* h, const void* base_hidden,
+                                   const float* step_s, const int32_t* verified_tokens,
+                                   int32_t batch, int32_t K, int32_t* out_tokens,
+                                   float* out_top1_logit, void* stream);
+
+/* Same computation as domino_rollout_run, replayed from a HIP graph that the
+ * handle captures on first use for each distinct (batch, K mode, pointer
+ * set) and keeps until destroy.  The first call for a new key captures and
+ * instantiates (host work); later calls are a single hipGraphLaunch. */
+domino_status_t domino_rollout_run_graph(domino_rollout_t* h, const void* base_hidden,
+                                         const float* step_s, const int32_t* verified_tokens,
+                                         int32_t batch, int32_t K, int32_t* out_tokens,
+                                         float* out_top1_logit, void* stream);
+
+/* Teacher-forced variant for testing: the GRU consumes forced_tokens[b, j]
+ * (device, [batch, 15] int32, values in [0, V)) in place of proposal j+1,
+ * while out_tokens / out_top1_logit still report each step's argmax.  This
+ * lets every step's logits be compared even after two chains diverge. */
+domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const void* base_hidden,
+                                          const float* step_s, const int32_t* verified_tokens,
+                                          const int32_t* forced_tokens, int32_t batch, int32_t K,
+                                          int32_t* out_tokens, float* out_top1_logit,
+                                          void* stream);
+
+/* Copies a workspace buffer of the last run into dst (device memory of at
+ * least dst_bytes), stream-ordered on `stream`.  which: 0 = base logits fp32
+ * [15, batch, V] (step-major), 1 = pool ids int32 [batch, K] sorted
+ * ascending (pool runs only).  *bytes receives the buffer's size for the
+ * last run; with dst == NULL nothing is copied.  INVALID_ARG if which is
+ * unknown, no run has happened, or dst_bytes is too small. */
+domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t which, void* dst,
+                                              size_t dst_bytes, size_t* bytes, void* stream);
+
+/* Frees the workspace and cached graphs (not the borrowed weights). NULL is a no-op. */
+void domino_rollout_destroy(domino_rollout_t* h);
+
+/* Message of the handle's last error, or of the last failed create() when
+ * h is NULL.  Never NULL; "" when there was no error. */
+const char* domino_rollout_last_error(const domino_rollout_t* h);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DOMINO_ROLLOUT_H */
