@@ -1,0 +1,237 @@
+"""Benchmark of the Domino draft-block rollout on one MI355X.
+
+One step = one whole rollout (LM-head logits, first proposal, [pool], GRU
+prefix, 14 correction steps with feedback) for one batch of synthetic
+requests whose inputs are already resident in HBM, replayed from the
+library's HIP graph.  The default workload is the Qwen3-8B-shaped rollout
+at batch 1 with full-vocabulary correction (K = 0); ``--workload`` and
+``--k`` select the other cells of the matrix (8B at B = 1/8/64 with K = 0 or
+2048, 27B-class at B = 64).
+
+Prints one JSON line: ms per block (lower is better), the roofline figure of
+the dominant kernel (live HIP-event durations of each launch of that kernel
+in eager runs right after the timed region, on the launch stream), and the
+CPU oracle's time on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix
+FP32_PEAK_TFLOPS = 157.3
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(shape, B, K):
+    """Algorithmic bytes / flops per launch of each kernel class (the unit
+    figures of the design notes times the units one launch processes)."""
+    V, H, e, g, r = shape.vocab, shape.hidden, shape.emb_dim, shape.gru_hidden, shape.proj_dim
+    wb = 2 if shape.dtype == "bf16" else 4
+    pool = 0 < K < V
+    if pool:
+        # gathered fc2 rows + their biases, compact base values, pool ids, u
+        correct_bytes = B * K * (r * wb + wb + 4 + 4) + B * r * 4
+    else:
+        # the whole fc2 and b2, one base row per request, u
+        correct_bytes = V * r * wb + V * wb + B * V * 4 + B * r * 4
+    lm_bytes = V * H * wb + B * 15 * H * wb + 15 * B * V * 4
+    lm_flops = 2.0 * 15 * B * H * V
+    gru_bytes = 3 * g * (e + g) * wb + B * (e * wb + 2 * g * 4)
+    return {"correct_bytes": correct_bytes, "lm_bytes": lm_bytes, "lm_flops": lm_flops,
+            "gru_bytes": gru_bytes}
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "gru_corrected_draft_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload, digest):
+    """HBM bytes per launch recorded from rocprofv3 counters, if they were
+    taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
+    m_t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_d or not m_t or m_d.group(1) != digest:
+        return None
+    return float(m_t.group(1))
+
+
+def cpu_baseline(w, shape, B, K, input_seed, budget_s):
+    """The oracle, as it stands, on whole blocks of the same workload until
+    about budget_s seconds of work; ms per block."""
+    import oracle
+    from gru_corrected_draft_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count()
+    f32 = {n: w.f32(n) for n in ("lm_head", "embed", "gru_w_ih", "gru_w_hh", "fc1_w", "fc2_w",
+                                 "fc2_b")}
+    times = []
+    t_start = time.perf_counter()
+    trial = 0
+    while True:
+        inp = synth.make_inputs(shape, B, input_seed, trial)
+        X = inp.hidden_f32()
+        t0 = time.perf_counter()
+        oracle.rollout(f32, X, inp.step_s, inp.verified, K)
+        times.append(time.perf_counter() - t0)
+        trial += 1
+        if time.perf_counter() - t_start > budget_s or trial >= 20:
+            break
+    return {"value": round(1e3 * float(np.median(times)), 3), "unit": "ms/block",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{trial} whole blocks (trials 0..{trial - 1}) of the same workload, "
+                      f"NumPy fp32 oracle, median"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="8b_b1")
+    ap.add_argument("--k", type=int, default=None, help="pool size (0 = full vocabulary)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the rollout is built and timed on a single MI355X; "
+              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from gru_corrected_draft_amd import rollout as R
+    from gru_corrected_draft_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    wl = synth.WORKLOADS[args.workload]
+    shape = synth.MODELS[wl.model]
+    K = wl.ks[0] if args.k is None else args.k
+    B = wl.batch
+
+    t0 = time.time()
+    w = synth.make_weights(shape)
+    dev = R.device_weights(w)
+    inp = synth.make_inputs(shape, B, wl.input_seed, 0)
+    hid, s, ver = R.device_inputs(inp)
+    log(f"[bench] {args.workload} B={B} K={K}: inputs ready in {time.time() - t0:.1f}s")
+    h = R.DominoRollout(dev, max_batch=B, max_k=max(K, 1))
+    out_t = torch.empty((B, 15), dtype=torch.int32, device="cuda")
+    out_l = torch.empty((B, 15), dtype=torch.float32, device="cuda")
+
+    # warm-up (the first call captures the graph)
+    for _ in range(args.warmup):
+        h.run(hid, s, ver, K, out_tokens=out_t, out_top1=out_l, graph=True)
+    torch.cuda.synchronize()
+    ref_tokens = out_t.clone()
+
+    # timed region: graph replays on torch's current stream
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        h.run(hid, s, ver, K, out_tokens=out_t, out_top1=out_l, graph=True)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t_wall) * 1e3
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    assert torch.equal(out_t, ref_tokens), "graph replays disagree"
+
+    # per-kernel durations: HIP events around each launch, eager runs, same stream
+    h.set_timing(True)
+    h.reset_kernel_times()
+    for _ in range(args.steps):
+        h.run(hid, s, ver, K, out_tokens=out_t, out_top1=out_l)
+    torch.cuda.synchronize()
+    kt = h.kernel_times()
+    h.set_timing(False)
+    assert torch.equal(out_t, ref_tokens), "eager run disagrees with graph replay"
+    avg = {k: (ms / n if n else None) for k, (ms, n) in kt.items()}
+    log("[bench] per-launch ms: " + ", ".join(f"{k}={v:.4f}" for k, v in avg.items() if v))
+
+    alg = algorithmic(shape, B, K)
+    digest = kernel_source_digest()
+    corr_ms = avg["correct"]
+    lm_ms = avg["lmhead"]
+    corr_total = corr_ms * 14
+    lm_bound_mfma = 15 * B > 128
+    if lm_bound_mfma and lm_ms > corr_total:
+        achieved = alg["lm_flops"] / (lm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "lmhead_gemm", "achieved": round(achieved, 1),
+                "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                "traffic": read_traffic("lmhead", f"{args.workload}_k{K}", digest)}
+    else:
+        achieved = alg["correct_bytes"] / (corr_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "correct_" + ("pool" if 0 < K < shape.vocab else "full"),
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": read_traffic("correct", f"{args.workload}_k{K}", digest)}
+    roof["launch_ms"] = round(corr_ms if roof["bound"] == "hbm" else lm_ms, 5)
+    phases = {k: {"ms_per_launch": round(v, 5), "launches_per_block": kt[k][1] // args.steps}
+              for k, v in avg.items() if v}
+
+    line = {
+        "metric": "Domino rollout ms/block (15 proposals)",
+        "value": round(ms_step, 4),
+        "unit": "ms/block",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}-shaped Domino rollout, batch {B}, "
+                               f"{'full-vocabulary correction (K=0)' if K == 0 or K >= shape.vocab else f'pool K={K}'}",
+                   "batch": B, "K": K, "vocab": shape.vocab, "hidden": shape.hidden,
+                   "emb_dim": shape.emb_dim, "gru_hidden": shape.gru_hidden,
+                   "proj_dim": shape.proj_dim, "block_size": 16, "accumulate": "fp32",
+                   "mode": "hip graph replay"},
+        "roofline": roof,
+        "phases": phases,
+        "wall_ms_per_step": round(wall_ms / args.steps, 4),
+        "kernel_source_digest": digest,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline (~{args.cpu_budget:.0f}s)")
+        line["cpu_baseline"] = cpu_baseline(w, shape, B, K, wl.input_seed, args.cpu_budget)
+    else:
+        line["cpu_baseline"] = None
+    h.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

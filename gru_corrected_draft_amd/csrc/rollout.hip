@@ -43,6 +43,9 @@ struct GraphEntry {
   hipGraphExec_t exec;
 };
 
+constexpr int kPhases = 6;
+enum Phase { kLmHead = 0, kCorrect = 1, kGru = 2, kFc1 = 3, kPool = 4, kArgmax0 = 5 };
+
 }  // namespace
 
 struct domino_rollout {
@@ -55,6 +58,28 @@ struct domino_rollout {
   std::vector<GraphEntry> graphs;
   hipStream_t capture_stream = nullptr;
   int last_B = 0, last_K = 0;  // shape of the last enqueued run
+  // measurement: event pairs recorded around launches while timing is on
+  bool timing = false;
+  bool capturing = false;
+  struct Pending {
+    int phase;
+    hipEvent_t a, b;
+  };
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> free_events;
+  double phase_ms[kPhases] = {};
+  int64_t phase_n[kPhases] = {};
+
+  hipEvent_t take_event() {
+    if (!free_events.empty()) {
+      hipEvent_t e = free_events.back();
+      free_events.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
   std::string err;
 
   domino_status_t fail(domino_status_t st, const char* fmt, ...) {
@@ -202,6 +227,11 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
 
 extern "C" void domino_rollout_destroy(domino_rollout_t* h) {
   if (!h) return;
+  for (auto& p : h->pending) {
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
+  }
+  for (auto e : h->free_events) (void)hipEventDestroy(e);
   for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);
   if (h->capture_stream) (void)hipStreamDestroy(h->capture_stream);
   for (void* p : h->allocations) (void)hipFree(p);
@@ -232,6 +262,30 @@ static domino_status_t check_run_args(domino_rollout_t* h, const void* hidden, c
   return DOMINO_OK;
 }
 
+// Records an event pair around the launches issued inside its scope.
+struct PhaseTimer {
+  domino_rollout_t* h;
+  int phase;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  PhaseTimer(domino_rollout_t* h_, int phase_, hipStream_t st_) : h(h_), phase(phase_), st(st_) {
+    if (h->timing && !h->capturing) {
+      a = h->take_event();
+      if (a && hipEventRecord(a, st) != hipSuccess) a = nullptr;
+    }
+  }
+  ~PhaseTimer() {
+    if (!a) return;
+    hipEvent_t b = h->take_event();
+    if (b && hipEventRecord(b, st) == hipSuccess) {
+      h->pending.push_back({phase, a, b});
+    } else {
+      h->free_events.push_back(a);
+      if (b) h->free_events.push_back(b);
+    }
+  }
+};
+
 static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, const int32_t* ver,
                     const int32_t* forced, int B, int K, int32_t* out_tokens, float* out_top1,
                     hipStream_t st) {
@@ -241,23 +295,45 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
   h->last_B = B;
   h->last_K = pool ? K : 0;
   launch_reset(ws, B, pool ? K : 0, st);
-  launch_lmhead(sh, h->w.lm_head, hidden, ws.base, B, st);
-  launch_row0_argmax(sh, ws.base, B, ws.slots, st);
-  if (pool) launch_pool_build(sh, ws, B, K, st);
+  {
+    PhaseTimer t(h, kLmHead, st);
+    launch_lmhead(sh, h->w.lm_head, hidden, ws.base, B, st);
+  }
+  {
+    PhaseTimer t(h, kArgmax0, st);
+    launch_row0_argmax(sh, ws.base, B, ws.slots, st);
+  }
+  if (pool) {
+    PhaseTimer t(h, kPool, st);
+    launch_pool_build(sh, ws, B, K, st);
+  }
   // two-token prefix: h = GRU(E[verified], 0); h = GRU(E[p1], h)
-  launch_gru(sh, h->w, nullptr, ws.h[0], ver, 1, nullptr, ws.bad, B, st);
-  if (forced)
-    launch_gru(sh, h->w, ws.h[0], ws.h[1], forced, DOMINO_T, nullptr, ws.bad, B, st);
-  else
-    launch_gru(sh, h->w, ws.h[0], ws.h[1], nullptr, 0, ws.slots, ws.bad, B, st);
+  {
+    PhaseTimer t(h, kGru, st);
+    launch_gru(sh, h->w, nullptr, ws.h[0], ver, 1, nullptr, ws.bad, B, st);
+  }
+  {
+    PhaseTimer t(h, kGru, st);
+    if (forced)
+      launch_gru(sh, h->w, ws.h[0], ws.h[1], forced, DOMINO_T, nullptr, ws.bad, B, st);
+    else
+      launch_gru(sh, h->w, ws.h[0], ws.h[1], nullptr, 0, ws.slots, ws.bad, B, st);
+  }
   int cur = 1;
   for (int k = 1; k <= DOMINO_S; ++k) {
-    launch_fc1(sh, h->w, ws.h[cur], s, k - 1, ws, B, st);
-    if (pool)
-      launch_correct_pool(sh, h->w, ws, k, B, K, st);
-    else
-      launch_correct_full(sh, h->w, ws, k, B, st);
+    {
+      PhaseTimer t(h, kFc1, st);
+      launch_fc1(sh, h->w, ws.h[cur], s, k - 1, ws, B, st);
+    }
+    {
+      PhaseTimer t(h, kCorrect, st);
+      if (pool)
+        launch_correct_pool(sh, h->w, ws, k, B, K, st);
+      else
+        launch_correct_full(sh, h->w, ws, k, B, st);
+    }
     if (k < DOMINO_S) {
+      PhaseTimer t(h, kGru, st);
       if (forced)
         launch_gru(sh, h->w, ws.h[cur], ws.h[cur ^ 1], forced + k, DOMINO_T, nullptr, ws.bad, B, st);
       else
@@ -335,8 +411,10 @@ extern "C" domino_status_t domino_rollout_run_graph(domino_rollout_t* h, const v
     hipGraph_t graph = nullptr;
     if (hipStreamBeginCapture(h->capture_stream, hipStreamCaptureModeRelaxed) != hipSuccess)
       return h->fail(DOMINO_ERR_HIP, "run_graph: begin capture failed");
+    h->capturing = true;
     enqueue(h, base_hidden, step_s, verified_tokens, nullptr, batch, kmode, out_tokens,
             out_top1_logit, h->capture_stream);
+    h->capturing = false;
     hipError_t e1 = hipGetLastError();
     hipError_t e2 = hipStreamEndCapture(h->capture_stream, &graph);
     if (e1 != hipSuccess || e2 != hipSuccess || !graph) {
@@ -376,5 +454,37 @@ extern "C" domino_status_t domino_rollout_read_workspace(const domino_rollout_t*
   DeviceGuard dg(h->device);
   if (hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, (hipStream_t)stream) != hipSuccess)
     return DOMINO_ERR_HIP;
+  return DOMINO_OK;
+}
+
+extern "C" domino_status_t domino_rollout_set_timing(domino_rollout_t* h, int32_t enable) {
+  if (!h) return DOMINO_ERR_INVALID_ARG;
+  h->timing = enable != 0;
+  return DOMINO_OK;
+}
+
+extern "C" domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int32_t which,
+                                                       double* total_ms, int64_t* launches) {
+  if (!h || which < -1 || which >= kPhases) return DOMINO_ERR_INVALID_ARG;
+  DeviceGuard dg(h->device);
+  for (auto& p : h->pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess)
+      return h->fail(DOMINO_ERR_HIP, "kernel_times: event query failed");
+    h->phase_ms[p.phase] += ms;
+    h->phase_n[p.phase] += 1;
+    h->free_events.push_back(p.a);
+    h->free_events.push_back(p.b);
+  }
+  h->pending.clear();
+  if (which == -1) {
+    for (int i = 0; i < kPhases; ++i) {
+      h->phase_ms[i] = 0;
+      h->phase_n[i] = 0;
+    }
+    return DOMINO_OK;
+  }
+  if (total_ms) *total_ms = h->phase_ms[which];
+  if (launches) *launches = h->phase_n[which];
   return DOMINO_OK;
 }

@@ -27,7 +27,9 @@ N_STEPS = 14
 
 EXPORTED = ("domino_rollout_create", "domino_rollout_run", "domino_rollout_run_graph",
             "domino_rollout_run_forced", "domino_rollout_read_workspace", "domino_rollout_destroy",
-            "domino_rollout_last_error")
+            "domino_rollout_last_error", "domino_rollout_set_timing",
+            "domino_rollout_kernel_times")
+PHASES = {"lmhead": 0, "correct": 1, "gru": 2, "fc1": 3, "pool": 4, "argmax0": 5}
 
 
 class Config(ctypes.Structure):
@@ -78,6 +80,11 @@ def load_library():
     lib.domino_rollout_destroy.restype = None
     lib.domino_rollout_last_error.argtypes = [vp]
     lib.domino_rollout_last_error.restype = ctypes.c_char_p
+    lib.domino_rollout_set_timing.argtypes = [vp, i32]
+    lib.domino_rollout_set_timing.restype = ctypes.c_int
+    lib.domino_rollout_kernel_times.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double),
+                                                ctypes.POINTER(ctypes.c_int64)]
+    lib.domino_rollout_kernel_times.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -182,6 +189,22 @@ class DominoRollout:
         self._check(self.lib.domino_rollout_read_workspace(self.handle, which, _ptr(out), n.value,
                                                            ctypes.byref(n), st))
         return out
+
+    def set_timing(self, enable):
+        self._check(self.lib.domino_rollout_set_timing(self.handle, 1 if enable else 0))
+
+    def kernel_times(self):
+        """{phase: (total ms, launches)} of the timed runs so far (waits on their events)."""
+        out = {}
+        for name, i in PHASES.items():
+            ms, n = ctypes.c_double(), ctypes.c_int64()
+            self._check(self.lib.domino_rollout_kernel_times(self.handle, i, ctypes.byref(ms),
+                                                             ctypes.byref(n)))
+            out[name] = (ms.value, n.value)
+        return out
+
+    def reset_kernel_times(self):
+        self._check(self.lib.domino_rollout_kernel_times(self.handle, -1, None, None))
 
     def close(self):
         if getattr(self, "handle", None):
