@@ -485,7 +485,11 @@ static void gru_dispatch(const GruArgs<BF>& a, hipStream_t st) {
 void launch_gru(const Shape& s, const DeviceWeights& w, const float* h_in, float* h_out,
                 const int32_t* tok_i32, int tok_stride, const uint64_t* tok_key, int32_t* bad,
                 int B, hipStream_t st) {
-  if (s.bf16) {
+  if (s.bf16 && B <= kRowsMaxBatch && rows_supported(s.e, s.g, s.r)) {
+    GruArgs16 a{(const uint16_t*)w.embed, (const uint16_t*)w.w_ih, (const uint16_t*)w.w_hh, h_in,
+                h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g};
+    launch_gru_rows(a, st);
+  } else if (s.bf16) {
     GruArgs<true> a{(const bf16_t*)w.embed, (const bf16_t*)w.w_ih, (const bf16_t*)w.w_hh, h_in,
                     h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g};
     gru_dispatch<true>(a, st);
@@ -574,7 +578,10 @@ static void fc1_dispatch(const Fc1Args<BF>& a, hipStream_t st) {
 
 void launch_fc1(const Shape& s, const DeviceWeights& w, const float* h, const float* step_s,
                 int step, const Workspace& ws, int B, hipStream_t st) {
-  if (s.bf16) {
+  if (s.bf16 && B <= kRowsMaxBatch && rows_supported(s.e, s.g, s.r)) {
+    Fc1Args16 a{(const uint16_t*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r};
+    launch_fc1_rows(a, st);
+  } else if (s.bf16) {
     Fc1Args<true> a{(const bf16_t*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r};
     fc1_dispatch<true>(a, st);
   } else {
@@ -709,7 +716,11 @@ void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace
                          hipStream_t st) {
   const float* base_k = ws.base + (size_t)k * B * s.V;
   uint64_t* slot_k = ws.slots + (size_t)k * B;
-  if (s.bf16) {
+  if (s.bf16 && rowstream_supported(s.r, B)) {
+    StreamArgs a{(const uint16_t*)w.fc2, s.V, s.r, ws.u_hi, ws.u_lo, B, 0, 0, nullptr,
+                 (const uint16_t*)w.fc2_b, base_k, slot_k};
+    launch_rowstream_argmax(a, st);
+  } else if (s.bf16) {
     CorrArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, base_k, ws.u, ws.u_hi, ws.u_lo,
                      slot_k, B, s.V, s.r};
     correct_full_dispatch<true>(a, st);

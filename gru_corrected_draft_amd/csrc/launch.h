@@ -38,6 +38,53 @@ struct Workspace {
 
 constexpr int kPoolChunk = 1024;
 
+// streaming row kernel (stream.hip)
+struct StreamArgs {
+  const uint16_t* W;       // [N, K] bf16 weight rows, streamed once
+  int N, K;
+  const uint16_t* act_hi;  // activation rows, bf16
+  const uint16_t* act_lo;  // low halves (correction) or nullptr
+  int ncols;               // activation columns (<= 128)
+  int col_B;               // > 0: column m reads row (m % col_B) * 15 + m / col_B
+  int KS;                  // k slice staged in LDS (set by the launcher)
+  float* out;              // store epilogue: [ncols, N]
+  const uint16_t* b2;      // argmax epilogue: bias [N], base row [ncols, N], words [ncols]
+  const float* base_k;
+  uint64_t* slot_k;
+};
+bool rowstream_supported(int K, int ncols);
+void rowstream_prepare();
+void launch_rowstream_store(StreamArgs a, hipStream_t st);
+void launch_rowstream_argmax(StreamArgs a, hipStream_t st);
+
+// one-wave-per-row GRU / fc1 (rows.hip), bf16 weights
+struct GruArgs16 {
+  const uint16_t* E;
+  const uint16_t* w_ih;
+  const uint16_t* w_hh;
+  const float* h_in;
+  float* h_out;
+  const int32_t* tok_i32;
+  int tok_stride;
+  const uint64_t* tok_key;
+  int32_t* bad;
+  int B, V, e, g;
+};
+struct Fc1Args16 {
+  const uint16_t* F1;
+  const float* h;
+  const float* s;
+  int step;
+  float* u;
+  uint16_t* u_hi;
+  uint16_t* u_lo;
+  int B, g, r;
+};
+constexpr int kRowsMaxBatch = 16;
+bool rows_supported(int e, int g, int r);
+void launch_gru_rows(const GruArgs16& a, hipStream_t st);
+void launch_fc1_rows(const Fc1Args16& a, hipStream_t st);
+
 void lmhead_prepare();  // once per process: raise the tiled kernel's LDS limit
 void launch_reset(const Workspace& ws, int B, int K, hipStream_t st);
 void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int B, hipStream_t st);

@@ -220,7 +220,10 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
     return DOMINO_ERR_HIP;
   }
   static std::once_flag once;
-  std::call_once(once, lmhead_prepare);
+  std::call_once(once, [] {
+    lmhead_prepare();
+    rowstream_prepare();
+  });
   *out = h;
   return DOMINO_OK;
 }

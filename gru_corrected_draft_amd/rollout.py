@@ -11,7 +11,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdomino_rollout.so")
+LIB_PATH = os.environ.get("DOMINO_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libdomino_rollout.so")
 
 DOMINO_OK = 0
 DOMINO_ERR_INVALID_ARG = -1

@@ -83,6 +83,22 @@ def test_small_bf16_ragged_rollout(B, K):
     assert checked > 0
 
 
+DEEP = synth.custom_shape(3001, 1024, 256, 256, 256, "bf16", 78, name="small-bf16-deep")
+
+
+@pytest.mark.parametrize("B,K", [(8, 0), (3, 50), (8, 200)])
+def test_lmhead_with_many_activation_slices(B, K):
+    """H = 1024 at B = 8 streams the LM-head against eight 128-wide slices of
+    the 120-column activation panel (an odd super-chunk count per slice)."""
+    G.log(f"[gpu-test] deep hidden B={B} K={K}")
+    tok, top, h = G.gpu_run(DEEP, B, 700 + B, 0, K, max_batch=64, max_k=2048)
+    ref = G.oracle_run(DEEP, B, 700 + B, 0, K)
+    compare(tok, top, ref, TOL["bf16"])
+    base = h.read_workspace(0).cpu().numpy().reshape(15, B, -1)
+    want = ref_base(DEEP, B, 700 + B, 0)
+    assert np.max(np.abs(base - want)) < 1e-4
+
+
 @pytest.mark.parametrize("K", [0, 64])
 def test_teacher_forced_every_step(K):
     B, seed = 6, 900
