@@ -21,6 +21,7 @@
 typedef uint16_t bf16_t;
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define DOMINO_T 15   // proposals per block (block size 16)
 #define DOMINO_S 14   // correction steps
@@ -45,10 +46,7 @@ __device__ __forceinline__ v4f mfma_f32(float a, float b, v4f c) {
 
 // 8 bf16 -> one fragment register quad
 __device__ __forceinline__ v8s load_frag_bf16(const bf16_t* p) {
-  uint4 w = *reinterpret_cast<const uint4*>(p);
-  v8s r;
-  __builtin_memcpy(&r, &w, 16);
-  return r;
+  return *reinterpret_cast<const v8s*>(p);
 }
 __device__ __forceinline__ v8s zero_frag() {
   v8s r = {0, 0, 0, 0, 0, 0, 0, 0};

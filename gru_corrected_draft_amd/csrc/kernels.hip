@@ -198,7 +198,7 @@ template <int PASS>
 __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restrict__ keys, int V,
                                                         const uint32_t* __restrict__ state,
                                                         uint32_t* __restrict__ hist) {
-  constexpr int NBINS = PASS == 1 ? 2048 : 1024;
+  constexpr int NBINS = PASS < 2 ? 2048 : 1024;
   __shared__ uint32_t h[NBINS];
   const int b = blockIdx.y;
   const uint32_t prefix = state[2 * b];
@@ -210,7 +210,9 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
     const int v = v0 + j * 256 + threadIdx.x;
     if (v < V) {
       const uint32_t key = keys[(size_t)b * V + v];
-      if (PASS == 1) {
+      if (PASS == 0) {
+        atomicAdd(&h[key >> 21], 1u);
+      } else if (PASS == 1) {
         if ((key >> 21) == prefix) atomicAdd(&h[(key >> 10) & 2047u], 1u);
       } else {
         if ((key >> 10) == prefix) atomicAdd(&h[key & 1023u], 1u);
@@ -333,10 +335,14 @@ __global__ __launch_bounds__(256) void pool_compact_kernel(
   }
 }
 
-void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, hipStream_t st) {
+void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, bool keys_ready,
+                       hipStream_t st) {
   const int nch = (s.V + kPoolChunk - 1) / kPoolChunk;
   const dim3 grid(nch, B), blk(256);
-  hipLaunchKernelGGL(pool_score_hist_kernel, grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
+  if (keys_ready)
+    hipLaunchKernelGGL(pool_hist_kernel<0>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+  else
+    hipLaunchKernelGGL(pool_score_hist_kernel, grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
   hipLaunchKernelGGL(pool_select_kernel<0>, dim3(B), blk, 0, st, ws.hist, ws.state);
   hipLaunchKernelGGL(pool_hist_kernel<1>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
   hipLaunchKernelGGL(pool_select_kernel<1>, dim3(B), blk, 0, st, ws.hist, ws.state);
@@ -694,6 +700,8 @@ __global__ __launch_bounds__(256) void correct_full_kernel(CorrArgs<BF> a) {
 }
 
 constexpr int kCorrRT = 4;
+// consecutive correction steps stream fc2 in opposite k order
+constexpr bool kReverseOddSteps = true;
 
 template <bool BF, int NB>
 static void correct_full_launch(const CorrArgs<BF>& a, hipStream_t st) {
@@ -718,7 +726,7 @@ void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace
   uint64_t* slot_k = ws.slots + (size_t)k * B;
   if (s.bf16 && rowstream_supported(s.r, B)) {
     StreamArgs a{(const uint16_t*)w.fc2, s.V, s.r, ws.u_hi, ws.u_lo, B, 0, 0, nullptr,
-                 (const uint16_t*)w.fc2_b, base_k, slot_k};
+                 (const uint16_t*)w.fc2_b, base_k, slot_k, kReverseOddSteps ? (k & 1) : 0};
     launch_rowstream_argmax(a, st);
   } else if (s.bf16) {
     CorrArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, base_k, ws.u, ws.u_hi, ws.u_lo,

@@ -51,6 +51,7 @@ struct StreamArgs {
   const uint16_t* b2;      // argmax epilogue: bias [N], base row [ncols, N], words [ncols]
   const float* base_k;
   uint64_t* slot_k;
+  int reverse;             // walk k from the end (alternated between steps)
 };
 bool rowstream_supported(int K, int ncols);
 void rowstream_prepare();
@@ -81,6 +82,20 @@ struct Fc1Args16 {
   int B, g, r;
 };
 constexpr int kRowsMaxBatch = 16;
+
+// LM-head GEMM with fused pool-score keys and first-proposal argmax (lmhead_fused.hip)
+struct FusedArgs {
+  const uint16_t* W;   // lm_head [V, H]
+  const uint16_t* X;   // hidden [B, 15, H]
+  float* base;         // [15, B, V]
+  uint32_t* keys;      // [B, V] orderable max over the block, or nullptr
+  uint64_t* slots;     // argmax words of position 0 [B]
+  int V, H, B;
+};
+constexpr int kFusedMinBatch = 2;
+void lmhead_fused_prepare();
+bool lmhead_fused_supported(int H);
+void launch_lmhead_fused(const FusedArgs& a, hipStream_t st);
 bool rows_supported(int e, int g, int r);
 void launch_gru_rows(const GruArgs16& a, hipStream_t st);
 void launch_fc1_rows(const Fc1Args16& a, hipStream_t st);
@@ -89,7 +104,9 @@ void lmhead_prepare();  // once per process: raise the tiled kernel's LDS limit
 void launch_reset(const Workspace& ws, int B, int K, hipStream_t st);
 void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int B, hipStream_t st);
 void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st);
-void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, hipStream_t st);
+// keys_ready: the per-id scores were already written by the fused LM-head
+void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, bool keys_ready,
+                       hipStream_t st);
 // token source: exactly one of tok_i32 (element b*stride) or tok_key (argmax word b)
 void launch_gru(const Shape& s, const DeviceWeights& w, const float* h_in, float* h_out,
                 const int32_t* tok_i32, int tok_stride, const uint64_t* tok_key, int32_t* bad,

@@ -257,7 +257,7 @@ void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int
     stream_dispatch<false>(s, W, X, out, B, st);
   } else if (M <= 128 && rowstream_supported(s.H, M)) {
     StreamArgs a{(const uint16_t*)W, s.V, s.H, (const uint16_t*)X, nullptr, M, B, 0, out,
-                 nullptr, nullptr, nullptr};
+                 nullptr, nullptr, nullptr, 0};
     launch_rowstream_store(a, st);
   } else if (M <= 128) {
     stream_dispatch<true>(s, W, X, out, B, st);

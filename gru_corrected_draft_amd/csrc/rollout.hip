@@ -223,6 +223,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   std::call_once(once, [] {
     lmhead_prepare();
     rowstream_prepare();
+    lmhead_fused_prepare();
   });
   *out = h;
   return DOMINO_OK;
@@ -298,17 +299,24 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
   h->last_B = B;
   h->last_K = pool ? K : 0;
   launch_reset(ws, B, pool ? K : 0, st);
-  {
+  const bool fused = sh.bf16 && B >= kFusedMinBatch && lmhead_fused_supported(sh.H);
+  if (fused) {
+    // base logits, pool-score keys and the first proposal in one pass
     PhaseTimer t(h, kLmHead, st);
-    launch_lmhead(sh, h->w.lm_head, hidden, ws.base, B, st);
-  }
-  {
+    FusedArgs fa{(const uint16_t*)h->w.lm_head, (const uint16_t*)hidden, ws.base,
+                 pool ? ws.keys : nullptr, ws.slots, sh.V, sh.H, B};
+    launch_lmhead_fused(fa, st);
+  } else {
+    {
+      PhaseTimer t(h, kLmHead, st);
+      launch_lmhead(sh, h->w.lm_head, hidden, ws.base, B, st);
+    }
     PhaseTimer t(h, kArgmax0, st);
     launch_row0_argmax(sh, ws.base, B, ws.slots, st);
   }
   if (pool) {
     PhaseTimer t(h, kPool, st);
-    launch_pool_build(sh, ws, B, K, st);
+    launch_pool_build(sh, ws, B, K, fused, st);
   }
   // two-token prefix: h = GRU(E[verified], 0); h = GRU(E[p1], h)
   {

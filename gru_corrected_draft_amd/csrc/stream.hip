@@ -101,18 +101,26 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
     __syncthreads();
   };
 
-  // Super-chunks sc = 0 .. nsc-1 in order; A0 holds the even ones and A1
-  // the odd ones, each loaded one super-chunk ahead of its use.
+  // Super-chunks i = 0 .. nsc-1 in order (k ascending, or descending when
+  // a.reverse is set); A0 holds the even ones and A1 the odd ones, each
+  // loaded one super-chunk ahead of its use.  A slice is staged whenever the
+  // walk enters it.
   const int nsc = K / kSC;
-  if (active) load_sc(A0, 0);
-  for (int sc = 0; sc < nsc; sc += 2) {
-    if (sc % per_slice == 0) stage(sc);
-    if (active && sc + 1 < nsc) load_sc(A1, (sc + 1) * kSC);
-    if (active) compute_sc(A0, (sc % per_slice) * kSC);
-    if (sc + 1 >= nsc) break;
-    if ((sc + 1) % per_slice == 0) stage(sc + 1);
-    if (active && sc + 2 < nsc) load_sc(A0, (sc + 2) * kSC);
-    if (active) compute_sc(A1, ((sc + 1) % per_slice) * kSC);
+  const bool rev = a.reverse != 0;
+  auto chunk = [&](int i) { return rev ? nsc - 1 - i : i; };
+  auto enters_slice = [&](int i) {
+    const int sc = chunk(i);
+    return rev ? (sc % per_slice == per_slice - 1) : (sc % per_slice == 0);
+  };
+  if (active) load_sc(A0, chunk(0) * kSC);
+  for (int i = 0; i < nsc; i += 2) {
+    if (enters_slice(i)) stage(chunk(i));
+    if (active && i + 1 < nsc) load_sc(A1, chunk(i + 1) * kSC);
+    if (active) compute_sc(A0, (chunk(i) % per_slice) * kSC);
+    if (i + 1 >= nsc) break;
+    if (enters_slice(i + 1)) stage(chunk(i + 1));
+    if (active && i + 2 < nsc) load_sc(A0, chunk(i + 2) * kSC);
+    if (active) compute_sc(A1, (chunk(i + 1) % per_slice) * kSC);
   }
 
   if (EPI == kEpiStore) {
