@@ -118,6 +118,9 @@ def main():
     ap.add_argument("--k", type=int, default=None, help="pool size (0 = full vocabulary)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times "
+                         "(reference for the HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -131,6 +134,16 @@ def main():
     from gru_corrected_draft_amd import synth
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_read": n, "bytes_written": n, "launches": 3}))
+        return
     wl = synth.WORKLOADS[args.workload]
     shape = synth.MODELS[wl.model]
     K = wl.ks[0] if args.k is None else args.k

@@ -812,17 +812,87 @@ __global__ __launch_bounds__(256) void correct_pool_kernel(PoolArgs<BF> a) {
   if (lane == 0) publish_max(&a.slot_k[b], best);
 }
 
+// bf16 pool correction with the projector width split over the four waves
+// of a workgroup: one workgroup per 16 gathered candidates of one request,
+// every wave with all of its fc2 loads in flight at once (latency bound at
+// small batch, so parallelism matters more than reuse).
+template <int CPW>  // 32-wide k chunks per wave
+__global__ __launch_bounds__(256) void correct_pool_split_kernel(PoolArgs<true> a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, q = lane >> 4;
+  const int tiles = (a.K + 15) / 16;
+  const int b = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+  const int K = a.K, r = a.r;
+  const int32_t* ids = a.pool_ids + (size_t)b * K;
+  const int i = tile * 16 + row;
+  const int id = min(max(ids[min(i, K - 1)], 0), a.V - 1);
+  const bf16_t* pa = a.F2 + (size_t)id * r + q * 8;
+  const size_t uoff = (size_t)b * r + q * 8;
+  const int nch = r / 32;
+  v8s A[CPW], U[CPW];
+#pragma unroll
+  for (int c = 0; c < CPW; ++c) {
+    const int k = min(wave + 4 * c, nch - 1) * 32;  // chunks past the width are masked below
+    A[c] = load_frag_bf16(pa + k);
+    U[c] = row == 0 ? load_frag_bf16(a.u_hi + uoff + k)
+                    : (row == 1 ? load_frag_bf16(a.u_lo + uoff + k) : zero_frag());
+  }
+  v4f acc = zero4();
+#pragma unroll
+  for (int c = 0; c < CPW; ++c)
+    if (wave + 4 * c < nch) acc = mfma_bf16(A[c], U[c], acc);
+  __shared__ float red[4][4][64];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[wave][e][lane] = acc[e];
+  __syncthreads();
+  if (wave != 0) return;  // no barrier below
+  uint64_t best = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float part = ((red[0][e][lane] + red[1][e][lane]) + red[2][e][lane]) + red[3][e][lane];
+    const float dot = part + __shfl_down(part, 1, 64);  // hi (column 0) + lo (column 1)
+    const int idx = tile * 16 + 4 * q + e;
+    if (row == 0 && idx < K) {
+      const int cid = min(max(ids[idx], 0), a.V - 1);
+      const float y = a.pool_base_k[(size_t)b * K + idx] + (dot + bf16_to_f32(a.b2[cid]));
+      best = umax64(best, pack_key(y, (uint32_t)cid));
+    }
+  }
+  best = wave_max_u64(best);
+  if (lane == 0) publish_max(&a.slot_k[b], best);
+}
+
 constexpr int kPoolRT = 2;
+constexpr int kPoolSplitMaxBatch = 16;
 
 void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
                          int K, hipStream_t st) {
   const int tiles = (K + 15) / 16;
-  const int upr = (tiles + kPoolRT - 1) / kPoolRT;
+  const int upr = (tiles + kPoolRT - 1) / kPoolRT;  // units per request (fp32 / wide kernels)
   const int units = upr * B;
   const dim3 grid((units + 3) / 4);
   const float* pb = ws.pool_base + (size_t)(k - 1) * B * K;
   uint64_t* slot_k = ws.slots + (size_t)k * B;
-  if (s.bf16) {
+  // small batches are latency bound: spread each request's pool over many workgroups
+  if (s.bf16 && B <= kPoolSplitMaxBatch && s.r % 32 == 0 && s.r <= 32 * 4 * 12) {
+    PoolArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,
+                     ws.u_lo, slot_k, B, K, s.r, s.V, upr};
+    const dim3 g2((unsigned)(B * tiles));
+    switch ((s.r / 32 + 3) / 4) {
+      case 1: hipLaunchKernelGGL((correct_pool_split_kernel<1>), g2, dim3(256), 0, st, a); break;
+      case 2: hipLaunchKernelGGL((correct_pool_split_kernel<2>), g2, dim3(256), 0, st, a); break;
+      case 3: hipLaunchKernelGGL((correct_pool_split_kernel<3>), g2, dim3(256), 0, st, a); break;
+      case 4: hipLaunchKernelGGL((correct_pool_split_kernel<4>), g2, dim3(256), 0, st, a); break;
+      case 5: hipLaunchKernelGGL((correct_pool_split_kernel<5>), g2, dim3(256), 0, st, a); break;
+      case 6: hipLaunchKernelGGL((correct_pool_split_kernel<6>), g2, dim3(256), 0, st, a); break;
+      case 7: hipLaunchKernelGGL((correct_pool_split_kernel<7>), g2, dim3(256), 0, st, a); break;
+      case 8: hipLaunchKernelGGL((correct_pool_split_kernel<8>), g2, dim3(256), 0, st, a); break;
+      case 9: hipLaunchKernelGGL((correct_pool_split_kernel<9>), g2, dim3(256), 0, st, a); break;
+      case 10: hipLaunchKernelGGL((correct_pool_split_kernel<10>), g2, dim3(256), 0, st, a); break;
+      case 11: hipLaunchKernelGGL((correct_pool_split_kernel<11>), g2, dim3(256), 0, st, a); break;
+      default: hipLaunchKernelGGL((correct_pool_split_kernel<12>), g2, dim3(256), 0, st, a); break;
+    }
+  } else if (s.bf16) {
     PoolArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,
                      ws.u_lo, slot_k, B, K, s.r, s.V, upr};
     hipLaunchKernelGGL((correct_pool_kernel<true, kPoolRT>), grid, dim3(256), 0, st, a);
