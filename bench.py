@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="8b_b1")
     ap.add_argument("--k", type=int, default=None, help="pool size (0 = full vocabulary)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="requests per block (default: the workload's batch)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -147,7 +149,7 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     shape = synth.MODELS[wl.model]
     K = wl.ks[0] if args.k is None else args.k
-    B = wl.batch
+    B = wl.batch if args.batch is None else args.batch
 
     t0 = time.time()
     w = synth.make_weights(shape)

@@ -371,7 +371,22 @@ struct GruArgs {
   const uint64_t* tok_key; // or the argmax word of request b
   int32_t* bad;
   int B, V, e, g;
+  float* partial;          // [tiles][splits][4][64][16] when split over workgroups
 };
+
+// floats per (tile, split, gate) block of split partials: 64 requests x 16 units
+constexpr int kPartGate = 64 * 16;
+
+// h' = (1 - z) * n + z * h from the four pre-activation sums of one unit
+template <bool BF>
+__device__ __forceinline__ void gru_finish(const GruArgs<BF>& a, int b, int j, float sr, float sz,
+                                           float an, float cn) {
+  const float hold = a.h_in ? a.h_in[(size_t)b * a.g + j] : 0.0f;
+  const float rg = sigmoidf_(sr);
+  const float zg = sigmoidf_(sz);
+  const float ng = tanhf(an + rg * cn);
+  a.h_out[(size_t)b * a.g + j] = (1.0f - zg) * ng + zg * hold;
+}
 
 template <bool BF, int NB>
 __global__ __launch_bounds__(256) void gru_kernel(GruArgs<BF> a) {
@@ -405,7 +420,7 @@ __global__ __launch_bounds__(256) void gru_kernel(GruArgs<BF> a) {
     const W_t<BF>* pr = a.w_ih + (size_t)(j0 + row) * e + q * 8;
     const W_t<BF>* pz = pr + (size_t)g * e;
     const W_t<BF>* pn = pz + (size_t)g * e;
-    for (int c = wave; c < e / 32; c += 4) {
+    for (int c = blockIdx.y * 4 + wave; c < e / 32; c += 4 * gridDim.y) {
       const int k = c * 32;
       WFrag<BF> A_r, A_z, A_n;
       A_r.load(pr + k);
@@ -425,7 +440,7 @@ __global__ __launch_bounds__(256) void gru_kernel(GruArgs<BF> a) {
     const W_t<BF>* pr = a.w_hh + (size_t)(j0 + row) * g + q * 8;
     const W_t<BF>* pz = pr + (size_t)g * g;
     const W_t<BF>* pn = pz + (size_t)g * g;
-    for (int c = wave; c < g / 32; c += 4) {
+    for (int c = blockIdx.y * 4 + wave; c < g / 32; c += 4 * gridDim.y) {
       const int k = c * 32;
       WFrag<BF> A_r, A_z, A_n;
       A_r.load(pr + k);
@@ -455,27 +470,63 @@ __global__ __launch_bounds__(256) void gru_kernel(GruArgs<BF> a) {
   __syncthreads();
   // thread t finishes register i = t / 64 of lane l = t % 64 of every tile
   const int l = threadIdx.x & 63, i = threadIdx.x >> 6;
-  const int j = j0 + 4 * (l >> 4) + i;
+  const int jj = 4 * (l >> 4) + i, j = j0 + jj;
+  const int nsplit = gridDim.y;
+  float S[NB][4];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int gt = 0; gt < 4; ++gt)
+      S[cb][gt] = ((red[0][gt][cb][threadIdx.x] + red[1][gt][cb][threadIdx.x]) +
+                   red[2][gt][cb][threadIdx.x]) + red[3][gt][cb][threadIdx.x];
+  if (nsplit > 1) {
+    // partial[tile][split][gate][b][jj]; gru_combine_kernel finishes the units
+    float* mine = a.partial + ((size_t)blockIdx.x * nsplit + blockIdx.y) * 4 * kPartGate;
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+      for (int gt = 0; gt < 4; ++gt)
+        mine[(size_t)gt * kPartGate + (cb * 16 + (l & 15)) * 16 + jj] = S[cb][gt];
+    return;
+  }
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     const int b = cb * 16 + (l & 15);
-    if (b >= a.B) continue;
-    float S[4];
-#pragma unroll
-    for (int gt = 0; gt < 4; ++gt)
-      S[gt] = ((red[0][gt][cb][threadIdx.x] + red[1][gt][cb][threadIdx.x]) +
-               red[2][gt][cb][threadIdx.x]) + red[3][gt][cb][threadIdx.x];
-    const float hold = a.h_in ? a.h_in[(size_t)b * g + j] : 0.0f;
-    const float rg = sigmoidf_(S[0]);
-    const float zg = sigmoidf_(S[1]);
-    const float ng = tanhf(S[2] + rg * S[3]);
-    a.h_out[(size_t)b * g + j] = (1.0f - zg) * ng + zg * hold;
+    if (b < a.B) gru_finish(a, b, j, S[cb][0], S[cb][1], S[cb][2], S[cb][3]);
   }
+}
+
+// Sums the split partials of every (request, unit) in split order and applies
+// the gates; one thread per output, units fastest.
+template <bool BF>
+__global__ __launch_bounds__(256) void gru_combine_kernel(GruArgs<BF> a, int nsplit) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.B * a.g) return;
+  const int b = t / a.g, j = t - b * a.g;
+  const float* p = a.partial + (size_t)(j >> 4) * nsplit * 4 * kPartGate + b * 16 + (j & 15);
+  float S[4];
+#pragma unroll
+  for (int gt = 0; gt < 4; ++gt) {
+    float acc_s = p[gt * kPartGate];
+    for (int sp = 1; sp < nsplit; ++sp) acc_s += p[((size_t)sp * 4 + gt) * kPartGate];
+    S[gt] = acc_s;
+  }
+  gru_finish(a, b, j, S[0], S[1], S[2], S[3]);
+}
+
+// workgroups per tile along k: at least one 32-wide chunk per wave
+static int gemv_splits(int kdim) {
+  const int n = (kdim / 32) / 4;
+  return n < 1 ? 1 : (n > kGemvSplit ? kGemvSplit : n);
 }
 
 template <bool BF, int NB>
 static void gru_launch(const GruArgs<BF>& a, hipStream_t st) {
-  hipLaunchKernelGGL((gru_kernel<BF, NB>), dim3(a.g / 16), dim3(256), 0, st, a);
+  const int ns = a.partial ? gemv_splits(a.e < a.g ? a.e : a.g) : 1;
+  hipLaunchKernelGGL((gru_kernel<BF, NB>), dim3(a.g / 16, ns), dim3(256), 0, st, a);
+  if (ns > 1)
+    hipLaunchKernelGGL((gru_combine_kernel<BF>), dim3((a.B * a.g + 255) / 256), dim3(256), 0, st, a,
+                       ns);
 }
 
 template <bool BF>
@@ -490,18 +541,18 @@ static void gru_dispatch(const GruArgs<BF>& a, hipStream_t st) {
 
 void launch_gru(const Shape& s, const DeviceWeights& w, const float* h_in, float* h_out,
                 const int32_t* tok_i32, int tok_stride, const uint64_t* tok_key, int32_t* bad,
-                int B, hipStream_t st) {
-  if (s.bf16 && B <= kRowsMaxBatch && rows_supported(s.e, s.g, s.r)) {
+                int B, const Workspace& ws, hipStream_t st) {
+  if (s.bf16 && B <= kRowsGruMaxBatch && rows_supported(s.e, s.g, s.r)) {
     GruArgs16 a{(const uint16_t*)w.embed, (const uint16_t*)w.w_ih, (const uint16_t*)w.w_hh, h_in,
                 h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g};
     launch_gru_rows(a, st);
   } else if (s.bf16) {
     GruArgs<true> a{(const bf16_t*)w.embed, (const bf16_t*)w.w_ih, (const bf16_t*)w.w_hh, h_in,
-                    h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g};
+                    h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g, ws.partial};
     gru_dispatch<true>(a, st);
   } else {
     GruArgs<false> a{(const float*)w.embed, (const float*)w.w_ih, (const float*)w.w_hh, h_in,
-                     h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g};
+                     h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g, nullptr};
     gru_dispatch<false>(a, st);
   }
 }
@@ -519,7 +570,22 @@ struct Fc1Args {
   uint16_t* u_hi;
   uint16_t* u_lo;
   int B, g, r;
+  float* partial;   // [tiles][splits][64][16]
 };
+
+// u = SiLU(z + s) of one projector unit, with its bf16 hi/lo planes
+template <bool BF>
+__device__ __forceinline__ void fc1_finish(const Fc1Args<BF>& a, int b, int iu, float z) {
+  const int r = a.r;
+  const float v = z + a.s[((size_t)b * DOMINO_S + a.step) * r + iu];
+  const float uu = v * sigmoidf_(v);
+  a.u[(size_t)b * r + iu] = uu;
+  if (BF) {
+    const uint32_t hi = f32_to_bf16(uu);
+    a.u_hi[(size_t)b * r + iu] = (uint16_t)hi;
+    a.u_lo[(size_t)b * r + iu] = (uint16_t)f32_to_bf16(uu - bf16_to_f32(hi));
+  }
+}
 
 template <bool BF, int NB>
 __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args<BF> a) {
@@ -531,7 +597,7 @@ __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args<BF> a) {
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) acc[cb] = zero4();
   const W_t<BF>* pw = a.F1 + (size_t)(i0 + row) * g + q * 8;
-  for (int c = wave; c < g / 32; c += 4) {
+  for (int c = blockIdx.y * 4 + wave; c < g / 32; c += 4 * gridDim.y) {
     const int k = c * 32;
     WFrag<BF> A;
     A.load(pw + k);
@@ -550,27 +616,45 @@ __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args<BF> a) {
     for (int i = 0; i < 4; ++i) red[wave][cb][i * 64 + lane] = acc[cb][i];
   __syncthreads();
   const int l = threadIdx.x & 63, i = threadIdx.x >> 6;
-  const int iu = i0 + 4 * (l >> 4) + i;
+  const int ii = 4 * (l >> 4) + i, iu = i0 + ii;
+  const int nsplit = gridDim.y;
+  float Z[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+    Z[cb] = ((red[0][cb][threadIdx.x] + red[1][cb][threadIdx.x]) + red[2][cb][threadIdx.x]) +
+            red[3][cb][threadIdx.x];
+  if (nsplit > 1) {
+    // partial[tile][split][b][ii]; fc1_combine_kernel finishes the units
+    float* mine = a.partial + ((size_t)blockIdx.x * nsplit + blockIdx.y) * kPartGate;
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) mine[(cb * 16 + (l & 15)) * 16 + ii] = Z[cb];
+    return;
+  }
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     const int b = cb * 16 + (l & 15);
-    if (b >= a.B) continue;
-    const float z = ((red[0][cb][threadIdx.x] + red[1][cb][threadIdx.x]) + red[2][cb][threadIdx.x]) +
-                    red[3][cb][threadIdx.x];
-    const float v = z + a.s[((size_t)b * DOMINO_S + a.step) * r + iu];
-    const float uu = v * sigmoidf_(v);
-    a.u[(size_t)b * r + iu] = uu;
-    if (BF) {
-      const uint32_t hi = f32_to_bf16(uu);
-      a.u_hi[(size_t)b * r + iu] = (uint16_t)hi;
-      a.u_lo[(size_t)b * r + iu] = (uint16_t)f32_to_bf16(uu - bf16_to_f32(hi));
-    }
+    if (b < a.B) fc1_finish(a, b, iu, Z[cb]);
   }
+}
+
+template <bool BF>
+__global__ __launch_bounds__(256) void fc1_combine_kernel(Fc1Args<BF> a, int nsplit) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= a.B * a.r) return;
+  const int b = t / a.r, iu = t - b * a.r;
+  const float* p = a.partial + (size_t)(iu >> 4) * nsplit * kPartGate + b * 16 + (iu & 15);
+  float z = p[0];
+  for (int sp = 1; sp < nsplit; ++sp) z += p[(size_t)sp * kPartGate];
+  fc1_finish(a, b, iu, z);
 }
 
 template <bool BF, int NB>
 static void fc1_launch(const Fc1Args<BF>& a, hipStream_t st) {
-  hipLaunchKernelGGL((fc1_kernel<BF, NB>), dim3(a.r / 16), dim3(256), 0, st, a);
+  const int ns = a.partial ? gemv_splits(a.g) : 1;
+  hipLaunchKernelGGL((fc1_kernel<BF, NB>), dim3(a.r / 16, ns), dim3(256), 0, st, a);
+  if (ns > 1)
+    hipLaunchKernelGGL((fc1_combine_kernel<BF>), dim3((a.B * a.r + 255) / 256), dim3(256), 0, st, a,
+                       ns);
 }
 template <bool BF>
 static void fc1_dispatch(const Fc1Args<BF>& a, hipStream_t st) {
@@ -584,14 +668,16 @@ static void fc1_dispatch(const Fc1Args<BF>& a, hipStream_t st) {
 
 void launch_fc1(const Shape& s, const DeviceWeights& w, const float* h, const float* step_s,
                 int step, const Workspace& ws, int B, hipStream_t st) {
-  if (s.bf16 && B <= kRowsMaxBatch && rows_supported(s.e, s.g, s.r)) {
+  if (s.bf16 && B <= kRowsFc1MaxBatch && rows_supported(s.e, s.g, s.r)) {
     Fc1Args16 a{(const uint16_t*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r};
     launch_fc1_rows(a, st);
   } else if (s.bf16) {
-    Fc1Args<true> a{(const bf16_t*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r};
+    Fc1Args<true> a{(const bf16_t*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r,
+                    ws.partial};
     fc1_dispatch<true>(a, st);
   } else {
-    Fc1Args<false> a{(const float*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r};
+    Fc1Args<false> a{(const float*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r,
+                     nullptr};
     fc1_dispatch<false>(a, st);
   }
 }

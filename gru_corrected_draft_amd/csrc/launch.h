@@ -34,7 +34,11 @@ struct Workspace {
   uint16_t* u_lo;      // [Bmax, r]
   uint64_t* slots;     // [15, Bmax] argmax words
   int32_t* bad;        // [Bmax]
+  float* partial;      // split-k partial sums of the GRU / fc1 products
 };
+
+// most workgroups per 16-unit tile along k in the MFMA GRU / fc1 products
+constexpr int kGemvSplit = 4;
 
 constexpr int kPoolChunk = 1024;
 
@@ -81,7 +85,12 @@ struct Fc1Args16 {
   uint16_t* u_lo;
   int B, g, r;
 };
-constexpr int kRowsMaxBatch = 16;
+constexpr int kRowsMaxBatch = 16;  // the rows kernels take at most this many requests
+// measured crossovers to the split MFMA products (8B shapes: GRU rows win up
+// to 4 requests, fc1 rows up to 12)
+constexpr int kRowsGruMaxBatch = 4;
+constexpr int kRowsFc1MaxBatch = 12;
+static_assert(kRowsGruMaxBatch <= kRowsMaxBatch && kRowsFc1MaxBatch <= kRowsMaxBatch, "rows kernels");
 
 // LM-head GEMM with fused pool-score keys and first-proposal argmax (lmhead_fused.hip)
 struct FusedArgs {
@@ -110,7 +119,7 @@ void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, bool k
 // token source: exactly one of tok_i32 (element b*stride) or tok_key (argmax word b)
 void launch_gru(const Shape& s, const DeviceWeights& w, const float* h_in, float* h_out,
                 const int32_t* tok_i32, int tok_stride, const uint64_t* tok_key, int32_t* bad,
-                int B, hipStream_t st);
+                int B, const Workspace& ws, hipStream_t st);
 void launch_fc1(const Shape& s, const DeviceWeights& w, const float* h, const float* step_s,
                 int step, const Workspace& ws, int B, hipStream_t st);
 void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,

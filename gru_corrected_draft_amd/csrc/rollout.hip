@@ -200,9 +200,13 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   ws.u_lo = (uint16_t*)alloc(Bm * r * 2);
   ws.slots = (uint64_t*)alloc(DOMINO_T * Bm * 8);
   ws.bad = (int32_t*)alloc(Bm * 4);
+  // split-k partials: [16-unit tile][split][gate (GRU: 4, fc1: 1)][64 requests][16 units]
+  const size_t tiles = (g > r ? g : r) / 16;
+  ws.partial = (float*)alloc(tiles * kGemvSplit * 4 * 64 * 16 * sizeof(float));
   for (void* p : {(void*)ws.base, (void*)ws.keys, (void*)ws.hist, (void*)ws.state, (void*)ws.counts,
                   (void*)ws.pool_ids, (void*)ws.pool_base, (void*)ws.h[0], (void*)ws.h[1],
-                  (void*)ws.u, (void*)ws.u_hi, (void*)ws.u_lo, (void*)ws.slots, (void*)ws.bad}) {
+                  (void*)ws.u, (void*)ws.u_hi, (void*)ws.u_lo, (void*)ws.slots, (void*)ws.bad,
+                  (void*)ws.partial}) {
     if (!p) {
       set_global_err("create: workspace allocation failed");
       domino_rollout_destroy(h);
@@ -321,14 +325,14 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
   // two-token prefix: h = GRU(E[verified], 0); h = GRU(E[p1], h)
   {
     PhaseTimer t(h, kGru, st);
-    launch_gru(sh, h->w, nullptr, ws.h[0], ver, 1, nullptr, ws.bad, B, st);
+    launch_gru(sh, h->w, nullptr, ws.h[0], ver, 1, nullptr, ws.bad, B, ws, st);
   }
   {
     PhaseTimer t(h, kGru, st);
     if (forced)
-      launch_gru(sh, h->w, ws.h[0], ws.h[1], forced, DOMINO_T, nullptr, ws.bad, B, st);
+      launch_gru(sh, h->w, ws.h[0], ws.h[1], forced, DOMINO_T, nullptr, ws.bad, B, ws, st);
     else
-      launch_gru(sh, h->w, ws.h[0], ws.h[1], nullptr, 0, ws.slots, ws.bad, B, st);
+      launch_gru(sh, h->w, ws.h[0], ws.h[1], nullptr, 0, ws.slots, ws.bad, B, ws, st);
   }
   int cur = 1;
   for (int k = 1; k <= DOMINO_S; ++k) {
@@ -346,10 +350,11 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
     if (k < DOMINO_S) {
       PhaseTimer t(h, kGru, st);
       if (forced)
-        launch_gru(sh, h->w, ws.h[cur], ws.h[cur ^ 1], forced + k, DOMINO_T, nullptr, ws.bad, B, st);
+        launch_gru(sh, h->w, ws.h[cur], ws.h[cur ^ 1], forced + k, DOMINO_T, nullptr, ws.bad, B, ws,
+                   st);
       else
         launch_gru(sh, h->w, ws.h[cur], ws.h[cur ^ 1], nullptr, 0, ws.slots + (size_t)k * B, ws.bad,
-                   B, st);
+                   B, ws, st);
       cur ^= 1;
     }
   }

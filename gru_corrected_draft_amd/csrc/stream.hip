@@ -215,7 +215,8 @@ void dispatch(StreamArgs a, hipStream_t st) {
   const int nb = (a.ncols + 15) / 16;
   a.KS = pick_slice(a.K, a.ncols, SPLIT ? 2 : 1, 32 * 1024);
   switch (nb) {
-    case 1: launch_t<1, 2, SPLIT, EPI>(a, st); break;
+    // one column block of stores: a single row tile per wave streams faster
+    case 1: launch_t<1, EPI == kEpiStore ? 1 : 2, SPLIT, EPI>(a, st); break;
     case 2: launch_t<2, 2, SPLIT, EPI>(a, st); break;
     case 3: launch_t<3, 2, SPLIT, EPI>(a, st); break;
     case 4: launch_t<4, 2, SPLIT, EPI>(a, st); break;
@@ -240,7 +241,7 @@ void rowstream_prepare() {
 #define SET(NB, RT, SP, EP)                                                                      \
   (void)hipFuncSetAttribute((const void*)rowstream_kernel<NB, RT, SP, EP>,                       \
                             hipFuncAttributeMaxDynamicSharedMemorySize, lim)
-  SET(1, 2, false, kEpiStore); SET(2, 2, false, kEpiStore); SET(3, 2, false, kEpiStore);
+  SET(1, 1, false, kEpiStore); SET(2, 2, false, kEpiStore); SET(3, 2, false, kEpiStore);
   SET(4, 2, false, kEpiStore); SET(5, 1, false, kEpiStore); SET(6, 1, false, kEpiStore);
   SET(7, 1, false, kEpiStore); SET(8, 1, false, kEpiStore);
   SET(1, 2, true, kEpiArgmax); SET(2, 2, true, kEpiArgmax); SET(3, 2, true, kEpiArgmax);

@@ -99,6 +99,25 @@ def test_lmhead_with_many_activation_slices(B, K):
     assert np.max(np.abs(base - want)) < 1e-4
 
 
+WIDE = synth.custom_shape(2053, 256, 512, 512, 512, "bf16", 79, name="small-bf16-wide")
+
+
+@pytest.mark.parametrize("B,K", [(17, 0), (40, 100), (64, 0), (64, 300)])
+def test_gemv_split_over_workgroups(B, K):
+    """Above 16 requests the GRU and fc1 products of a 16-unit tile are split
+    over four workgroups along the reduction (512 = 16 chunks of 32) and the
+    last one to arrive adds the partials; the arrival counters reset
+    themselves, so a second run on the same handle must repeat the first."""
+    G.log(f"[gpu-test] split GEMVs B={B} K={K}")
+    tok, top, h = G.gpu_run(WIDE, B, 800 + B, 0, K, max_batch=64, max_k=2048, scales_key=STRONG)
+    ref = G.oracle_run(WIDE, B, 800 + B, 0, K, scales_key=STRONG)
+    c, _ = compare(tok, top, ref, TOL["bf16"])
+    compare(tok, top, ref, TOL["bf16"], margin_min=TIGHT_MARGIN)
+    assert c > 0
+    tok2, top2, _ = G.gpu_run(WIDE, B, 800 + B, 0, K, max_batch=64, max_k=2048, scales_key=STRONG)
+    assert np.array_equal(tok, tok2) and np.array_equal(top.view(np.uint32), top2.view(np.uint32))
+
+
 @pytest.mark.parametrize("K", [0, 64])
 def test_teacher_forced_every_step(K):
     B, seed = 6, 900
