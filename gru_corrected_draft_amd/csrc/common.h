@@ -35,6 +35,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   return u >> 16;
 }
 
+// Index of the calling wave in its workgroup.  It is the same in every lane;
+// reading it through readfirstlane lets the compiler know that, so loops and
+// branches derived from it stay scalar instead of becoming exec-masked.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ v4f zero4() { return v4f{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ v4f mfma_bf16(v8s a, v8s b, v4f c) {

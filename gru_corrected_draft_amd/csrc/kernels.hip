@@ -390,7 +390,7 @@ __device__ __forceinline__ void gru_finish(const GruArgs<BF>& a, int b, int j, f
 
 template <bool BF, int NB>
 __global__ __launch_bounds__(256) void gru_kernel(GruArgs<BF> a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
   const int j0 = blockIdx.x * 16;
   const int e = a.e, g = a.g;
@@ -589,7 +589,7 @@ __device__ __forceinline__ void fc1_finish(const Fc1Args<BF>& a, int b, int iu, 
 
 template <bool BF, int NB>
 __global__ __launch_bounds__(256) void fc1_kernel(Fc1Args<BF> a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
   const int i0 = blockIdx.x * 16;
   const int g = a.g, r = a.r;
@@ -712,7 +712,7 @@ __device__ __forceinline__ void load_u_frag(const CorrArgs<BF>& a, int b, int k,
 
 template <bool BF, int NB, int RT>
 __global__ __launch_bounds__(256) void correct_full_kernel(CorrArgs<BF> a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
   const int tile0 = (blockIdx.x * 4 + wave) * RT;
   const int V = a.V, r = a.r;
@@ -843,7 +843,7 @@ struct PoolArgs {
 
 template <bool BF, int RT>
 __global__ __launch_bounds__(256) void correct_pool_kernel(PoolArgs<BF> a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
   const int unit = blockIdx.x * 4 + wave;
   const int b = unit / a.units_per_req;
@@ -904,7 +904,7 @@ __global__ __launch_bounds__(256) void correct_pool_kernel(PoolArgs<BF> a) {
 // small batch, so parallelism matters more than reuse).
 template <int CPW>  // 32-wide k chunks per wave
 __global__ __launch_bounds__(256) void correct_pool_split_kernel(PoolArgs<true> a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
   const int tiles = (a.K + 15) / 16;
   const int b = blockIdx.x / tiles, tile = blockIdx.x % tiles;

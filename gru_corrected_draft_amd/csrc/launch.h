@@ -56,6 +56,7 @@ struct StreamArgs {
   const float* base_k;
   uint64_t* slot_k;
   int reverse;             // walk k from the end (alternated between steps)
+  int groups;              // column groups (set by the launcher)
 };
 bool rowstream_supported(int K, int ncols);
 void rowstream_prepare();

@@ -28,7 +28,7 @@ __global__ __launch_bounds__(256) void lmhead_stream_kernel(const W_t<BF>* __res
                                                             float* __restrict__ out, int V, int H,
                                                             int B) {
   const int M = B * DOMINO_T;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
   const int v0 = (blockIdx.x * 4 + wave) * 64;
   if (v0 >= V) return;  // no workgroup barrier in this kernel

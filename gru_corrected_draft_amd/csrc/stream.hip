@@ -24,15 +24,25 @@ namespace {
 enum { kEpiStore = 0, kEpiArgmax = 1 };
 
 constexpr int kSC = 128;  // k per super-chunk (4 MFMA k-slices of 32)
+constexpr bool kStraightWalk = true;
 
-template <int NB, int RT, bool SPLIT, int EPI>
+template <int NB, int RT, bool SPLIT, int EPI, int D>
 __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
   extern __shared__ __align__(16) bf16_t sact[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
-  const int N = a.N, K = a.K, KS = a.KS, ncols = a.ncols;
+  const int N = a.N, K = a.K, KS = a.KS;
   const int ldsrow = KS + 8;  // 16-byte pad per panel row
-  const int tile0 = (blockIdx.x * 4 + wave) * RT;
+  // Column groups of NB*16 activation columns: the a.groups blocks that
+  // share one set of weight rows are consecutive on one XCD (blocks j and
+  // j + 8 land on the same XCD), so all but the first read their tiles from
+  // that XCD's L2.
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int grp = local % a.groups;
+  const int rowblock = (local / a.groups) * 8 + xcd;
+  const int c0 = grp * NB * 16;
+  const int ncl = min(NB * 16, a.ncols - c0);  // columns of this block (>= 1)
+  const int tile0 = (rowblock * 4 + wave) * RT;
   const bool active = tile0 * 16 < N;
 
   const bf16_t* pa[RT];
@@ -46,14 +56,14 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) acc[t][cb] = zero4();
 
-  v8s A0[RT][4], A1[RT][4];
-  auto load_sc = [&](v8s (&A)[RT][4], int k) {
+  v8s A[D][RT][4];  // ring of D super-chunks, D - 1 of them in flight
+  auto load_sc = [&](v8s (&dst)[RT][4], int k) {
 #pragma unroll
     for (int t = 0; t < RT; ++t)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) A[t][c] = load_frag_bf16(pa[t] + k + c * 32);
+      for (int c = 0; c < 4; ++c) dst[t][c] = load_frag_bf16(pa[t] + k + c * 32);
   };
-  auto compute_sc = [&](const v8s (&A)[RT][4], int kk) {
+  auto compute_sc = [&](const v8s (&Ac)[RT][4], int kk) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       // columns past the panel read row 0 and are masked to zero afterwards
@@ -61,21 +71,21 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
         const int col = cb * 16 + row;
-        const bf16_t* src = sact + (col < ncols ? col : 0) * ldsrow + kk + c * 32 + q * 8;
+        const bf16_t* src = sact + (col < ncl ? col : 0) * ldsrow + kk + c * 32 + q * 8;
         bh[cb] = load_frag_bf16(src);
-        if (SPLIT) bl[cb] = load_frag_bf16(src + ncols * ldsrow);
+        if (SPLIT) bl[cb] = load_frag_bf16(src + ncl * ldsrow);
       }
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
-        if (cb * 16 + row >= ncols) {
+        if (cb * 16 + row >= ncl) {
           bh[cb] = zero_frag();
           if (SPLIT) bl[cb] = zero_frag();
         }
 #pragma unroll
-        for (int t = 0; t < RT; ++t) acc[t][cb] = mfma_bf16(A[t][c], bh[cb], acc[t][cb]);
+        for (int t = 0; t < RT; ++t) acc[t][cb] = mfma_bf16(Ac[t][c], bh[cb], acc[t][cb]);
         if (SPLIT) {
 #pragma unroll
-          for (int t = 0; t < RT; ++t) acc[t][cb] = mfma_bf16(A[t][c], bl[cb], acc[t][cb]);
+          for (int t = 0; t < RT; ++t) acc[t][cb] = mfma_bf16(Ac[t][c], bl[cb], acc[t][cb]);
         }
       }
     }
@@ -88,23 +98,25 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
     const int slice0 = (sc / per_slice) * KS;
     __syncthreads();  // the previous slice has been consumed
     const int per_row = KS / 8;
-    for (int idx = threadIdx.x; idx < ncols * per_row; idx += 256) {
+    for (int idx = threadIdx.x; idx < ncl * per_row; idx += 256) {
       const int c = idx / per_row, p = idx - c * per_row;
-      const int arow = a.col_B ? (c % a.col_B) * DOMINO_T + c / a.col_B : c;
+      const int m = c0 + c;
+      const int arow = a.col_B ? (m % a.col_B) * DOMINO_T + m / a.col_B : m;
       const size_t g = (size_t)arow * K + slice0 + p * 8;
       *reinterpret_cast<uint4*>(sact + c * ldsrow + p * 8) =
           *reinterpret_cast<const uint4*>(a.act_hi + g);
       if (SPLIT)
-        *reinterpret_cast<uint4*>(sact + (ncols + c) * ldsrow + p * 8) =
+        *reinterpret_cast<uint4*>(sact + (ncl + c) * ldsrow + p * 8) =
             *reinterpret_cast<const uint4*>(a.act_lo + g);
     }
     __syncthreads();
   };
 
   // Super-chunks i = 0 .. nsc-1 in order (k ascending, or descending when
-  // a.reverse is set); A0 holds the even ones and A1 the odd ones, each
-  // loaded one super-chunk ahead of its use.  A slice is staged whenever the
-  // walk enters it.
+  // a.reverse is set); super-chunk i lives in ring slot i % D and is loaded
+  // D - 1 super-chunks ahead of its use.  A slice is staged whenever the walk
+  // enters it; the first one before any weight load is issued, so that its
+  // barrier does not wait for them.
   const int nsc = K / kSC;
   const bool rev = a.reverse != 0;
   auto chunk = [&](int i) { return rev ? nsc - 1 - i : i; };
@@ -112,24 +124,42 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
     const int sc = chunk(i);
     return rev ? (sc % per_slice == per_slice - 1) : (sc % per_slice == 0);
   };
-  if (active) load_sc(A0, chunk(0) * kSC);
-  for (int i = 0; i < nsc; i += 2) {
-    if (enters_slice(i)) stage(chunk(i));
-    if (active && i + 1 < nsc) load_sc(A1, chunk(i + 1) * kSC);
-    if (active) compute_sc(A0, (chunk(i) % per_slice) * kSC);
-    if (i + 1 >= nsc) break;
-    if (enters_slice(i + 1)) stage(chunk(i + 1));
-    if (active && i + 2 < nsc) load_sc(A0, chunk(i + 2) * kSC);
-    if (active) compute_sc(A1, (chunk(i + 1) % per_slice) * kSC);
+  stage(chunk(0));
+  // Loads are unconditional (past the end they repeat the last super-chunk,
+  // an L2 hit): a skipped load on one path would make the compiler wait for
+  // every outstanding load before each super-chunk.
+#pragma unroll
+  for (int p = 0; p < D - 1; ++p) load_sc(A[p], chunk(min(p, nsc - 1)) * kSC);
+  if (kStraightWalk && per_slice == nsc && nsc % D == 0) {
+    // one slice holds all of K: a straight walk, no staging or tail inside
+    int i0 = 0;
+    do {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        load_sc(A[(d + D - 1) % D], chunk(min(i0 + d + D - 1, nsc - 1)) * kSC);
+        compute_sc(A[d], chunk(i0 + d) * kSC);
+      }
+      i0 += D;
+    } while (i0 < nsc);
+  } else {
+    for (int i0 = 0; i0 < nsc; i0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        const int i = i0 + d;
+        if (i >= nsc) break;
+        if (i > 0 && enters_slice(i)) stage(chunk(i));
+        load_sc(A[(d + D - 1) % D], chunk(min(i + D - 1, nsc - 1)) * kSC);
+        compute_sc(A[d], (chunk(i) % per_slice) * kSC);
+      }
+    }
   }
 
   if (EPI == kEpiStore) {
     if (!active) return;  // no barrier follows
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
-      const int m = cb * 16 + row;
-      if (m >= ncols) continue;
-      float* orow = a.out + (size_t)m * N;
+      if (cb * 16 + row >= ncl) continue;
+      float* orow = a.out + (size_t)(c0 + cb * 16 + row) * N;
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int v = (tile0 + t) * 16 + 4 * q;
@@ -156,8 +186,8 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       best[cb] = 0;
-      const int b = cb * 16 + row;
-      const float* brow = a.base_k + (size_t)(b < ncols ? b : 0) * N;
+      const int b = cb * 16 + row;  // column within the block
+      const float* brow = a.base_k + (size_t)(c0 + (b < ncl ? b : 0)) * N;
       float bv[RT][4];
 #pragma unroll
       for (int t = 0; t < RT; ++t)
@@ -170,7 +200,7 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
           const int c = (tile0 + t) * 16 + 4 * q + i;
           const float y = bv[t][i] + (acc[t][cb][i] + bias[t][i]);
           const uint64_t key = pack_key(y, (uint32_t)c);
-          best[cb] = (active && b < ncols && c < N) ? umax64(best[cb], key) : best[cb];
+          best[cb] = (active && b < ncl && c < N) ? umax64(best[cb], key) : best[cb];
         }
     }
 #pragma unroll
@@ -186,20 +216,252 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
     if (threadIdx.x < NB * 16) {
       const int cb = threadIdx.x >> 4, n = threadIdx.x & 15;
       const int b = cb * 16 + n;
-      if (b < ncols)
-        publish_max(&a.slot_k[b], umax64(umax64(wb[0][cb][n], wb[1][cb][n]),
+      if (b < ncl)
+        publish_max(&a.slot_k[c0 + b], umax64(umax64(wb[0][cb][n], wb[1][cb][n]),
                                          umax64(wb[2][cb][n], wb[3][cb][n])));
     }
   }
 }
 
-template <int NB, int RT, bool SPLIT, int EPI>
-void launch_t(const StreamArgs& a, hipStream_t st) {
+// Persistent correction argmax for more than 16 requests.  Requests form
+// column groups of NB*16 whose u panel (hi and lo planes over all of K)
+// stays in LDS for the whole launch; every block owns one group and a
+// strided set of row units (RT tiles of 16 fc2 rows), walked as one
+// continuous stream of 128-wide super-chunks through a ring of D register
+// buffers, so the weight stream never drains between units.  The blocks of
+// all groups that share a row unit are consecutive on one XCD and read the
+// unit through its L2.  Each wave folds its units into one packed argmax key
+// per request held in registers; the block publishes once at the end.
+template <int NB, int RT, int D, bool VEC>
+__global__ __launch_bounds__(256) void corrgroup_kernel(StreamArgs a) {
+  extern __shared__ __align__(16) bf16_t sact[];
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  const int row = lane & 15, q = lane >> 4;
+  const int N = a.N, K = a.K, G = a.groups;
+  const int ldsrow = K + 8;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int grp = local % G;
+  const int parts = gridDim.x / G;  // the grid is a multiple of 8 * G
+  const int part = (local / G) * 8 + xcd;
+  const int c0 = grp * NB * 16;
+  const int ncl = min(NB * 16, a.ncols - c0);
+
+  {  // the group's panel: hi plane rows [0, ncl), lo plane rows [ncl, 2 ncl)
+    const int per_row = K / 8;
+    for (int idx = threadIdx.x; idx < ncl * per_row; idx += 256) {
+      const int c = idx / per_row, p = idx - c * per_row;
+      const size_t g = (size_t)(c0 + c) * K + p * 8;
+      *reinterpret_cast<u32x4*>(sact + c * ldsrow + p * 8) =
+          *reinterpret_cast<const u32x4*>(a.act_hi + g);
+      *reinterpret_cast<u32x4*>(sact + (ncl + c) * ldsrow + p * 8) =
+          *reinterpret_cast<const u32x4*>(a.act_lo + g);
+    }
+    __syncthreads();
+  }
+
+  // this wave's row units: w, w + stride, ... (walked backwards when reversed)
+  const int units = ((N + 15) / 16 + RT - 1) / RT;
+  const int w = part * 4 + wave, stride = parts * 4;
+  const int my_n = units > w ? (units - w + stride - 1) / stride : 0;
+  const bool rev = a.reverse != 0;
+  const int nsc = K / kSC;
+  auto unit_of = [&](int j) { return w + (rev ? my_n - 1 - j : j) * stride; };
+  auto kchunk = [&](int ci) { return rev ? nsc - 1 - ci : ci; };
+
+  // Prefetch cursor (unit pj, chunk pci), D - 1 super-chunks ahead of the
+  // consumer.  Past this wave's last unit (or for a wave without units) the
+  // rows are clamped into [0, N), so every load stays inside fc2; such loads
+  // are never consumed.  D divides nsc, so super-chunk ci of any unit sits
+  // in ring slot ci % D.
+  int pj = 0, pci = 0;
+  v8s A[D][RT][4];
+  auto load_next = [&](v8s (&dst)[RT][4]) {
+    const int u = unit_of(pj);
+    const int k = kchunk(pci) * kSC + q * 8;
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int r = min(max((u * RT + t) * 16 + row, 0), N - 1);
+      const bf16_t* p = a.W + (size_t)r * K + k;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) dst[t][c] = load_frag_bf16(p + c * 32);
+    }
+    if (++pci == nsc) {
+      pci = 0;
+      ++pj;
+    }
+  };
+
+  v4f acc[RT][NB];
+#pragma unroll
+  for (int t = 0; t < RT; ++t)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) acc[t][cb] = zero4();
+  uint64_t best[NB];
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) best[cb] = 0;
+
+  // Loads are unconditional: a load skipped on one path would make the
+  // compiler wait for every outstanding load before each super-chunk.
+#pragma unroll
+  for (int p = 0; p < D - 1; ++p) load_next(A[p]);
+  for (int j = 0; j < my_n; ++j) {
+    const int u = unit_of(j);
+    // epilogue operands of this unit (raw bias bits, widened at use), issued
+    // ahead of the unit's remaining weight loads; VEC: N % 4 == 0 and the
+    // bias and base rows are 8- and 16-byte aligned, so the 4 rows of a lane
+    // come in one load (rows past N are clamped and masked at the fold)
+    uint32_t rbias[RT][4];
+    float ebase[NB][RT][4];
+    if (VEC) {
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const int v = min((u * RT + t) * 16 + 4 * q, N - 4);
+        const uint2 r2 = *reinterpret_cast<const uint2*>(a.b2 + v);
+        rbias[t][0] = r2.x & 0xFFFFu;
+        rbias[t][1] = r2.x >> 16;
+        rbias[t][2] = r2.y & 0xFFFFu;
+        rbias[t][3] = r2.y >> 16;
+      }
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int b = cb * 16 + row;
+        const float* brow = a.base_k + (size_t)(c0 + (b < ncl ? b : 0)) * N;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const int v = min((u * RT + t) * 16 + 4 * q, N - 4);
+          const float4 f = *reinterpret_cast<const float4*>(brow + v);
+          ebase[cb][t][0] = f.x;
+          ebase[cb][t][1] = f.y;
+          ebase[cb][t][2] = f.z;
+          ebase[cb][t][3] = f.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rbias[t][i] = a.b2[min((u * RT + t) * 16 + 4 * q + i, N - 1)];
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int b = cb * 16 + row;
+        const float* brow = a.base_k + (size_t)(c0 + (b < ncl ? b : 0)) * N;
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            ebase[cb][t][i] = brow[min((u * RT + t) * 16 + 4 * q + i, N - 1)];
+      }
+    }
+    int ci0 = 0;  // nsc >= D: at least one pass
+    do {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        load_next(A[(d + D - 1) % D]);
+        const int kk = kchunk(ci0 + d) * kSC;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          v8s bh[NB], bl[NB];
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb) {
+            const int col = cb * 16 + row;
+            const bf16_t* src = sact + (col < ncl ? col : 0) * ldsrow + kk + c * 32 + q * 8;
+            bh[cb] = load_frag_bf16(src);
+            bl[cb] = load_frag_bf16(src + ncl * ldsrow);
+            if (col >= ncl) {
+              bh[cb] = zero_frag();
+              bl[cb] = zero_frag();
+            }
+          }
+#pragma unroll
+          for (int cb = 0; cb < NB; ++cb) {
+#pragma unroll
+            for (int t = 0; t < RT; ++t) acc[t][cb] = mfma_bf16(A[d][t][c], bh[cb], acc[t][cb]);
+#pragma unroll
+            for (int t = 0; t < RT; ++t) acc[t][cb] = mfma_bf16(A[d][t][c], bl[cb], acc[t][cb]);
+          }
+        }
+      }
+      ci0 += D;
+    } while (ci0 < nsc);
+    // unit done: fold y = base + (fc2 . u + b2) into the running keys
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      const int b = cb * 16 + row;
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = (u * RT + t) * 16 + 4 * q + i;
+          const float y = ebase[cb][t][i] + (acc[t][cb][i] + bf16_to_f32(rbias[t][i]));
+          const uint64_t key = pack_key(y, (uint32_t)c);
+          best[cb] = (b < ncl && c < N) ? umax64(best[cb], key) : best[cb];
+        }
+#pragma unroll
+      for (int t = 0; t < RT; ++t) acc[t][cb] = zero4();
+    }
+  }
+
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb) {
+    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 16));
+    best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 32));
+  }
+  __shared__ uint64_t wb[4][NB][16];
+  if (q == 0)
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) wb[wave][cb][row] = best[cb];
+  __syncthreads();
+  if (threadIdx.x < NB * 16) {
+    const int cb = threadIdx.x >> 4, n = threadIdx.x & 15;
+    const int b = cb * 16 + n;
+    if (b < ncl)
+      publish_max(&a.slot_k[c0 + b], umax64(umax64(wb[0][cb][n], wb[1][cb][n]),
+                                            umax64(wb[2][cb][n], wb[3][cb][n])));
+  }
+}
+
+template <int NB, int RT, int D, bool VEC>
+void launch_group_t(const StreamArgs& a, size_t lds, hipStream_t st) {
+  static int per_cu = -1, cus = 0, per_cu_k = -1;  // resident blocks per CU at this K
+  if (per_cu < 0 || per_cu_k != a.K) {
+    per_cu_k = a.K;
+    int dev = 0, n = 0;
+    (void)hipGetDevice(&dev);
+    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, corrgroup_kernel<NB, RT, D, VEC>, 256,
+                                                     NB * 16 * 2 * (a.K + 8) * 2) != hipSuccess)
+      n = 1;
+    per_cu = n < 1 ? 1 : n;
+  }
+  // a multiple of 8 * groups blocks, about one wave of resident blocks
+  const int unit = 8 * a.groups;
+  const int want = (cus > 0 ? cus : 256) * per_cu;
+  const int grid = ((want + unit - 1) / unit) * unit;
+  hipLaunchKernelGGL((corrgroup_kernel<NB, RT, D, VEC>), dim3(grid), dim3(256), lds, st, a);
+}
+
+template <int NB, int RT, int D>
+void launch_group(StreamArgs a, hipStream_t st) {
+  a.groups = (a.ncols + NB * 16 - 1) / (NB * 16);
+  const size_t lds = (size_t)2 * min(a.ncols, NB * 16) * (a.K + 8) * sizeof(bf16_t);
+  const bool vec = a.N % 4 == 0 && a.N >= 4 && (reinterpret_cast<uintptr_t>(a.b2) & 7) == 0 &&
+                   (reinterpret_cast<uintptr_t>(a.base_k) & 15) == 0;
+  if (vec)
+    launch_group_t<NB, RT, D, true>(a, lds, st);
+  else
+    launch_group_t<NB, RT, D, false>(a, lds, st);
+}
+
+template <int NB, int RT, bool SPLIT, int EPI, int D>
+void launch_t(StreamArgs a, hipStream_t st) {
   const int tiles = (a.N + 15) / 16;
   const int waves = (tiles + RT - 1) / RT;
-  const size_t lds = (size_t)(SPLIT ? 2 : 1) * a.ncols * (a.KS + 8) * sizeof(bf16_t);
-  hipLaunchKernelGGL((rowstream_kernel<NB, RT, SPLIT, EPI>), dim3((waves + 3) / 4), dim3(256), lds,
-                     st, a);
+  const int rowblocks = (waves + 3) / 4;
+  const int cols = min(a.ncols, NB * 16);
+  a.groups = (a.ncols + NB * 16 - 1) / (NB * 16);
+  const size_t lds = (size_t)(SPLIT ? 2 : 1) * cols * (a.KS + 8) * sizeof(bf16_t);
+  hipLaunchKernelGGL((rowstream_kernel<NB, RT, SPLIT, EPI, D>),
+                     dim3(8 * a.groups * ((rowblocks + 7) / 8)), dim3(256), lds, st, a);
 }
 
 // largest multiple of 128 that divides K with the panel slice within `budget` bytes
@@ -210,20 +472,52 @@ int pick_slice(int K, int ncols, int planes, int budget) {
   return best;
 }
 
-template <bool SPLIT, int EPI>
-void dispatch(StreamArgs a, hipStream_t st) {
+// LM-head store: every column in one block, 32 KB panel slices.
+constexpr int kStoreD1 = 2;  // ring depth of the single-column-block store
+void dispatch_store(StreamArgs a, hipStream_t st) {
   const int nb = (a.ncols + 15) / 16;
-  a.KS = pick_slice(a.K, a.ncols, SPLIT ? 2 : 1, 32 * 1024);
+  a.KS = pick_slice(a.K, a.ncols, 1, 32 * 1024);
   switch (nb) {
-    // one column block of stores: a single row tile per wave streams faster
-    case 1: launch_t<1, EPI == kEpiStore ? 1 : 2, SPLIT, EPI>(a, st); break;
-    case 2: launch_t<2, 2, SPLIT, EPI>(a, st); break;
-    case 3: launch_t<3, 2, SPLIT, EPI>(a, st); break;
-    case 4: launch_t<4, 2, SPLIT, EPI>(a, st); break;
-    case 5: launch_t<5, 1, SPLIT, EPI>(a, st); break;
-    case 6: launch_t<6, 1, SPLIT, EPI>(a, st); break;
-    case 7: launch_t<7, 1, SPLIT, EPI>(a, st); break;
-    default: launch_t<8, 1, SPLIT, EPI>(a, st); break;
+    // one column block: a single row tile per wave streams faster
+    case 1: launch_t<1, 1, false, kEpiStore, kStoreD1>(a, st); break;
+    case 2: launch_t<2, 2, false, kEpiStore, 2>(a, st); break;
+    case 3: launch_t<3, 2, false, kEpiStore, 2>(a, st); break;
+    case 4: launch_t<4, 2, false, kEpiStore, 2>(a, st); break;
+    case 5: launch_t<5, 1, false, kEpiStore, 2>(a, st); break;
+    case 6: launch_t<6, 1, false, kEpiStore, 2>(a, st); break;
+    case 7: launch_t<7, 1, false, kEpiStore, 2>(a, st); break;
+    default: launch_t<8, 1, false, kEpiStore, 2>(a, st); break;
+  }
+}
+
+// Correction argmax: u is a hi/lo pair, so the whole-K panel of 32
+// requests is 132 KB (r = 1024).  Up to 16 requests run in one block per row
+// set with the panel in 32 KB slices; wider batches take the persistent
+// column-group kernel with 32-request groups when their panel fits the LDS
+// budget, else 16-request groups, else the sliced kernel.
+constexpr int kGroupRT = 2;
+constexpr int kGroupD = 2;
+constexpr int kGroupBudget = 150 * 1024;
+bool group_fits(int K, int cols) {
+  return (K / kSC) % kGroupD == 0 && (size_t)2 * cols * (K + 8) * 2 <= (size_t)kGroupBudget;
+}
+
+constexpr bool kSmallPersistent = true;
+constexpr int kSmallRT = 2;
+constexpr bool kGroup16 = false;
+void dispatch_argmax(StreamArgs a, hipStream_t st) {
+  if (a.ncols <= 16 && !(kSmallPersistent && a.col_B == 0 && group_fits(a.K, 16))) {
+    a.KS = pick_slice(a.K, a.ncols, 2, 32 * 1024);
+    launch_t<1, 2, true, kEpiArgmax, 2>(a, st);
+  } else if (a.ncols <= 16) {
+    launch_group<1, kSmallRT, kGroupD>(a, st);
+  } else if (a.col_B == 0 && group_fits(a.K, 32)) {
+    launch_group<2, kGroupRT, kGroupD>(a, st);
+  } else if (kGroup16 && a.col_B == 0 && group_fits(a.K, 16)) {
+    launch_group<1, kGroupRT, kGroupD>(a, st);
+  } else {
+    a.KS = pick_slice(a.K, min(a.ncols, 64), 2, 32 * 1024);
+    launch_t<4, 2, true, kEpiArgmax, 2>(a, st);
   }
 }
 
@@ -231,21 +525,29 @@ void dispatch(StreamArgs a, hipStream_t st) {
 
 bool rowstream_supported(int K, int ncols) { return K % kSC == 0 && ncols >= 1 && ncols <= 128; }
 
-void launch_rowstream_store(StreamArgs a, hipStream_t st) { dispatch<false, kEpiStore>(a, st); }
+void launch_rowstream_store(StreamArgs a, hipStream_t st) { dispatch_store(a, st); }
 
-void launch_rowstream_argmax(StreamArgs a, hipStream_t st) { dispatch<true, kEpiArgmax>(a, st); }
+void launch_rowstream_argmax(StreamArgs a, hipStream_t st) { dispatch_argmax(a, st); }
 
 void rowstream_prepare() {
-  // panels up to 64 KB of dynamic LDS
+  // store panels up to 64 KB of dynamic LDS, argmax panels up to the budget
   const int lim = 64 * 1024;
-#define SET(NB, RT, SP, EP)                                                                      \
-  (void)hipFuncSetAttribute((const void*)rowstream_kernel<NB, RT, SP, EP>,                       \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lim)
-  SET(1, 1, false, kEpiStore); SET(2, 2, false, kEpiStore); SET(3, 2, false, kEpiStore);
-  SET(4, 2, false, kEpiStore); SET(5, 1, false, kEpiStore); SET(6, 1, false, kEpiStore);
-  SET(7, 1, false, kEpiStore); SET(8, 1, false, kEpiStore);
-  SET(1, 2, true, kEpiArgmax); SET(2, 2, true, kEpiArgmax); SET(3, 2, true, kEpiArgmax);
-  SET(4, 2, true, kEpiArgmax); SET(5, 1, true, kEpiArgmax); SET(6, 1, true, kEpiArgmax);
-  SET(7, 1, true, kEpiArgmax); SET(8, 1, true, kEpiArgmax);
+#define SET(NB, RT, SP, EP, D, L)                                                                \
+  (void)hipFuncSetAttribute((const void*)rowstream_kernel<NB, RT, SP, EP, D>,                    \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, L)
+  SET(1, 1, false, kEpiStore, kStoreD1, lim); SET(2, 2, false, kEpiStore, 2, lim);
+  SET(3, 2, false, kEpiStore, 2, lim); SET(4, 2, false, kEpiStore, 2, lim);
+  SET(5, 1, false, kEpiStore, 2, lim); SET(6, 1, false, kEpiStore, 2, lim);
+  SET(7, 1, false, kEpiStore, 2, lim); SET(8, 1, false, kEpiStore, 2, lim);
+  SET(1, 2, true, kEpiArgmax, 2, lim); SET(4, 2, true, kEpiArgmax, 2, lim);
+#define SETG(NB, VEC)                                                                            \
+  (void)hipFuncSetAttribute((const void*)corrgroup_kernel<NB, kGroupRT, kGroupD, VEC>,           \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kGroupBudget)
+  SETG(2, true); SETG(2, false); SETG(1, true); SETG(1, false);
+#undef SETG
+  (void)hipFuncSetAttribute((const void*)corrgroup_kernel<1, kSmallRT, kGroupD, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kGroupBudget);
+  (void)hipFuncSetAttribute((const void*)corrgroup_kernel<1, kSmallRT, kGroupD, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kGroupBudget);
 #undef SET
 }
