@@ -57,6 +57,7 @@ struct StreamArgs {
   uint64_t* slot_k;
   int reverse;             // walk k from the end (alternated between steps)
   int groups;              // column groups (set by the launcher)
+  int gcols;               // columns per group (set by the launcher)
 };
 bool rowstream_supported(int K, int ncols);
 void rowstream_prepare();
@@ -102,7 +103,10 @@ struct FusedArgs {
   uint64_t* slots;     // argmax words of position 0 [B]
   int V, H, B;
 };
-constexpr int kFusedMinBatch = 2;
+// Below this batch the LM-head streams lm_head once through the row kernel
+// (more workgroups, measured faster up to 4 requests); from it on, the fused
+// GEMM with the pool-key and first-proposal epilogue.
+constexpr int kFusedMinBatch = 5;
 void lmhead_fused_prepare();
 bool lmhead_fused_supported(int H);
 void launch_lmhead_fused(const FusedArgs& a, hipStream_t st);

@@ -47,6 +47,64 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Epilogue shared by both kernels: store base, the pool score keys and the
+// position-0 argmax of the workgroup's 256 rows x 16 requests.
+__device__ __forceinline__ void fused_epilogue(const FusedArgs& a, const v4f (&acc)[4][DOMINO_T],
+                                               unsigned char* ring, int v0, int b0, int wave,
+                                               int row, int q, int tid) {
+  const int V = a.V, B = a.B;
+  const int b = b0 + row;
+  const bool bok = b < B;
+  const bool vec = (V & 3) == 0;
+  uint64_t best0 = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int v = v0 + wave * 64 + r * 16 + 4 * q;
+    const bool full = vec && v + 3 < V;
+#pragma unroll
+    for (int t = 0; t < DOMINO_T; ++t) {
+      if (!bok) break;
+      float* o = a.base + ((size_t)t * B + b) * V + v;
+      if (full) {
+        *reinterpret_cast<float4*>(o) = make_float4(acc[r][t][0], acc[r][t][1], acc[r][t][2], acc[r][t][3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (v + i < V) o[i] = acc[r][t][i];
+      }
+    }
+    uint32_t kk[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = acc[r][0][i];
+#pragma unroll
+      for (int t = 1; t < DOMINO_T; ++t) m = fmaxf(m, acc[r][t][i]);
+      kk[i] = orderable(m);
+      const uint64_t k0 = pack_key(acc[r][0][i], (uint32_t)(v + i));
+      best0 = (v + i < V) ? umax64(best0, k0) : best0;
+    }
+    if (a.keys && bok) {
+      uint32_t* kp = a.keys + (size_t)b * V + v;
+      if (full) {
+        *reinterpret_cast<uint4*>(kp) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (v + i < V) kp[i] = kk[i];
+      }
+    }
+  }
+  // first proposal: lanes row, row+16, row+32, row+48 hold request b
+  best0 = umax64(best0, shfl_xor_u64(best0, 16));
+  best0 = umax64(best0, shfl_xor_u64(best0, 32));
+  uint64_t (*wb)[16] = reinterpret_cast<uint64_t (*)[16]>(ring);
+  if (q == 0) wb[wave][row] = best0;
+  __syncthreads();
+  if (tid < 16 && b0 + tid < B)
+    publish_max(&a.slots[b0 + tid],
+                umax64(umax64(wb[0][tid], wb[1][tid]), umax64(wb[2][tid], wb[3][tid])));
+}
+
 __global__ __launch_bounds__(256) void lmhead_fused_kernel(FusedArgs a) {
   const int V = a.V, H = a.H, B = a.B;
   const int nvt = (V + kBN - 1) / kBN, ngrp = (B + kBJ - 1) / kBJ;
@@ -61,7 +119,7 @@ __global__ __launch_bounds__(256) void lmhead_fused_kernel(FusedArgs a) {
   // that lane's MFMA fragment (row/column l % 16, k = 8 * (l / 16) .. +7).
   extern __shared__ __align__(1024) unsigned char ring[];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
 
   // this wave's copy duties per slice: A blocks wave*4 .. +3 and B blocks
@@ -119,60 +177,11 @@ __global__ __launch_bounds__(256) void lmhead_fused_kernel(FusedArgs a) {
   }
   lds_barrier();  // the ring is free again
 
-  // ------------------------------------------------------------- epilogue
-  const int b = b0 + row;
-  const bool bok = b < B;
-  const bool vec = (V & 3) == 0;
-  uint64_t best0 = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int v = v0 + wave * 64 + r * 16 + 4 * q;
-    const bool full = vec && v + 3 < V;
-#pragma unroll
-    for (int t = 0; t < DOMINO_T; ++t) {
-      if (!bok) break;
-      float* o = a.base + ((size_t)t * B + b) * V + v;
-      if (full) {
-        *reinterpret_cast<float4*>(o) = make_float4(acc[r][t][0], acc[r][t][1], acc[r][t][2], acc[r][t][3]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (v + i < V) o[i] = acc[r][t][i];
-      }
-    }
-    uint32_t kk[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float m = acc[r][0][i];
-#pragma unroll
-      for (int t = 1; t < DOMINO_T; ++t) m = fmaxf(m, acc[r][t][i]);
-      kk[i] = orderable(m);
-      const uint64_t k0 = pack_key(acc[r][0][i], (uint32_t)(v + i));
-      best0 = (v + i < V) ? umax64(best0, k0) : best0;
-    }
-    if (a.keys && bok) {
-      uint32_t* kp = a.keys + (size_t)b * V + v;
-      if (full) {
-        *reinterpret_cast<uint4*>(kp) = make_uint4(kk[0], kk[1], kk[2], kk[3]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (v + i < V) kp[i] = kk[i];
-      }
-    }
-  }
-  // first proposal: lanes row, row+16, row+32, row+48 hold request b
-  best0 = umax64(best0, shfl_xor_u64(best0, 16));
-  best0 = umax64(best0, shfl_xor_u64(best0, 32));
-  uint64_t (*wb)[16] = reinterpret_cast<uint64_t (*)[16]>(ring);
-  if (q == 0) wb[wave][row] = best0;
-  __syncthreads();
-  if (tid < 16 && b0 + tid < B)
-    publish_max(&a.slots[b0 + tid],
-                umax64(umax64(wb[0][tid], wb[1][tid]), umax64(wb[2][tid], wb[3][tid])));
+  fused_epilogue(a, acc, ring, v0, b0, wave, row, q, tid);
 }
 
 constexpr size_t kLds = (size_t)kStages * kSliceBytes;
+
 
 }  // namespace
 

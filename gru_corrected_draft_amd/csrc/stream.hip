@@ -223,17 +223,18 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
   }
 }
 
-// Persistent correction argmax for more than 16 requests.  Requests form
-// column groups of NB*16 whose u panel (hi and lo planes over all of K)
-// stays in LDS for the whole launch; every block owns one group and a
-// strided set of row units (RT tiles of 16 fc2 rows), walked as one
-// continuous stream of 128-wide super-chunks through a ring of D register
-// buffers, so the weight stream never drains between units.  The blocks of
-// all groups that share a row unit are consecutive on one XCD and read the
-// unit through its L2.  Each wave folds its units into one packed argmax key
-// per request held in registers; the block publishes once at the end.
-template <int NB, int RT, int D, bool VEC>
-__global__ __launch_bounds__(256) void corrgroup_kernel(StreamArgs a) {
+// Persistent row stream.  Activation columns form groups of NB*16 whose
+// panel (SPLIT: hi and lo planes) over all of K stays in LDS for the whole
+// launch; every block owns one group and a strided set of row units (RT
+// tiles of 16 weight rows), walked as one continuous stream of 128-wide
+// super-chunks through a ring of D register buffers, so the weight stream
+// never drains between units.  The blocks of all groups that share a row
+// unit are consecutive on one XCD and read the unit through its L2.
+// Epilogues: store the unit's logits (LM-head), or fold y = base + (W.u + b2)
+// into one packed argmax key per request held in registers, published once
+// per block at the end (correction).
+template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI>
+__global__ __launch_bounds__(256) void rowpersist_kernel(StreamArgs a) {
   extern __shared__ __align__(16) bf16_t sact[];
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
@@ -243,18 +244,21 @@ __global__ __launch_bounds__(256) void corrgroup_kernel(StreamArgs a) {
   const int grp = local % G;
   const int parts = gridDim.x / G;  // the grid is a multiple of 8 * G
   const int part = (local / G) * 8 + xcd;
-  const int c0 = grp * NB * 16;
-  const int ncl = min(NB * 16, a.ncols - c0);
+  const int c0 = grp * a.gcols;
+  const int ncl = min(a.gcols, a.ncols - c0);  // 1 .. NB * 16
 
   {  // the group's panel: hi plane rows [0, ncl), lo plane rows [ncl, 2 ncl)
     const int per_row = K / 8;
     for (int idx = threadIdx.x; idx < ncl * per_row; idx += 256) {
       const int c = idx / per_row, p = idx - c * per_row;
-      const size_t g = (size_t)(c0 + c) * K + p * 8;
+      const int m = c0 + c;
+      const int arow = a.col_B ? (m % a.col_B) * DOMINO_T + m / a.col_B : m;
+      const size_t g = (size_t)arow * K + p * 8;
       *reinterpret_cast<u32x4*>(sact + c * ldsrow + p * 8) =
           *reinterpret_cast<const u32x4*>(a.act_hi + g);
-      *reinterpret_cast<u32x4*>(sact + (ncl + c) * ldsrow + p * 8) =
-          *reinterpret_cast<const u32x4*>(a.act_lo + g);
+      if (SPLIT)
+        *reinterpret_cast<u32x4*>(sact + (ncl + c) * ldsrow + p * 8) =
+            *reinterpret_cast<const u32x4*>(a.act_lo + g);
     }
     __syncthreads();
   }
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(256) void corrgroup_kernel(StreamArgs a) {
 
   // Prefetch cursor (unit pj, chunk pci), D - 1 super-chunks ahead of the
   // consumer.  Past this wave's last unit (or for a wave without units) the
-  // rows are clamped into [0, N), so every load stays inside fc2; such loads
+  // rows are clamped into [0, N), so every load stays inside W; such loads
   // are never consumed.  D divides nsc, so super-chunk ci of any unit sits
   // in ring slot ci % D.
   int pj = 0, pci = 0;
@@ -306,13 +310,13 @@ __global__ __launch_bounds__(256) void corrgroup_kernel(StreamArgs a) {
   for (int p = 0; p < D - 1; ++p) load_next(A[p]);
   for (int j = 0; j < my_n; ++j) {
     const int u = unit_of(j);
-    // epilogue operands of this unit (raw bias bits, widened at use), issued
-    // ahead of the unit's remaining weight loads; VEC: N % 4 == 0 and the
-    // bias and base rows are 8- and 16-byte aligned, so the 4 rows of a lane
-    // come in one load (rows past N are clamped and masked at the fold)
+    // argmax epilogue operands of this unit (raw bias bits, widened at use),
+    // issued ahead of the unit's remaining weight loads; VEC: N % 4 == 0 and
+    // the bias and base rows are 8- and 16-byte aligned, so the 4 rows of a
+    // lane come in one load (rows past N are clamped and masked at the fold)
     uint32_t rbias[RT][4];
     float ebase[NB][RT][4];
-    if (VEC) {
+    if (EPI == kEpiArgmax && VEC) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int v = min((u * RT + t) * 16 + 4 * q, N - 4);
@@ -336,7 +340,7 @@ __global__ __launch_bounds__(256) void corrgroup_kernel(StreamArgs a) {
           ebase[cb][t][3] = f.w;
         }
       }
-    } else {
+    } else if (EPI == kEpiArgmax) {
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -366,40 +370,60 @@ __global__ __launch_bounds__(256) void corrgroup_kernel(StreamArgs a) {
             const int col = cb * 16 + row;
             const bf16_t* src = sact + (col < ncl ? col : 0) * ldsrow + kk + c * 32 + q * 8;
             bh[cb] = load_frag_bf16(src);
-            bl[cb] = load_frag_bf16(src + ncl * ldsrow);
+            if (SPLIT) bl[cb] = load_frag_bf16(src + ncl * ldsrow);
             if (col >= ncl) {
               bh[cb] = zero_frag();
-              bl[cb] = zero_frag();
+              if (SPLIT) bl[cb] = zero_frag();
             }
           }
 #pragma unroll
           for (int cb = 0; cb < NB; ++cb) {
 #pragma unroll
             for (int t = 0; t < RT; ++t) acc[t][cb] = mfma_bf16(A[d][t][c], bh[cb], acc[t][cb]);
+            if (SPLIT) {
 #pragma unroll
-            for (int t = 0; t < RT; ++t) acc[t][cb] = mfma_bf16(A[d][t][c], bl[cb], acc[t][cb]);
+              for (int t = 0; t < RT; ++t) acc[t][cb] = mfma_bf16(A[d][t][c], bl[cb], acc[t][cb]);
+            }
           }
         }
       }
       ci0 += D;
     } while (ci0 < nsc);
-    // unit done: fold y = base + (fc2 . u + b2) into the running keys
+    // unit done
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
       const int b = cb * 16 + row;
+      if (EPI == kEpiArgmax) {
 #pragma unroll
-      for (int t = 0; t < RT; ++t)
+        for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int c = (u * RT + t) * 16 + 4 * q + i;
-          const float y = ebase[cb][t][i] + (acc[t][cb][i] + bf16_to_f32(rbias[t][i]));
-          const uint64_t key = pack_key(y, (uint32_t)c);
-          best[cb] = (b < ncl && c < N) ? umax64(best[cb], key) : best[cb];
+          for (int i = 0; i < 4; ++i) {
+            const int c = (u * RT + t) * 16 + 4 * q + i;
+            const float y = ebase[cb][t][i] + (acc[t][cb][i] + bf16_to_f32(rbias[t][i]));
+            const uint64_t key = pack_key(y, (uint32_t)c);
+            best[cb] = (b < ncl && c < N) ? umax64(best[cb], key) : best[cb];
+          }
+      } else if (b < ncl) {
+        float* orow = a.out + (size_t)(c0 + b) * N;
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+          const int v = (u * RT + t) * 16 + 4 * q;
+          if (VEC) {
+            if (v < N)
+              *reinterpret_cast<float4*>(orow + v) =
+                  make_float4(acc[t][cb][0], acc[t][cb][1], acc[t][cb][2], acc[t][cb][3]);
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (v + i < N) orow[v + i] = acc[t][cb][i];
+          }
         }
+      }
 #pragma unroll
       for (int t = 0; t < RT; ++t) acc[t][cb] = zero4();
     }
   }
+  if (EPI != kEpiArgmax) return;  // no barrier follows
 
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
@@ -420,16 +444,17 @@ __global__ __launch_bounds__(256) void corrgroup_kernel(StreamArgs a) {
   }
 }
 
-template <int NB, int RT, int D, bool VEC>
-void launch_group_t(const StreamArgs& a, size_t lds, hipStream_t st) {
-  static int per_cu = -1, cus = 0, per_cu_k = -1;  // resident blocks per CU at this K
-  if (per_cu < 0 || per_cu_k != a.K) {
-    per_cu_k = a.K;
+template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI>
+void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
+  static int per_cu = -1, cus = 0;  // resident blocks per CU at this panel size
+  static size_t per_cu_lds = 0;
+  if (per_cu < 0 || per_cu_lds != lds) {
+    per_cu_lds = lds;
     int dev = 0, n = 0;
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, corrgroup_kernel<NB, RT, D, VEC>, 256,
-                                                     NB * 16 * 2 * (a.K + 8) * 2) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI>, 256, lds) != hipSuccess)
       n = 1;
     per_cu = n < 1 ? 1 : n;
   }
@@ -437,19 +462,30 @@ void launch_group_t(const StreamArgs& a, size_t lds, hipStream_t st) {
   const int unit = 8 * a.groups;
   const int want = (cus > 0 ? cus : 256) * per_cu;
   const int grid = ((want + unit - 1) / unit) * unit;
-  hipLaunchKernelGGL((corrgroup_kernel<NB, RT, D, VEC>), dim3(grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI>), dim3(grid), dim3(256), lds,
+                     st, a);
 }
 
-template <int NB, int RT, int D>
-void launch_group(StreamArgs a, hipStream_t st) {
-  a.groups = (a.ncols + NB * 16 - 1) / (NB * 16);
-  const size_t lds = (size_t)2 * min(a.ncols, NB * 16) * (a.K + 8) * sizeof(bf16_t);
-  const bool vec = a.N % 4 == 0 && a.N >= 4 && (reinterpret_cast<uintptr_t>(a.b2) & 7) == 0 &&
-                   (reinterpret_cast<uintptr_t>(a.base_k) & 15) == 0;
+// panel bytes of one group of `cols` columns over all of K
+size_t persist_lds(int K, int cols, bool split) {
+  return (size_t)(split ? 2 : 1) * cols * (K + 8) * sizeof(bf16_t);
+}
+
+// gcols: activation columns per group (at most NB * 16)
+template <int NB, int RT, int D, bool SPLIT, int EPI>
+void launch_persist(StreamArgs a, int gcols, hipStream_t st) {
+  a.gcols = gcols;
+  a.groups = (a.ncols + gcols - 1) / gcols;
+  const size_t lds = persist_lds(a.K, min(a.ncols, gcols), SPLIT);
+  const bool vec =
+      a.N % 4 == 0 && a.N >= 4 &&
+      (EPI == kEpiArgmax ? ((reinterpret_cast<uintptr_t>(a.b2) & 7) == 0 &&
+                            (reinterpret_cast<uintptr_t>(a.base_k) & 15) == 0)
+                         : (reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
   if (vec)
-    launch_group_t<NB, RT, D, true>(a, lds, st);
+    launch_persist_t<NB, RT, D, true, SPLIT, EPI>(a, lds, st);
   else
-    launch_group_t<NB, RT, D, false>(a, lds, st);
+    launch_persist_t<NB, RT, D, false, SPLIT, EPI>(a, lds, st);
 }
 
 template <int NB, int RT, bool SPLIT, int EPI, int D>
@@ -472,14 +508,25 @@ int pick_slice(int K, int ncols, int planes, int budget) {
   return best;
 }
 
-// LM-head store: every column in one block, 32 KB panel slices.
-constexpr int kStoreD1 = 2;  // ring depth of the single-column-block store
+// Persistent launches keep a group's whole-K panel within this LDS budget
+// and need the ring depth to divide the super-chunk count.
+constexpr int kPersistBudget = 150 * 1024;
+template <int D>
+bool persist_fits(int K, int cols, bool split) {
+  return (K / kSC) % D == 0 && persist_lds(K, cols, split) <= (size_t)kPersistBudget;
+}
+
+// LM-head store: every column in one block, panel slices within
+// kStoreBudget.  (A persistent whole-K panel allows one block per CU at
+// H = 4096 and streams slower.)
+constexpr int kStoreBudget = 32 * 1024;
+constexpr int kStoreD = 3;
 void dispatch_store(StreamArgs a, hipStream_t st) {
   const int nb = (a.ncols + 15) / 16;
-  a.KS = pick_slice(a.K, a.ncols, 1, 32 * 1024);
+  a.KS = pick_slice(a.K, a.ncols, 1, kStoreBudget);
   switch (nb) {
     // one column block: a single row tile per wave streams faster
-    case 1: launch_t<1, 1, false, kEpiStore, kStoreD1>(a, st); break;
+    case 1: launch_t<1, 1, false, kEpiStore, kStoreD>(a, st); break;
     case 2: launch_t<2, 2, false, kEpiStore, 2>(a, st); break;
     case 3: launch_t<3, 2, false, kEpiStore, 2>(a, st); break;
     case 4: launch_t<4, 2, false, kEpiStore, 2>(a, st); break;
@@ -490,31 +537,19 @@ void dispatch_store(StreamArgs a, hipStream_t st) {
   }
 }
 
-// Correction argmax: u is a hi/lo pair, so the whole-K panel of 32
-// requests is 132 KB (r = 1024).  Up to 16 requests run in one block per row
-// set with the panel in 32 KB slices; wider batches take the persistent
-// column-group kernel with 32-request groups when their panel fits the LDS
-// budget, else 16-request groups, else the sliced kernel.
-constexpr int kGroupRT = 2;
-constexpr int kGroupD = 2;
-constexpr int kGroupBudget = 150 * 1024;
-bool group_fits(int K, int cols) {
-  return (K / kSC) % kGroupD == 0 && (size_t)2 * cols * (K + 8) * 2 <= (size_t)kGroupBudget;
-}
-
-constexpr bool kSmallPersistent = true;
-constexpr int kSmallRT = 2;
-constexpr bool kGroup16 = false;
+// Correction argmax (u as a hi/lo pair): up to 16 requests, and wider
+// batches in 32-request groups (132 KB panel at r = 1024), take the
+// persistent stream; panels that do not fit run the sliced kernel.
+constexpr int kArgmaxRT = 2;
+constexpr int kArgmaxD = 2;
 void dispatch_argmax(StreamArgs a, hipStream_t st) {
-  if (a.ncols <= 16 && !(kSmallPersistent && a.col_B == 0 && group_fits(a.K, 16))) {
+  if (a.ncols <= 16 && persist_fits<kArgmaxD>(a.K, a.ncols, true)) {
+    launch_persist<1, kArgmaxRT, kArgmaxD, true, kEpiArgmax>(a, a.ncols, st);
+  } else if (a.ncols <= 16) {
     a.KS = pick_slice(a.K, a.ncols, 2, 32 * 1024);
     launch_t<1, 2, true, kEpiArgmax, 2>(a, st);
-  } else if (a.ncols <= 16) {
-    launch_group<1, kSmallRT, kGroupD>(a, st);
-  } else if (a.col_B == 0 && group_fits(a.K, 32)) {
-    launch_group<2, kGroupRT, kGroupD>(a, st);
-  } else if (kGroup16 && a.col_B == 0 && group_fits(a.K, 16)) {
-    launch_group<1, kGroupRT, kGroupD>(a, st);
+  } else if (persist_fits<kArgmaxD>(a.K, 32, true)) {
+    launch_persist<2, kArgmaxRT, kArgmaxD, true, kEpiArgmax>(a, 32, st);
   } else {
     a.KS = pick_slice(a.K, min(a.ncols, 64), 2, 32 * 1024);
     launch_t<4, 2, true, kEpiArgmax, 2>(a, st);
@@ -530,24 +565,23 @@ void launch_rowstream_store(StreamArgs a, hipStream_t st) { dispatch_store(a, st
 void launch_rowstream_argmax(StreamArgs a, hipStream_t st) { dispatch_argmax(a, st); }
 
 void rowstream_prepare() {
-  // store panels up to 64 KB of dynamic LDS, argmax panels up to the budget
+  // sliced panels up to 64 KB of dynamic LDS, persistent panels up to the budget
   const int lim = 64 * 1024;
-#define SET(NB, RT, SP, EP, D, L)                                                                \
+#define SET(NB, RT, SP, EP, D)                                                                   \
   (void)hipFuncSetAttribute((const void*)rowstream_kernel<NB, RT, SP, EP, D>,                    \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, L)
-  SET(1, 1, false, kEpiStore, kStoreD1, lim); SET(2, 2, false, kEpiStore, 2, lim);
-  SET(3, 2, false, kEpiStore, 2, lim); SET(4, 2, false, kEpiStore, 2, lim);
-  SET(5, 1, false, kEpiStore, 2, lim); SET(6, 1, false, kEpiStore, 2, lim);
-  SET(7, 1, false, kEpiStore, 2, lim); SET(8, 1, false, kEpiStore, 2, lim);
-  SET(1, 2, true, kEpiArgmax, 2, lim); SET(4, 2, true, kEpiArgmax, 2, lim);
-#define SETG(NB, VEC)                                                                            \
-  (void)hipFuncSetAttribute((const void*)corrgroup_kernel<NB, kGroupRT, kGroupD, VEC>,           \
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kGroupBudget)
-  SETG(2, true); SETG(2, false); SETG(1, true); SETG(1, false);
-#undef SETG
-  (void)hipFuncSetAttribute((const void*)corrgroup_kernel<1, kSmallRT, kGroupD, true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kGroupBudget);
-  (void)hipFuncSetAttribute((const void*)corrgroup_kernel<1, kSmallRT, kGroupD, false>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kGroupBudget);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lim)
+  SET(1, 1, false, kEpiStore, kStoreD); SET(2, 2, false, kEpiStore, 2);
+  SET(3, 2, false, kEpiStore, 2); SET(4, 2, false, kEpiStore, 2);
+  SET(5, 1, false, kEpiStore, 2); SET(6, 1, false, kEpiStore, 2);
+  SET(7, 1, false, kEpiStore, 2); SET(8, 1, false, kEpiStore, 2);
+  SET(1, 2, true, kEpiArgmax, 2); SET(4, 2, true, kEpiArgmax, 2);
 #undef SET
+#define SETP(NB, RT, D, VEC, SP, EP)                                                             \
+  (void)hipFuncSetAttribute((const void*)rowpersist_kernel<NB, RT, D, VEC, SP, EP>,              \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPersistBudget)
+  SETP(1, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax);
+  SETP(1, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax);
+  SETP(2, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax);
+  SETP(2, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax);
+#undef SETP
 }
