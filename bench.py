@@ -9,9 +9,10 @@ at batch 1 with full-vocabulary correction (K = 0); ``--workload`` and
 2048, 27B-class at B = 64).
 
 Prints one JSON line: ms per block (lower is better), the roofline figure of
-the dominant kernel (live HIP-event durations of each launch of that kernel
-in eager runs right after the timed region, on the launch stream), and the
-CPU oracle's time on a bounded sample of the same workload.
+the dominant kernel (its average duration from HIP events stamped by each of
+its launches' own dispatch, in eager runs right after the timed region on the
+same stream), and the CPU oracle's time on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -181,7 +182,7 @@ def main():
     ms_step = ms_total / args.steps
     assert torch.equal(out_t, ref_tokens), "graph replays disagree"
 
-    # per-kernel durations: HIP events around each launch, eager runs, same stream
+    # per-kernel durations: HIP events stamped by each kernel's dispatch, eager runs, same stream
     h.set_timing(True)
     h.reset_kernel_times()
     for _ in range(args.steps):

@@ -114,7 +114,7 @@ __global__ void reset_kernel(uint64_t* slots, int nslots, uint32_t* hist, int nh
 
 void launch_reset(const Workspace& ws, int B, int K, hipStream_t st) {
   const int nslots = DOMINO_T * B, nhist = B * 3 * 2048;
-  hipLaunchKernelGGL(reset_kernel, dim3(64), dim3(256), 0, st, ws.slots, nslots, ws.hist, nhist,
+  DLAUNCH(reset_kernel, dim3(64), dim3(256), 0, st, ws.slots, nslots, ws.hist, nhist,
                      ws.state, ws.bad, B, K);
 }
 
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void row0_argmax_kernel(const float* __restric
 }
 
 void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st) {
-  hipLaunchKernelGGL(row0_argmax_kernel, dim3((s.V + 2047) / 2048, B), dim3(256), 0, st, base, s.V,
+  DLAUNCH(row0_argmax_kernel, dim3((s.V + 2047) / 2048, B), dim3(256), 0, st, base, s.V,
                      slots);
 }
 
@@ -340,16 +340,16 @@ void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, bool k
   const int nch = (s.V + kPoolChunk - 1) / kPoolChunk;
   const dim3 grid(nch, B), blk(256);
   if (keys_ready)
-    hipLaunchKernelGGL(pool_hist_kernel<0>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+    DLAUNCH(pool_hist_kernel<0>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
   else
-    hipLaunchKernelGGL(pool_score_hist_kernel, grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
-  hipLaunchKernelGGL(pool_select_kernel<0>, dim3(B), blk, 0, st, ws.hist, ws.state);
-  hipLaunchKernelGGL(pool_hist_kernel<1>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
-  hipLaunchKernelGGL(pool_select_kernel<1>, dim3(B), blk, 0, st, ws.hist, ws.state);
-  hipLaunchKernelGGL(pool_hist_kernel<2>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
-  hipLaunchKernelGGL(pool_select_kernel<2>, dim3(B), blk, 0, st, ws.hist, ws.state);
-  hipLaunchKernelGGL(pool_count_kernel, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.counts, nch);
-  hipLaunchKernelGGL(pool_compact_kernel, grid, blk, 0, st, ws.keys, ws.base, s.V, B, K, ws.state,
+    DLAUNCH(pool_score_hist_kernel, grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
+  DLAUNCH(pool_select_kernel<0>, dim3(B), blk, 0, st, ws.hist, ws.state);
+  DLAUNCH(pool_hist_kernel<1>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+  DLAUNCH(pool_select_kernel<1>, dim3(B), blk, 0, st, ws.hist, ws.state);
+  DLAUNCH(pool_hist_kernel<2>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+  DLAUNCH(pool_select_kernel<2>, dim3(B), blk, 0, st, ws.hist, ws.state);
+  DLAUNCH(pool_count_kernel, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.counts, nch);
+  DLAUNCH(pool_compact_kernel, grid, blk, 0, st, ws.keys, ws.base, s.V, B, K, ws.state,
                      ws.counts, nch, ws.pool_ids, ws.pool_base);
 }
 
@@ -523,9 +523,9 @@ static int gemv_splits(int kdim) {
 template <bool BF, int NB>
 static void gru_launch(const GruArgs<BF>& a, hipStream_t st) {
   const int ns = a.partial ? gemv_splits(a.e < a.g ? a.e : a.g) : 1;
-  hipLaunchKernelGGL((gru_kernel<BF, NB>), dim3(a.g / 16, ns), dim3(256), 0, st, a);
+  DLAUNCH((gru_kernel<BF, NB>), dim3(a.g / 16, ns), dim3(256), 0, st, a);
   if (ns > 1)
-    hipLaunchKernelGGL((gru_combine_kernel<BF>), dim3((a.B * a.g + 255) / 256), dim3(256), 0, st, a,
+    DLAUNCH((gru_combine_kernel<BF>), dim3((a.B * a.g + 255) / 256), dim3(256), 0, st, a,
                        ns);
 }
 
@@ -651,9 +651,9 @@ __global__ __launch_bounds__(256) void fc1_combine_kernel(Fc1Args<BF> a, int nsp
 template <bool BF, int NB>
 static void fc1_launch(const Fc1Args<BF>& a, hipStream_t st) {
   const int ns = a.partial ? gemv_splits(a.g) : 1;
-  hipLaunchKernelGGL((fc1_kernel<BF, NB>), dim3(a.r / 16, ns), dim3(256), 0, st, a);
+  DLAUNCH((fc1_kernel<BF, NB>), dim3(a.r / 16, ns), dim3(256), 0, st, a);
   if (ns > 1)
-    hipLaunchKernelGGL((fc1_combine_kernel<BF>), dim3((a.B * a.r + 255) / 256), dim3(256), 0, st, a,
+    DLAUNCH((fc1_combine_kernel<BF>), dim3((a.B * a.r + 255) / 256), dim3(256), 0, st, a,
                        ns);
 }
 template <bool BF>
@@ -793,7 +793,7 @@ template <bool BF, int NB>
 static void correct_full_launch(const CorrArgs<BF>& a, hipStream_t st) {
   const int tiles = (a.V + 15) / 16;
   const int units = (tiles + kCorrRT - 1) / kCorrRT;
-  hipLaunchKernelGGL((correct_full_kernel<BF, NB, kCorrRT>), dim3((units + 3) / 4), dim3(256), 0,
+  DLAUNCH((correct_full_kernel<BF, NB, kCorrRT>), dim3((units + 3) / 4), dim3(256), 0,
                      st, a);
 }
 template <bool BF>
@@ -965,27 +965,27 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
                      ws.u_lo, slot_k, B, K, s.r, s.V, upr};
     const dim3 g2((unsigned)(B * tiles));
     switch ((s.r / 32 + 3) / 4) {
-      case 1: hipLaunchKernelGGL((correct_pool_split_kernel<1>), g2, dim3(256), 0, st, a); break;
-      case 2: hipLaunchKernelGGL((correct_pool_split_kernel<2>), g2, dim3(256), 0, st, a); break;
-      case 3: hipLaunchKernelGGL((correct_pool_split_kernel<3>), g2, dim3(256), 0, st, a); break;
-      case 4: hipLaunchKernelGGL((correct_pool_split_kernel<4>), g2, dim3(256), 0, st, a); break;
-      case 5: hipLaunchKernelGGL((correct_pool_split_kernel<5>), g2, dim3(256), 0, st, a); break;
-      case 6: hipLaunchKernelGGL((correct_pool_split_kernel<6>), g2, dim3(256), 0, st, a); break;
-      case 7: hipLaunchKernelGGL((correct_pool_split_kernel<7>), g2, dim3(256), 0, st, a); break;
-      case 8: hipLaunchKernelGGL((correct_pool_split_kernel<8>), g2, dim3(256), 0, st, a); break;
-      case 9: hipLaunchKernelGGL((correct_pool_split_kernel<9>), g2, dim3(256), 0, st, a); break;
-      case 10: hipLaunchKernelGGL((correct_pool_split_kernel<10>), g2, dim3(256), 0, st, a); break;
-      case 11: hipLaunchKernelGGL((correct_pool_split_kernel<11>), g2, dim3(256), 0, st, a); break;
-      default: hipLaunchKernelGGL((correct_pool_split_kernel<12>), g2, dim3(256), 0, st, a); break;
+      case 1: DLAUNCH((correct_pool_split_kernel<1>), g2, dim3(256), 0, st, a); break;
+      case 2: DLAUNCH((correct_pool_split_kernel<2>), g2, dim3(256), 0, st, a); break;
+      case 3: DLAUNCH((correct_pool_split_kernel<3>), g2, dim3(256), 0, st, a); break;
+      case 4: DLAUNCH((correct_pool_split_kernel<4>), g2, dim3(256), 0, st, a); break;
+      case 5: DLAUNCH((correct_pool_split_kernel<5>), g2, dim3(256), 0, st, a); break;
+      case 6: DLAUNCH((correct_pool_split_kernel<6>), g2, dim3(256), 0, st, a); break;
+      case 7: DLAUNCH((correct_pool_split_kernel<7>), g2, dim3(256), 0, st, a); break;
+      case 8: DLAUNCH((correct_pool_split_kernel<8>), g2, dim3(256), 0, st, a); break;
+      case 9: DLAUNCH((correct_pool_split_kernel<9>), g2, dim3(256), 0, st, a); break;
+      case 10: DLAUNCH((correct_pool_split_kernel<10>), g2, dim3(256), 0, st, a); break;
+      case 11: DLAUNCH((correct_pool_split_kernel<11>), g2, dim3(256), 0, st, a); break;
+      default: DLAUNCH((correct_pool_split_kernel<12>), g2, dim3(256), 0, st, a); break;
     }
   } else if (s.bf16) {
     PoolArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,
                      ws.u_lo, slot_k, B, K, s.r, s.V, upr};
-    hipLaunchKernelGGL((correct_pool_kernel<true, kPoolRT>), grid, dim3(256), 0, st, a);
+    DLAUNCH((correct_pool_kernel<true, kPoolRT>), grid, dim3(256), 0, st, a);
   } else {
     PoolArgs<false> a{(const float*)w.fc2, (const float*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,
                       ws.u_lo, slot_k, B, K, s.r, s.V, upr};
-    hipLaunchKernelGGL((correct_pool_kernel<false, kPoolRT>), grid, dim3(256), 0, st, a);
+    DLAUNCH((correct_pool_kernel<false, kPoolRT>), grid, dim3(256), 0, st, a);
   }
 }
 
@@ -1005,6 +1005,6 @@ __global__ void writeout_kernel(const uint64_t* __restrict__ slots, const int32_
 void launch_writeout(const Workspace& ws, int B, int32_t* out_tokens, float* out_top1,
                      hipStream_t st) {
   const int n = B * DOMINO_T;
-  hipLaunchKernelGGL(writeout_kernel, dim3((n + 255) / 256), dim3(256), 0, st, ws.slots, ws.bad, B,
+  DLAUNCH(writeout_kernel, dim3((n + 255) / 256), dim3(256), 0, st, ws.slots, ws.bad, B,
                      out_tokens, out_top1);
 }

@@ -1,8 +1,24 @@
 // Host-side launchers of the rollout kernels (internal interface between the
 // orchestration in rollout.hip and the kernels in kernels.hip / lmhead.hip).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+// Kernel timing.  While a phase of a run is being timed on the calling
+// thread, timing_events hands out an event pair that the launch attaches to
+// the kernel's own dispatch (start and end stamps of that kernel alone);
+// otherwise it returns false and the launch is a plain one.
+bool timing_events(hipEvent_t* start, hipEvent_t* stop);
+#define DLAUNCH(kernel, grid, block, shmem, stream, ...)                                          \
+  do {                                                                                           \
+    hipEvent_t dl_start_ = nullptr, dl_stop_ = nullptr;                                          \
+    if (timing_events(&dl_start_, &dl_stop_))                                                    \
+      hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, dl_start_, dl_stop_, 0,          \
+                            __VA_ARGS__);                                                        \
+    else                                                                                         \
+      hipLaunchKernelGGL(kernel, grid, block, shmem, stream, __VA_ARGS__);                       \
+  } while (0)
 
 struct DeviceWeights {
   const void* lm_head;

@@ -223,7 +223,7 @@ template <bool BF, int NB>
 static void stream_launch(const Shape& s, const void* W, const void* X, float* out, int B,
                           hipStream_t st) {
   const int units = (s.V + 63) / 64;
-  hipLaunchKernelGGL((lmhead_stream_kernel<BF, NB>), dim3((units + 3) / 4), dim3(256), 0, st,
+  DLAUNCH((lmhead_stream_kernel<BF, NB>), dim3((units + 3) / 4), dim3(256), 0, st,
                      (const W_t<BF>*)W, (const W_t<BF>*)X, out, s.V, s.H, B);
 }
 
@@ -264,7 +264,7 @@ void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int
   } else {
     const int nvt = (s.V + kTV - 1) / kTV, nmt = (M + kTM - 1) / kTM;
     const int grid = 8 * ((nvt + 7) / 8) * nmt;
-    hipLaunchKernelGGL(lmhead_tiled_kernel, dim3(grid), dim3(256), kTiledLds, st,
+    DLAUNCH(lmhead_tiled_kernel, dim3(grid), dim3(256), kTiledLds, st,
                        (const bf16_t*)W, (const bf16_t*)X, out, s.V, s.H, B, nvt, nmt);
   }
 }

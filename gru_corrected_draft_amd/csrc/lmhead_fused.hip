@@ -195,5 +195,5 @@ bool lmhead_fused_supported(int H) { return H % 32 == 0; }
 void launch_lmhead_fused(const FusedArgs& a, hipStream_t st) {
   const int nvt = (a.V + kBN - 1) / kBN, ngrp = (a.B + kBJ - 1) / kBJ;
   const int grid = 8 * ((nvt + 7) / 8) * ngrp;
-  hipLaunchKernelGGL(lmhead_fused_kernel, dim3(grid), dim3(256), kLds, st, a);
+  DLAUNCH(lmhead_fused_kernel, dim3(grid), dim3(256), kLds, st, a);
 }

@@ -58,7 +58,7 @@ struct domino_rollout {
   std::vector<GraphEntry> graphs;
   hipStream_t capture_stream = nullptr;
   int last_B = 0, last_K = 0;  // shape of the last enqueued run
-  // measurement: event pairs recorded around launches while timing is on
+  // measurement: kernel event pairs of the timed phases (see PhaseTimer)
   bool timing = false;
   bool capturing = false;
   struct Pending {
@@ -270,27 +270,48 @@ static domino_status_t check_run_args(domino_rollout_t* h, const void* hidden, c
   return DOMINO_OK;
 }
 
-// Records an event pair around the launches issued inside its scope.
-struct PhaseTimer {
+// Times the launches issued inside its scope: each kernel launched while it
+// is active carries an event pair stamped by its own dispatch (see DLAUNCH),
+// and the phase accumulates the kernels' durations.
+namespace {
+struct ActivePhase {
   domino_rollout_t* h;
   int phase;
-  hipStream_t st;
-  hipEvent_t a = nullptr;
-  PhaseTimer(domino_rollout_t* h_, int phase_, hipStream_t st_) : h(h_), phase(phase_), st(st_) {
+};
+thread_local ActivePhase* g_active_phase = nullptr;
+}  // namespace
+
+bool timing_events(hipEvent_t* start, hipEvent_t* stop) {
+  ActivePhase* p = g_active_phase;
+  if (!p) return false;
+  hipEvent_t a = p->h->take_event(), b = p->h->take_event();
+  if (!a || !b) {
+    if (a) p->h->free_events.push_back(a);
+    if (b) p->h->free_events.push_back(b);
+    return false;
+  }
+  p->h->pending.push_back({p->phase, a, b});
+  *start = a;
+  *stop = b;
+  return true;
+}
+
+struct PhaseTimer {
+  domino_rollout_t* h;
+  ActivePhase self;
+  ActivePhase* prev = nullptr;
+  bool on = false;
+  PhaseTimer(domino_rollout_t* h_, int phase, hipStream_t) : h(h_), self{h_, phase} {
     if (h->timing && !h->capturing) {
-      a = h->take_event();
-      if (a && hipEventRecord(a, st) != hipSuccess) a = nullptr;
+      prev = g_active_phase;
+      g_active_phase = &self;
+      on = true;
     }
   }
   ~PhaseTimer() {
-    if (!a) return;
-    hipEvent_t b = h->take_event();
-    if (b && hipEventRecord(b, st) == hipSuccess) {
-      h->pending.push_back({phase, a, b});
-    } else {
-      h->free_events.push_back(a);
-      if (b) h->free_events.push_back(b);
-    }
+    if (!on) return;
+    g_active_phase = prev;
+    h->phase_n[self.phase] += 1;
   }
 };
 
@@ -488,7 +509,6 @@ extern "C" domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int3
     if (hipEventSynchronize(p.b) != hipSuccess || hipEventElapsedTime(&ms, p.a, p.b) != hipSuccess)
       return h->fail(DOMINO_ERR_HIP, "kernel_times: event query failed");
     h->phase_ms[p.phase] += ms;
-    h->phase_n[p.phase] += 1;
     h->free_events.push_back(p.a);
     h->free_events.push_back(p.b);
   }

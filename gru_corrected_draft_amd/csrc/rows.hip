@@ -193,27 +193,27 @@ void launch_gru_rows(const GruArgs16& a, hipStream_t st) {
   const int ie = (a.e + 255) / 256, ig = (a.g + 255) / 256;
 #define CASE(E, G)                                                       \
   if (ie == E && ig == G) {                                              \
-    hipLaunchKernelGGL((gru_rows_kernel<E, G>), grid, blk, 0, st, a);    \
+    DLAUNCH((gru_rows_kernel<E, G>), grid, blk, 0, st, a);    \
     return;                                                              \
   }
   CASE(1, 1) CASE(2, 2) CASE(3, 3) CASE(4, 4) CASE(5, 5)
 #undef CASE
   // mixed widths: the largest block count covers both
   const int m = ie > ig ? ie : ig;
-  if (m <= 1) hipLaunchKernelGGL((gru_rows_kernel<1, 1>), grid, blk, 0, st, a);
-  else if (m == 2) hipLaunchKernelGGL((gru_rows_kernel<2, 2>), grid, blk, 0, st, a);
-  else if (m == 3) hipLaunchKernelGGL((gru_rows_kernel<3, 3>), grid, blk, 0, st, a);
-  else if (m == 4) hipLaunchKernelGGL((gru_rows_kernel<4, 4>), grid, blk, 0, st, a);
-  else hipLaunchKernelGGL((gru_rows_kernel<5, 5>), grid, blk, 0, st, a);
+  if (m <= 1) DLAUNCH((gru_rows_kernel<1, 1>), grid, blk, 0, st, a);
+  else if (m == 2) DLAUNCH((gru_rows_kernel<2, 2>), grid, blk, 0, st, a);
+  else if (m == 3) DLAUNCH((gru_rows_kernel<3, 3>), grid, blk, 0, st, a);
+  else if (m == 4) DLAUNCH((gru_rows_kernel<4, 4>), grid, blk, 0, st, a);
+  else DLAUNCH((gru_rows_kernel<5, 5>), grid, blk, 0, st, a);
 }
 
 void launch_fc1_rows(const Fc1Args16& a, hipStream_t st) {
   const dim3 grid((a.r + 3) / 4), blk(256);
   switch ((a.g + 255) / 256) {
-    case 1: hipLaunchKernelGGL((fc1_rows_kernel<1>), grid, blk, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((fc1_rows_kernel<2>), grid, blk, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((fc1_rows_kernel<3>), grid, blk, 0, st, a); break;
-    case 4: hipLaunchKernelGGL((fc1_rows_kernel<4>), grid, blk, 0, st, a); break;
-    default: hipLaunchKernelGGL((fc1_rows_kernel<5>), grid, blk, 0, st, a); break;
+    case 1: DLAUNCH((fc1_rows_kernel<1>), grid, blk, 0, st, a); break;
+    case 2: DLAUNCH((fc1_rows_kernel<2>), grid, blk, 0, st, a); break;
+    case 3: DLAUNCH((fc1_rows_kernel<3>), grid, blk, 0, st, a); break;
+    case 4: DLAUNCH((fc1_rows_kernel<4>), grid, blk, 0, st, a); break;
+    default: DLAUNCH((fc1_rows_kernel<5>), grid, blk, 0, st, a); break;
   }
 }

@@ -462,7 +462,7 @@ void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
   const int unit = 8 * a.groups;
   const int want = (cus > 0 ? cus : 256) * per_cu;
   const int grid = ((want + unit - 1) / unit) * unit;
-  hipLaunchKernelGGL((rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI>), dim3(grid), dim3(256), lds,
+  DLAUNCH((rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI>), dim3(grid), dim3(256), lds,
                      st, a);
 }
 
@@ -496,7 +496,7 @@ void launch_t(StreamArgs a, hipStream_t st) {
   const int cols = min(a.ncols, NB * 16);
   a.groups = (a.ncols + NB * 16 - 1) / (NB * 16);
   const size_t lds = (size_t)(SPLIT ? 2 : 1) * cols * (a.KS + 8) * sizeof(bf16_t);
-  hipLaunchKernelGGL((rowstream_kernel<NB, RT, SPLIT, EPI, D>),
+  DLAUNCH((rowstream_kernel<NB, RT, SPLIT, EPI, D>),
                      dim3(8 * a.groups * ((rowblocks + 7) / 8)), dim3(256), lds, st, a);
 }
 

@@ -147,15 +147,17 @@ domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const void* base_
 domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t which, void* dst,
                                               size_t dst_bytes, size_t* bytes, void* stream);
 
-/* Measurement support.  While enabled, domino_rollout_run and
- * domino_rollout_run_forced record a HIP event pair on the caller's stream
- * around every launch of each phase (graph replays are not instrumented).
- * domino_rollout_kernel_times waits for the recorded events, adds their
- * elapsed times to per-phase totals and returns the total milliseconds and
- * launch count of one phase: 0 = LM-head GEMM, 1 = correction + argmax
- * (full vocabulary or pool), 2 = GRU cell, 3 = fc1 + SiLU, 4 = pool build
- * (all its kernels as one launch), 5 = first-proposal argmax.  which = -1
- * clears the totals.  Timing changes no result. */
+/* Measurement support.  While enabled, every kernel that domino_rollout_run
+ * and domino_rollout_run_forced launch carries a HIP event pair stamped by
+ * that kernel's own dispatch (its start and end on the GPU, without launch
+ * gaps); graph replays are not instrumented.  domino_rollout_kernel_times
+ * waits for the pending events, adds the kernel durations to per-phase
+ * totals and returns the total milliseconds and the number of phase
+ * instances of one phase: 0 = LM-head GEMM, 1 = correction + argmax (full
+ * vocabulary or pool), 2 = GRU cell (with its split-sum kernel where used),
+ * 3 = fc1 + SiLU (likewise), 4 = pool build (all its kernels), 5 =
+ * first-proposal argmax.  which = -1 clears the totals.  Timing changes no
+ * result. */
 domino_status_t domino_rollout_set_timing(domino_rollout_t* h, int32_t enable);
 domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int32_t which, double* total_ms,
                                             int64_t* launches);
