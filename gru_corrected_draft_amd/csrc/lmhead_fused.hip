@@ -180,7 +180,159 @@ __global__ __launch_bounds__(256) void lmhead_fused_kernel(FusedArgs a) {
   fused_epilogue(a, acc, ring, v0, b0, wave, row, q, tid);
 }
 
+// Line-copy kernel with separate operand rings.  A direct global->LDS copy
+// moves fastest when its 64 lanes cover whole 128-byte lines (8 rows x 128 B
+// per instruction run at about four times the rate of the 16 rows x 64 B of
+// an MFMA fragment on gfx950), so a stage holds 64 k and every 1 KB block is
+// 8 rows x 64 bf16.  Within a row the 16-byte chunk of logical index c sits
+// at position c ^ (r16 >> 1), r16 being the row's index in its 16-row tile,
+// which keeps the 16 lanes of a fragment read on distinct banks.  lm_head
+// rows come from HBM, so their ring is three stages deep (two in flight);
+// the activations are cache resident and double-buffered.  Each iteration
+// issues the activation copies of stage s + 1 before the lm_head copies of
+// stage s + 2, so "all but this wave's newest 8 copies have landed" covers
+// both operands of stage s + 1 at the next iteration.
+constexpr int kStageK = 64;
+constexpr int kABlocks = kBN / 8;                  // 32 blocks of 8 lm_head rows
+constexpr int kBBlocks = 2 * DOMINO_T;             // 30 blocks of 8 requests at one position
+constexpr int kARing = 3, kBRing = 2;
+static_assert(kARing + kBRing == 5 && (kARing == 2 || kARing == 3), "ring depths");
+constexpr bool kADeep = kARing > kBRing;  // which operand runs two stages ahead
+constexpr int kReadWindow = 8;  // fragment reads kept ahead of the products
+constexpr int kAStage = kABlocks * 1024, kBStage = kBBlocks * 1024;
+constexpr size_t kLinesLds = (size_t)kARing * kAStage + (size_t)kBRing * kBStage;  // 154-156 KB
+constexpr int kACopies = kABlocks / 4;             // 8 per wave
+constexpr int kBCopies = (kBBlocks + 3) / 4;       // 8 (7 for waves 2, 3)
+
+__global__ __launch_bounds__(256) void lmhead_lines_kernel(FusedArgs a) {
+  const int V = a.V, H = a.H, B = a.B;
+  const int nvt = (V + kBN - 1) / kBN, ngrp = (B + kBJ - 1) / kBJ;
+  const int j = blockIdx.x, xcd = j & 7, local = j >> 3;
+  const int vt = (local / ngrp) * 8 + xcd, grp = local % ngrp;
+  if (vt >= nvt) return;  // uniform per workgroup, before any barrier
+  const int v0 = vt * kBN, b0 = grp * kBJ;
+  extern __shared__ __align__(1024) unsigned char ring[];
+  unsigned char* const aring = ring;
+  unsigned char* const bring = ring + kARing * kAStage;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int row = lane & 15, q = lane >> 4;
+
+  // copy duties: A blocks wave + 4i (i < 8), B blocks wave + 4i (< 30); lane
+  // (rr = lane / 8, p = lane % 8) fetches logical chunk p ^ (r16 >> 1) of row
+  // rr of its block
+  const char* const Wb = reinterpret_cast<const char*>(a.W);
+  const char* const Xb = reinterpret_cast<const char*>(a.X);
+  const int rr = lane >> 3, pp = lane & 7;
+  uint32_t aoff[kACopies], boff[kBCopies];
+#pragma unroll
+  for (int i = 0; i < kACopies; ++i) {
+    const int blk = wave + 4 * i;
+    const int r16 = (blk & 1) * 8 + rr;
+    const int v = min(v0 + blk * 8 + rr, V - 1);
+    aoff[i] = ((uint32_t)v * (uint32_t)H + (pp ^ (r16 >> 1)) * 8) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < kBCopies; ++i) {
+    const int blk = min(wave + 4 * i, kBBlocks - 1);
+    const int r16 = (blk & 1) * 8 + rr;
+    const int t = blk >> 1;
+    const int bb = min(b0 + r16, B - 1);
+    boff[i] = (((uint32_t)bb * DOMINO_T + t) * (uint32_t)H + (pp ^ (r16 >> 1)) * 8) * 2u;
+  }
+  const bool eight_b = wave + 4 * (kBCopies - 1) < kBBlocks;
+  auto issue_a = [&](int s) {
+    unsigned char* slot = aring + (s % kARing) * kAStage;
+    const uint32_t kb = (uint32_t)s * (kStageK * 2);
+#pragma unroll
+    for (int i = 0; i < kACopies; ++i) dma16(Wb + (aoff[i] + kb), slot + (wave + 4 * i) * 1024);
+  };
+  auto issue_b = [&](int s) {
+    unsigned char* slot = bring + (s % kBRing) * kBStage;
+    const uint32_t kb = (uint32_t)s * (kStageK * 2);
+#pragma unroll
+    for (int i = 0; i < kBCopies - 1; ++i) dma16(Xb + (boff[i] + kb), slot + (wave + 4 * i) * 1024);
+    if (eight_b)
+      dma16(Xb + (boff[kBCopies - 1] + kb), slot + (wave + 4 * (kBCopies - 1)) * 1024);
+  };
+
+  v4f acc[4][DOMINO_T];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int t = 0; t < DOMINO_T; ++t) acc[r][t] = zero4();
+
+  // fragment of this lane inside a block pair (16 rows): block 2T + (row >> 3),
+  // row (row & 7), chunk (h * 4 + q) ^ (row >> 1)
+  const int frag0 = (row >> 3) * 1024 + (row & 7) * 128;
+  const int sw = row >> 1;
+  const int ns = H / kStageK;
+  // prologue: the shallow operand's stage 0, then the deep one's stages 0, 1
+  // in the order the loop keeps (deep copies of the farthest stage newest)
+  if (kADeep) {
+    issue_a(0);
+    issue_b(0);
+    if (ns > 1) issue_a(1);
+  } else {
+    issue_b(0);
+    issue_a(0);
+    if (ns > 1) issue_b(1);
+  }
+  for (int s = 0; s < ns; ++s) {
+    // this wave's newest copies are the deep operand's stage s + 1 (if any)
+    if (s + 1 < ns) {
+      if (kADeep) wait_vm<kACopies>();
+      else if (eight_b) wait_vm<kBCopies>();
+      else wait_vm<kBCopies - 1>();
+    } else {
+      wait_vm<0>();
+    }
+    lds_barrier();  // everyone's copies of stage s landed; stage s - 1 is consumed
+    if (kADeep) {
+      if (s + 1 < ns) issue_b(s + 1);
+      if (s + 2 < ns) issue_a(s + 2);
+    } else {
+      if (s + 1 < ns) issue_a(s + 1);
+      if (s + 2 < ns) issue_b(s + 2);
+    }
+    const unsigned char* as = aring + (s % kARing) * kAStage + frag0;
+    const unsigned char* bs = bring + (s % kBRing) * kBStage + frag0;
+    // The stage's 38 fragment reads (A then B of the first 32-wide half, then
+    // of the second) run as one stream kReadWindow reads ahead of the 30
+    // product steps (4 MFMAs against one B fragment each).  Fewer than 16
+    // reads are ever outstanding, so every wait names exactly the fragment
+    // it needs; the scheduling barriers keep that order.
+    constexpr int kFrags = 2 * (4 + DOMINO_T);
+    v8s fr[kFrags];
+    auto rd = [&](int k) {
+      const int h = k / (4 + DOMINO_T), idx = k % (4 + DOMINO_T);
+      const int cofs = ((h * 4 + q) ^ sw) * 16;
+      fr[k] = idx < 4 ? *reinterpret_cast<const v8s*>(as + 2 * (wave * 4 + idx) * 1024 + cofs)
+                      : *reinterpret_cast<const v8s*>(bs + 2 * (idx - 4) * 1024 + cofs);
+    };
+    int issued = 0;
+#pragma unroll
+    for (int jstep = 0; jstep < 2 * DOMINO_T; ++jstep) {
+      const int h = jstep / DOMINO_T, t = jstep % DOMINO_T;
+      const int need = h * (4 + DOMINO_T) + 4 + t;
+      const int upto = min(need + kReadWindow, kFrags - 1);
+#pragma unroll
+      for (int k = 0; k < kFrags; ++k)
+        if (k >= issued && k <= upto) rd(k);
+      issued = max(issued, upto + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[r][t] = mfma_bf16(fr[h * (4 + DOMINO_T) + r], fr[need], acc[r][t]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  lds_barrier();  // the rings are free again
+  fused_epilogue(a, acc, ring, v0, b0, wave, row, q, tid);
+}
+
 constexpr size_t kLds = (size_t)kStages * kSliceBytes;
+// line-copy kernel whenever H is a multiple of its 64-wide stage
 
 
 }  // namespace
@@ -188,6 +340,8 @@ constexpr size_t kLds = (size_t)kStages * kSliceBytes;
 void lmhead_fused_prepare() {
   (void)hipFuncSetAttribute((const void*)lmhead_fused_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  (void)hipFuncSetAttribute((const void*)lmhead_lines_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLinesLds);
 }
 
 bool lmhead_fused_supported(int H) { return H % 32 == 0; }
@@ -195,5 +349,8 @@ bool lmhead_fused_supported(int H) { return H % 32 == 0; }
 void launch_lmhead_fused(const FusedArgs& a, hipStream_t st) {
   const int nvt = (a.V + kBN - 1) / kBN, ngrp = (a.B + kBJ - 1) / kBJ;
   const int grid = 8 * ((nvt + 7) / 8) * ngrp;
-  DLAUNCH(lmhead_fused_kernel, dim3(grid), dim3(256), kLds, st, a);
+  if (a.H % kStageK == 0)
+    DLAUNCH(lmhead_lines_kernel, dim3(grid), dim3(256), kLinesLds, st, a);
+  else
+    DLAUNCH(lmhead_fused_kernel, dim3(grid), dim3(256), kLds, st, a);
 }
