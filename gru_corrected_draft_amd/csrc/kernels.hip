@@ -991,20 +991,20 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
 
 // ---------------------------------------------------------------- outputs
 __global__ void writeout_kernel(const uint64_t* __restrict__ slots, const int32_t* __restrict__ bad,
-                                int B, int32_t* __restrict__ out_tokens,
+                                int B, int P, int32_t* __restrict__ out_tokens,
                                 float* __restrict__ out_top1) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * DOMINO_T) return;
-  const int b = idx / DOMINO_T, k = idx % DOMINO_T;
+  if (idx >= B * P) return;
+  const int b = idx / P, k = idx % P;
   const uint64_t key = slots[(size_t)k * B + b];
   const bool invalid = bad[b] != 0 || key == 0;
   out_tokens[idx] = invalid ? -1 : key_id(key);
   if (out_top1) out_top1[idx] = invalid ? __builtin_nanf("") : key_value(key);
 }
 
-void launch_writeout(const Workspace& ws, int B, int32_t* out_tokens, float* out_top1,
+void launch_writeout(const Workspace& ws, int B, int P, int32_t* out_tokens, float* out_top1,
                      hipStream_t st) {
-  const int n = B * DOMINO_T;
-  DLAUNCH(writeout_kernel, dim3((n + 255) / 256), dim3(256), 0, st, ws.slots, ws.bad, B,
-                     out_tokens, out_top1);
+  const int n = B * P;
+  DLAUNCH(writeout_kernel, dim3((n + 255) / 256), dim3(256), 0, st, ws.slots, ws.bad, B, P,
+          out_tokens, out_top1);
 }

@@ -147,5 +147,6 @@ void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace
                          hipStream_t st);
 void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
                          int K, hipStream_t st);
-void launch_writeout(const Workspace& ws, int B, int32_t* out_tokens, float* out_top1,
+// tokens and top-1 logits of proposals 1..P, [B, P]
+void launch_writeout(const Workspace& ws, int B, int P, int32_t* out_tokens, float* out_top1,
                      hipStream_t st);

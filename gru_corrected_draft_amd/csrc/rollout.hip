@@ -28,10 +28,10 @@ void set_global_err(const std::string& s) {
 }
 
 struct GraphKey {
-  int B, K, forced;
+  int B, K, forced, P;
   const void* p[6];
   bool operator==(const GraphKey& o) const {
-    if (B != o.B || K != o.K || forced != o.forced) return false;
+    if (B != o.B || K != o.K || forced != o.forced || P != o.P) return false;
     for (int i = 0; i < 6; ++i)
       if (p[i] != o.p[i]) return false;
     return true;
@@ -315,9 +315,12 @@ struct PhaseTimer {
   }
 };
 
+// One rollout producing the first P proposals (P = DOMINO_T: the whole block):
+// base logits, first proposal and pool of the whole block, then P - 1
+// correction steps.
 static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, const int32_t* ver,
-                    const int32_t* forced, int B, int K, int32_t* out_tokens, float* out_top1,
-                    hipStream_t st) {
+                    const int32_t* forced, int B, int K, int P, int32_t* out_tokens,
+                    float* out_top1, hipStream_t st) {
   const Shape& sh = h->shape;
   const Workspace& ws = h->ws;
   const bool pool = K > 0 && K < sh.V;
@@ -343,7 +346,8 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
     PhaseTimer t(h, kPool, st);
     launch_pool_build(sh, ws, B, K, fused, st);
   }
-  // two-token prefix: h = GRU(E[verified], 0); h = GRU(E[p1], h)
+  // two-token prefix: h = GRU(E[verified], 0); h = GRU(E[p1], h).  It runs
+  // for every P: the first cell is where an invalid verified token is flagged.
   {
     PhaseTimer t(h, kGru, st);
     launch_gru(sh, h->w, nullptr, ws.h[0], ver, 1, nullptr, ws.bad, B, ws, st);
@@ -356,7 +360,8 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
       launch_gru(sh, h->w, ws.h[0], ws.h[1], nullptr, 0, ws.slots, ws.bad, B, ws, st);
   }
   int cur = 1;
-  for (int k = 1; k <= DOMINO_S; ++k) {
+  const int steps = P - 1;  // correction steps of this run
+  for (int k = 1; k <= steps; ++k) {
     {
       PhaseTimer t(h, kFc1, st);
       launch_fc1(sh, h->w, ws.h[cur], s, k - 1, ws, B, st);
@@ -368,7 +373,7 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
       else
         launch_correct_full(sh, h->w, ws, k, B, st);
     }
-    if (k < DOMINO_S) {
+    if (k < steps) {
       PhaseTimer t(h, kGru, st);
       if (forced)
         launch_gru(sh, h->w, ws.h[cur], ws.h[cur ^ 1], forced + k, DOMINO_T, nullptr, ws.bad, B, ws,
@@ -379,7 +384,7 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
       cur ^= 1;
     }
   }
-  launch_writeout(ws, B, out_tokens, out_top1, st);
+  launch_writeout(ws, B, P, out_tokens, out_top1, st);
 }
 
 namespace {
@@ -396,12 +401,12 @@ struct DeviceGuard {
 
 static domino_status_t run_common(domino_rollout_t* h, const void* hidden, const float* s,
                                   const int32_t* ver, const int32_t* forced, int32_t B, int32_t K,
-                                  int32_t* out_tokens, float* out_top1, void* stream) {
+                                  int32_t P, int32_t* out_tokens, float* out_top1, void* stream) {
   domino_status_t st = check_run_args(h, hidden, s, ver, B, K, out_tokens);
   if (st != DOMINO_OK) return st;
   DeviceGuard dg(h->device);
   (void)hipGetLastError();  // clear a stale error of an unrelated call
-  enqueue(h, hidden, s, ver, forced, B, K, out_tokens, out_top1, (hipStream_t)stream);
+  enqueue(h, hidden, s, ver, forced, B, K, P, out_tokens, out_top1, (hipStream_t)stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return h->fail(DOMINO_ERR_HIP, "run: kernel launch failed: %s", hipGetErrorString(e));
   h->err.clear();
@@ -412,8 +417,8 @@ extern "C" domino_status_t domino_rollout_run(domino_rollout_t* h, const void* b
                                               const float* step_s, const int32_t* verified_tokens,
                                               int32_t batch, int32_t K, int32_t* out_tokens,
                                               float* out_top1_logit, void* stream) {
-  return run_common(h, base_hidden, step_s, verified_tokens, nullptr, batch, K, out_tokens,
-                    out_top1_logit, stream);
+  return run_common(h, base_hidden, step_s, verified_tokens, nullptr, batch, K, DOMINO_T,
+                    out_tokens, out_top1_logit, stream);
 }
 
 extern "C" domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const void* base_hidden,
@@ -423,20 +428,20 @@ extern "C" domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const 
                                                      int32_t K, int32_t* out_tokens,
                                                      float* out_top1_logit, void* stream) {
   if (h && !forced_tokens) return h->fail(DOMINO_ERR_INVALID_ARG, "run_forced: forced_tokens is NULL");
-  return run_common(h, base_hidden, step_s, verified_tokens, forced_tokens, batch, K, out_tokens,
-                    out_top1_logit, stream);
+  return run_common(h, base_hidden, step_s, verified_tokens, forced_tokens, batch, K, DOMINO_T,
+                    out_tokens, out_top1_logit, stream);
 }
 
-extern "C" domino_status_t domino_rollout_run_graph(domino_rollout_t* h, const void* base_hidden,
-                                                    const float* step_s,
-                                                    const int32_t* verified_tokens, int32_t batch,
-                                                    int32_t K, int32_t* out_tokens,
-                                                    float* out_top1_logit, void* stream) {
+static domino_status_t run_graph_common(domino_rollout_t* h, const void* base_hidden,
+                                        const float* step_s, const int32_t* verified_tokens,
+                                        int32_t batch, int32_t K, int32_t P, int32_t* out_tokens,
+                                        float* out_top1_logit, void* stream) {
   domino_status_t st = check_run_args(h, base_hidden, step_s, verified_tokens, batch, K, out_tokens);
   if (st != DOMINO_OK) return st;
   DeviceGuard dg(h->device);
   const int kmode = (K > 0 && K < h->cfg.vocab) ? K : 0;
-  GraphKey key{batch, kmode, 0, {base_hidden, step_s, verified_tokens, out_tokens, out_top1_logit, nullptr}};
+  GraphKey key{batch, kmode, 0, P,
+               {base_hidden, step_s, verified_tokens, out_tokens, out_top1_logit, nullptr}};
   hipGraphExec_t exec = nullptr;
   for (auto& g : h->graphs)
     if (g.key == key) exec = g.exec;
@@ -449,7 +454,7 @@ extern "C" domino_status_t domino_rollout_run_graph(domino_rollout_t* h, const v
     if (hipStreamBeginCapture(h->capture_stream, hipStreamCaptureModeRelaxed) != hipSuccess)
       return h->fail(DOMINO_ERR_HIP, "run_graph: begin capture failed");
     h->capturing = true;
-    enqueue(h, base_hidden, step_s, verified_tokens, nullptr, batch, kmode, out_tokens,
+    enqueue(h, base_hidden, step_s, verified_tokens, nullptr, batch, kmode, P, out_tokens,
             out_top1_logit, h->capture_stream);
     h->capturing = false;
     hipError_t e1 = hipGetLastError();
@@ -468,6 +473,32 @@ extern "C" domino_status_t domino_rollout_run_graph(domino_rollout_t* h, const v
   if (e != hipSuccess) return h->fail(DOMINO_ERR_HIP, "run_graph: launch failed: %s", hipGetErrorString(e));
   h->err.clear();
   return DOMINO_OK;
+}
+
+extern "C" domino_status_t domino_rollout_run_graph(domino_rollout_t* h, const void* base_hidden,
+                                                    const float* step_s,
+                                                    const int32_t* verified_tokens, int32_t batch,
+                                                    int32_t K, int32_t* out_tokens,
+                                                    float* out_top1_logit, void* stream) {
+  return run_graph_common(h, base_hidden, step_s, verified_tokens, batch, K, DOMINO_T, out_tokens,
+                          out_top1_logit, stream);
+}
+
+extern "C" domino_status_t domino_rollout_run_prefix(domino_rollout_t* h, const void* base_hidden,
+                                                     const float* step_s,
+                                                     const int32_t* verified_tokens, int32_t batch,
+                                                     int32_t K, int32_t proposals,
+                                                     int32_t* out_tokens, float* out_top1_logit,
+                                                     int32_t graph, void* stream) {
+  if (!h) return DOMINO_ERR_INVALID_ARG;
+  if (proposals < 1 || proposals > DOMINO_T)
+    return h->fail(DOMINO_ERR_INVALID_ARG, "run_prefix: proposals %d outside [1, %d]", proposals,
+                   DOMINO_T);
+  if (graph)
+    return run_graph_common(h, base_hidden, step_s, verified_tokens, batch, K, proposals,
+                            out_tokens, out_top1_logit, stream);
+  return run_common(h, base_hidden, step_s, verified_tokens, nullptr, batch, K, proposals,
+                    out_tokens, out_top1_logit, stream);
 }
 
 extern "C" domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t which,

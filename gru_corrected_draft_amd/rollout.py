@@ -27,7 +27,8 @@ N_PROPOSALS = 15
 N_STEPS = 14
 
 EXPORTED = ("domino_rollout_create", "domino_rollout_run", "domino_rollout_run_graph",
-            "domino_rollout_run_forced", "domino_rollout_read_workspace", "domino_rollout_destroy",
+            "domino_rollout_run_prefix", "domino_rollout_run_forced",
+            "domino_rollout_read_workspace", "domino_rollout_destroy",
             "domino_rollout_last_error", "domino_rollout_set_timing",
             "domino_rollout_kernel_times")
 PHASES = {"lmhead": 0, "correct": 1, "gru": 2, "fc1": 3, "pool": 4, "argmax0": 5}
@@ -72,6 +73,9 @@ def load_library():
     lib.domino_rollout_run.restype = ctypes.c_int
     lib.domino_rollout_run_graph.argtypes = run_args
     lib.domino_rollout_run_graph.restype = ctypes.c_int
+    lib.domino_rollout_run_prefix.argtypes = [vp, vp, f32p, i32p, i32, i32, i32, i32p, f32p, i32,
+                                              vp]
+    lib.domino_rollout_run_prefix.restype = ctypes.c_int
     lib.domino_rollout_run_forced.argtypes = [vp, vp, f32p, i32p, i32p, i32, i32, i32p, f32p, vp]
     lib.domino_rollout_run_forced.restype = ctypes.c_int
     lib.domino_rollout_read_workspace.argtypes = [vp, i32, vp, ctypes.c_size_t,
@@ -143,8 +147,9 @@ class DominoRollout:
             raise DominoError(st, self.lib.domino_rollout_last_error(self.handle).decode())
 
     def run(self, hidden, step_s, verified, K, out_tokens=None, out_top1=None, graph=False,
-            forced=None, stream=None):
-        """Enqueue one rollout; returns (out_tokens [B,15] int32, out_top1 [B,15] fp32)."""
+            forced=None, stream=None, proposals=None):
+        """Enqueue one rollout; returns (out_tokens [B,P] int32, out_top1 [B,P] fp32),
+        P = 15, or `proposals` for a truncated rollout (domino_rollout_run_prefix)."""
         import torch
         B = hidden.shape[0]
         V, H, e, g, r = self.shape
@@ -158,13 +163,22 @@ class DominoRollout:
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError("inputs must be contiguous device tensors")
         dev = hidden.device
+        P = N_PROPOSALS if proposals is None else int(proposals)
         if out_tokens is None:
-            out_tokens = torch.empty((B, N_PROPOSALS), dtype=torch.int32, device=dev)
+            out_tokens = torch.empty((B, P), dtype=torch.int32, device=dev)
         if out_top1 is None:
-            out_top1 = torch.empty((B, N_PROPOSALS), dtype=torch.float32, device=dev)
+            out_top1 = torch.empty((B, P), dtype=torch.float32, device=dev)
+        if out_tokens.shape != (B, P) or out_top1.shape != (B, P):
+            raise ValueError("out_tokens / out_top1 must be [B, P]")
         st_ptr = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream if stream is None
                                  else stream)
-        if forced is not None:
+        if proposals is not None:
+            if forced is not None:
+                raise ValueError("teacher forcing runs the whole block")
+            st = self.lib.domino_rollout_run_prefix(self.handle, _ptr(hidden), _ptr(step_s),
+                                                    _ptr(verified), B, K, P, _ptr(out_tokens),
+                                                    _ptr(out_top1), int(bool(graph)), st_ptr)
+        elif forced is not None:
             if forced.shape != (B, N_PROPOSALS) or forced.dtype != torch.int32 or not forced.is_cuda:
                 raise ValueError("forced must be [B, 15] int32 on the device")
             st = self.lib.domino_rollout_run_forced(self.handle, _ptr(hidden), _ptr(step_s),

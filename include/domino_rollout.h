@@ -128,6 +128,23 @@ domino_status_t domino_rollout_run_graph(domino_rollout_t* h, const void* base_h
                                          int32_t batch, int32_t K, int32_t* out_tokens,
                                          float* out_top1_logit, void* stream);
 
+/* Truncated rollout: only the first `proposals` (1..15) proposals, for a
+ * target that verifies only the first positions of the block ("Qwen3.6-27B
+ * checkpoint and full serving benchmark", Methods: b8 keeps the block-16
+ * draft backbone and verifies the first 8 positions).  The base logits, the
+ * first proposal and the pool are those of the whole block, and the run stops
+ * after proposals - 1 correction steps, so the result equals the first
+ * `proposals` columns of domino_rollout_run.  out_tokens and out_top1_logit
+ * (or NULL) are [batch, proposals].  graph != 0 replays a HIP graph cached
+ * per (batch, K mode, proposals, pointer set), as domino_rollout_run_graph
+ * does.  Other arguments and errors as domino_rollout_run; proposals outside
+ * [1, 15] is DOMINO_ERR_INVALID_ARG. */
+domino_status_t domino_rollout_run_prefix(domino_rollout_t* h, const void* base_hidden,
+                                          const float* step_s, const int32_t* verified_tokens,
+                                          int32_t batch, int32_t K, int32_t proposals,
+                                          int32_t* out_tokens, float* out_top1_logit,
+                                          int32_t graph, void* stream);
+
 /* Teacher-forced variant for testing: the GRU consumes forced_tokens[b, j]
  * (device, [batch, 15] int32, values in [0, V)) in place of proposal j+1,
  * while out_tokens / out_top1_logit still report each step's argmax.  This

@@ -131,7 +131,8 @@ def gru_cell(x: np.ndarray, h: np.ndarray, w_ih: np.ndarray, w_hh: np.ndarray) -
 
 
 def rollout(weights: dict, hidden: np.ndarray, step_s: np.ndarray, verified: np.ndarray,
-            K: int, forced: np.ndarray | None = None, record: dict | None = None) -> dict:
+            K: int, forced: np.ndarray | None = None, record: dict | None = None,
+            proposals: int | None = None) -> dict:
     """The whole draft-block rollout for B requests.
 
     weights: float32 arrays lm_head [V,H], embed [V,e], gru_w_ih [3g,e],
@@ -139,10 +140,16 @@ def rollout(weights: dict, hidden: np.ndarray, step_s: np.ndarray, verified: np.
     hidden [B,15,H], step_s [B,14,r], verified [B] int, K >= 0.
     forced [B,15] (optional): teacher forcing — the GRU consumes forced[:, j]
     in place of proposal j+1 (the selections are still reported).
+    proposals (optional, 1..15): stop after that many proposals, i.e. after
+    proposals-1 correction steps (a truncated rollout, as when the target
+    verifies only the first positions of the block: "Qwen3.6-27B checkpoint
+    and full serving benchmark", Methods, b8).  The base logits, the first
+    proposal and the pool are those of the whole block, so the result is the
+    first `proposals` columns of the full rollout.
 
-    Returns tokens [B,15] int32, top1 [B,15] and margin [B,15] float32
-    (column 0 from base row 0, column k from correction step k) and the
-    pools (list of id arrays, None = full vocabulary).
+    Returns tokens [B,P] int32, top1 [B,P] and margin [B,P] float32 (P = 15
+    or `proposals`; column 0 from base row 0, column k from correction step
+    k) and the pools (list of id arrays, None = full vocabulary).
 
     Order of work, [DFV2] "Design" and [SPEC] "Motivation":
       1. base logits of all 15 positions (full vocabulary);
@@ -158,14 +165,17 @@ def rollout(weights: dict, hidden: np.ndarray, step_s: np.ndarray, verified: np.
     lm, E = W["lm_head"], W["embed"]
     w_ih, w_hh, F1, F2, b2 = W["gru_w_ih"], W["gru_w_hh"], W["fc1_w"], W["fc2_w"], W["fc2_b"]
     B, T, _ = hidden.shape
-    S = T - 1
+    P = T if proposals is None else int(proposals)
+    if not 1 <= P <= T:
+        raise ValueError(f"proposals must be in [1, {T}]")
+    S = P - 1                  # correction steps run
     V = lm.shape[0]
     g = w_hh.shape[1]
 
     base = base_logits(np.asarray(hidden, F32), lm)
-    tokens = np.zeros((B, T), np.int32)
-    top1 = np.zeros((B, T), F32)
-    margin = np.zeros((B, T), F32)
+    tokens = np.zeros((B, P), np.int32)
+    top1 = np.zeros((B, P), F32)
+    margin = np.zeros((B, P), F32)
 
     for b in range(B):
         j = first_max_index(base[0, b])
@@ -177,8 +187,9 @@ def rollout(weights: dict, hidden: np.ndarray, step_s: np.ndarray, verified: np.
         return tokens[:, j] if forced is None else np.asarray(forced[:, j])
 
     h = np.zeros((B, g), F32)
-    h = gru_cell(E[np.asarray(verified, np.int64)], h, w_ih, w_hh)
-    h = gru_cell(E[fed(0).astype(np.int64)], h, w_ih, w_hh)
+    if S > 0:  # the prefix only feeds the correction steps
+        h = gru_cell(E[np.asarray(verified, np.int64)], h, w_ih, w_hh)
+        h = gru_cell(E[fed(0).astype(np.int64)], h, w_ih, w_hh)
     if record is not None:
         record.update(base=base, pools=pools, h=[h.copy()], u=[], y=[])
 

@@ -45,16 +45,18 @@ def drop_handles():
 
 
 @functools.lru_cache(maxsize=64)
-def oracle_run(name_or_shape, batch, input_seed, trial, K, scales_key=(), forced_key=None):
+def oracle_run(name_or_shape, batch, input_seed, trial, K, scales_key=(), forced_key=None,
+               proposals=None):
     shape = synth.MODELS[name_or_shape] if isinstance(name_or_shape, str) else name_or_shape
     _, _, f32 = model(name_or_shape, scales_key)
     inp = synth.make_inputs(shape, batch, input_seed, trial)
     forced = None if forced_key is None else np.asarray(forced_key, np.int32).reshape(batch, 15)
-    return oracle.rollout(f32, inp.hidden_f32(), inp.step_s, inp.verified, K, forced=forced)
+    return oracle.rollout(f32, inp.hidden_f32(), inp.step_s, inp.verified, K, forced=forced,
+                          proposals=proposals)
 
 
 def gpu_run(name_or_shape, batch, input_seed, trial, K, max_batch=None, max_k=None,
-            scales_key=(), graph=False, forced=None):
+            scales_key=(), graph=False, forced=None, proposals=None):
     import torch
     shape = synth.MODELS[name_or_shape] if isinstance(name_or_shape, str) else name_or_shape
     h = handle(name_or_shape, max_batch or batch, max_k if max_k is not None else max(K, 1),
@@ -62,7 +64,7 @@ def gpu_run(name_or_shape, batch, input_seed, trial, K, max_batch=None, max_k=No
     inp = synth.make_inputs(shape, batch, input_seed, trial)
     hid, s, ver = R.device_inputs(inp)
     f = None if forced is None else torch.from_numpy(np.asarray(forced, np.int32)).cuda()
-    tok, top = h.run(hid, s, ver, K, graph=graph, forced=f)
+    tok, top = h.run(hid, s, ver, K, graph=graph, forced=f, proposals=proposals)
     torch.cuda.synchronize()
     return tok.cpu().numpy(), top.cpu().numpy(), h
 

@@ -259,9 +259,82 @@ def test_run_rejects_bad_scalars_without_launching():
     assert torch.all(out == 5)
 
 
+# ------------------------------------------------------- truncated rollouts
+
+@pytest.mark.parametrize("B,K", [(1, 0), (5, 100), (17, 0), (64, 100)])
+def test_truncated_rollout_is_prefix_and_matches_oracle(B, K):
+    """domino_rollout_run_prefix with P proposals returns the first P columns
+    of the full rollout bit for bit, and meets the oracle's truncated run."""
+    seed = 950 + B
+    full_t, full_l, _ = G.gpu_run(SMALL, B, seed, 0, K, max_batch=64, max_k=2048,
+                                  scales_key=STRONG)
+    for P in (1, 2, 8, 14, 15):
+        G.log(f"[gpu-test] truncated B={B} K={K} P={P}")
+        tok, top, _ = G.gpu_run(SMALL, B, seed, 0, K, max_batch=64, max_k=2048, scales_key=STRONG,
+                                proposals=P)
+        assert tok.shape == (B, P)
+        assert np.array_equal(tok, full_t[:, :P])
+        assert np.array_equal(top.view(np.uint32), full_l[:, :P].view(np.uint32))
+        ref = G.oracle_run(SMALL, B, seed, 0, K, scales_key=STRONG, proposals=P)
+        compare(tok, top, ref, TOL["bf16"])
+
+
+def test_truncated_rollout_graph_equals_eager():
+    import torch
+    B, seed, P = 9, 960, 8
+    h = G.handle(SMALL, 64, 2048, STRONG)
+    inp = synth.make_inputs(SMALL, B, seed, 0)
+    hid, s, ver = R.device_inputs(inp)
+    for K in (0, 100):
+        G.log(f"[gpu-test] truncated graph K={K}")
+        t_e, l_e = h.run(hid, s, ver, K, proposals=P)
+        t_e, l_e = t_e.clone(), l_e.clone()
+        out_t = torch.empty_like(t_e)
+        out_l = torch.empty_like(l_e)
+        for rep in range(3):
+            out_t.fill_(-7)
+            h.run(hid, s, ver, K, out_tokens=out_t, out_top1=out_l, graph=True, proposals=P)
+            torch.cuda.synchronize()
+            assert torch.equal(out_t, t_e) and torch.equal(out_l.view(torch.int32), l_e.view(torch.int32))
+            h.run(hid, s, ver, K)  # a full eager run on the same handle in between
+            torch.cuda.synchronize()
+
+
+def test_truncated_rollout_errors():
+    import torch
+    h = G.handle(SMALL, 64, 2048, STRONG)
+    inp = synth.make_inputs(SMALL, 3, 961, 0)
+    hid, s, ver = R.device_inputs(inp)
+    for P in (0, 16):
+        with pytest.raises(R.DominoError) as ei:
+            h.run(hid, s, ver, 0, proposals=P, out_tokens=torch.zeros((3, P), dtype=torch.int32,
+                                                                       device="cuda"),
+                  out_top1=torch.zeros((3, P), dtype=torch.float32, device="cuda"))
+        assert ei.value.status == R.DOMINO_ERR_INVALID_ARG
+    # an invalid verified token poisons its request even when no GRU output is used
+    bad = ver.clone()
+    bad[1] = -5
+    t, l = h.run(hid, s, bad, 0, proposals=1)
+    torch.cuda.synchronize()
+    assert int(t[1, 0]) == -1 and torch.isnan(l[1, 0])
+    assert int(t[0, 0]) >= 0 and int(t[2, 0]) >= 0
+
+
 # ------------------------------------------------------------ full-size shapes
 
 FULL = [("8b_b1", 0), ("8b_b8", 2048), ("8b_b64", 0), ("8b_b64", 2048), ("27b_b64", 2048)]
+
+
+def test_full_size_truncated_b8():
+    """The serving pages' b8 variant at full size: 8 proposals of the 8B-shaped
+    rollout at batch 64 with the K = 2048 pool."""
+    wl = synth.WORKLOADS["8b_b64"]
+    G.log("[gpu-test] 8b_b64 K=2048 P=8")
+    tok, top, _ = G.gpu_run(wl.model, wl.batch, wl.input_seed, 0, 2048, max_batch=64, max_k=2048,
+                            proposals=8)
+    ref = G.oracle_run(wl.model, wl.batch, wl.input_seed, 0, 2048, proposals=8)
+    c, _ = compare(tok, top, ref, TOL["bf16"])
+    assert c > 0
 
 
 @pytest.mark.parametrize("name,K", FULL)

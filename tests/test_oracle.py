@@ -36,12 +36,12 @@ def _rand_inputs(rng, B, V, H, r):
             rng.integers(0, V, B).astype(np.int32))
 
 
-def _check_against_brute(out, ref, tol=2e-5, min_margin=1e-3):
+def _check_against_brute(out, ref, tol=2e-5, min_margin=1e-3, steps=T):
     """Tokens equal up to the first step with a near-tie; logits within tol there."""
     B = len(ref["tokens"])
     checked = 0
     for b in range(B):
-        for k in range(T):
+        for k in range(steps):
             if ref["margin"][b][k] < min_margin:
                 break
             assert out["tokens"][b, k] == ref["tokens"][b][k], (b, k)
@@ -84,6 +84,36 @@ def test_teacher_forced_matches_brute_force_on_every_step():
                             forced=forced.tolist())
         got = np.asarray(out["top1"], np.float64)
         assert np.max(np.abs(got - np.asarray(ref["top1"]))) < 2e-5
+
+
+@pytest.mark.parametrize("P", [1, 2, 8, 14])
+@pytest.mark.parametrize("K", [0, 5])
+def test_truncated_rollout_matches_brute_force_prefix(P, K):
+    """A rollout stopped after P proposals (the b8 serving variant verifies 8)
+    is the first P columns of the whole block's rollout: the float64 brute
+    force of the full chain, cut to P columns, pins it."""
+    rng = np.random.default_rng(300 + P + K)
+    V, H, e, g, r, B = 40, 8, 4, 4, 4, 3
+    w = _rand_weights(rng, V, H, e, g, r, scale=2.0)
+    X, s, ver = _rand_inputs(rng, B, V, H, r)
+    out = oracle.rollout(w, X, s, ver, K, proposals=P)
+    assert out["tokens"].shape == (B, P) and out["top1"].shape == (B, P)
+    ref = brute_rollout({k: v.astype(np.float64).tolist() for k, v in w.items()},
+                        X.astype(np.float64).tolist(), s.astype(np.float64).tolist(), ver, K)
+    assert _check_against_brute(out, ref, steps=P) >= min(P, 2)
+    # P = 1 is the plain argmax of base row 0
+    if P == 1:
+        base = np.asarray(X, np.float64) @ np.asarray(w["lm_head"], np.float64).T
+        assert np.array_equal(out["tokens"][:, 0], np.argmax(base[:, 0], axis=1))
+
+
+def test_truncated_rollout_rejects_bad_counts():
+    rng = np.random.default_rng(9)
+    w = _rand_weights(rng, 16, 8, 4, 4, 4)
+    X, s, ver = _rand_inputs(rng, 1, 16, 8, 4)
+    for P in (0, T + 1):
+        with pytest.raises(ValueError):
+            oracle.rollout(w, X, s, ver, 0, proposals=P)
 
 
 # --------------------------------------------------------- library routines
