@@ -6,7 +6,9 @@ requests whose inputs are already resident in HBM, replayed from the
 library's HIP graph.  The default workload is the Qwen3-8B-shaped rollout
 at batch 1 with full-vocabulary correction (K = 0); ``--workload`` and
 ``--k`` select the other cells of the matrix (8B at B = 1/8/64 with K = 0 or
-2048, 27B-class at B = 64).
+2048, 27B-class at B = 64); ``--in-library-s`` has the library form the
+per-step projector offsets from the hiddens inside the timed step instead of
+taking them as an input.
 
 Prints one JSON line: ms per block (lower is better), the roofline figure of
 the dominant kernel (its average duration from HIP events stamped by each of
@@ -80,9 +82,10 @@ def read_traffic(kernel, workload, digest):
     return float(m_t.group(1))
 
 
-def cpu_baseline(w, shape, B, K, input_seed, budget_s, proposals=None):
+def cpu_baseline(w, shape, B, K, input_seed, budget_s, proposals=None, in_library_s=False):
     """The oracle, as it stands, on whole blocks of the same workload until
-    about budget_s seconds of work; ms per block."""
+    about budget_s seconds of work; ms per block (with in_library_s the
+    oracle also forms the step offsets from the hiddens, inside the timing)."""
     import oracle
     from gru_corrected_draft_amd import synth
     try:
@@ -91,7 +94,7 @@ def cpu_baseline(w, shape, B, K, input_seed, budget_s, proposals=None):
     except Exception:
         threads = os.cpu_count()
     f32 = {n: w.f32(n) for n in ("lm_head", "embed", "gru_w_ih", "gru_w_hh", "fc1_w", "fc2_w",
-                                 "fc2_b")}
+                                 "fc2_b", "fc1_x_w", "fc1_b")}
     times = []
     t_start = time.perf_counter()
     trial = 0
@@ -99,7 +102,9 @@ def cpu_baseline(w, shape, B, K, input_seed, budget_s, proposals=None):
         inp = synth.make_inputs(shape, B, input_seed, trial)
         X = inp.hidden_f32()
         t0 = time.perf_counter()
-        oracle.rollout(f32, X, inp.step_s, inp.verified, K, proposals=proposals)
+        s = (oracle.step_offsets(X, f32["fc1_x_w"], f32["fc1_b"]) if in_library_s
+             else inp.step_s)
+        oracle.rollout(f32, X, s, inp.verified, K, proposals=proposals)
         times.append(time.perf_counter() - t0)
         trial += 1
         if time.perf_counter() - t_start > budget_s or trial >= 20:
@@ -121,6 +126,9 @@ def main():
                     help="requests per block (default: the workload's batch)")
     ap.add_argument("--proposals", type=int, default=15,
                     help="proposals per block (< 15: truncated rollout, e.g. 8 for b8 serving)")
+    ap.add_argument("--in-library-s", action="store_true",
+                    help="form the per-step projector offsets in the library from the hiddens "
+                         "(run without step_s)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -163,6 +171,9 @@ def main():
     h = R.DominoRollout(dev, max_batch=B, max_k=max(K, 1))
     P = args.proposals
     prop = None if P == 15 else P
+    if args.in_library_s:
+        assert h.has_offsets, "the weight set has no fc1_x_w / fc1_b"
+        s = None
     out_t = torch.empty((B, P), dtype=torch.int32, device="cuda")
     out_l = torch.empty((B, P), dtype=torch.float32, device="cuda")
 
@@ -246,6 +257,7 @@ def main():
                    "batch": B, "K": K, "vocab": shape.vocab, "hidden": shape.hidden,
                    "emb_dim": shape.emb_dim, "gru_hidden": shape.gru_hidden,
                    "proj_dim": shape.proj_dim, "block_size": 16, "proposals": P,
+                   "step_offsets": "in library" if args.in_library_s else "input",
                    "accumulate": "fp32",
                    "mode": "hip graph replay"},
         "roofline": roof,
@@ -255,7 +267,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (~{args.cpu_budget:.0f}s)")
-        line["cpu_baseline"] = cpu_baseline(w, shape, B, K, wl.input_seed, args.cpu_budget, prop)
+        line["cpu_baseline"] = cpu_baseline(w, shape, B, K, wl.input_seed, args.cpu_budget, prop,
+                                            args.in_library_s)
     else:
         line["cpu_baseline"] = None
     h.close()

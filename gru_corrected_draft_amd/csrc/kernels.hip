@@ -13,6 +13,7 @@
 //    "Implementation" / "Validation and limitations": the pool is a TopK of
 //    the block's base logits whose cutoff ties the page leaves open (here:
 //    lower id wins).
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -96,6 +97,199 @@ __device__ __forceinline__ float load_w(const W_t<BF>* p) {
     return bf16_to_f32(*p);
   } else {
     return *p;
+  }
+}
+
+// ------------------------------------------------ per-step projector offsets
+// step_s[b, j, n] = fc1_x[n, :] . X[b, j+1, :] + fc1_b[n], j = 0..13: the
+// backbone-hidden half of the projector's first layer ([backbone hidden |
+// GRU state], "Add correctness-first Domino support to DFlash V2", commit
+// text) and its bias, for the hidden of the position whose base row the
+// correction step scores.
+//
+// bf16 models: one MFMA product C[m, n] over the M = 14B (request, step) rows
+// m = 14b + j, which is exactly the row order of step_s, so the epilogue
+// stores straight into [B, 14, r].  A workgroup computes 64 units n x 64 rows
+// m; its four waves own 32 x 32 each (2 x 2 tiles of 16x16x32).  k runs in
+// slices of 64 staged in LDS (two buffers, the next slice's 16-byte loads in
+// flight in registers while the current one is multiplied; rows padded to
+// 144 bytes so the fragment reads of 16 lanes hit distinct banks).  With few
+// tiles (small batches) k is split over up to 16 workgroups, each writing its
+// partial product, and a combine kernel adds the splits in a fixed order and
+// the bias.  fp32 models (small) take a direct kernel.
+constexpr int kOfsTile = 64;           // units and rows per workgroup
+constexpr int kOfsSlice = 64;          // k per LDS stage
+constexpr int kOfsPitch = 72;          // LDS row pitch in bf16 (144 bytes)
+constexpr int kOfsMinSlices = 4;       // k slices per split at least
+constexpr int kOfsTargetGroups = 256;  // split k until about this many workgroups
+
+__global__ __launch_bounds__(256) void offsets_gemm_kernel(const bf16_t* __restrict__ W,
+                                                           const bf16_t* __restrict__ X,
+                                                           const bf16_t* __restrict__ b1,
+                                                           float* __restrict__ out, int M, int N,
+                                                           int H, int kper) {
+  __shared__ __attribute__((aligned(16))) bf16_t lw[2][kOfsTile * kOfsPitch];
+  __shared__ __attribute__((aligned(16))) bf16_t lx[2][kOfsTile * kOfsPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int n0 = blockIdx.x * kOfsTile, m0 = blockIdx.y * kOfsTile, split = blockIdx.z;
+  const int kbeg = split * kper, nsl = kper / kOfsSlice;
+  // loader: thread t moves 16 bytes at column 8 (t % 8) of rows t / 8 and t / 8 + 32
+  const int lr = tid >> 3, lc = (tid & 7) * 8;
+  const bf16_t* wp[2];
+  const bf16_t* xp[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = min(n0 + lr + 32 * i, N - 1);  // rows past the end are loaded and dropped
+    const int m = min(m0 + lr + 32 * i, M - 1);
+    const int b = m / DOMINO_S, j = m - b * DOMINO_S;
+    wp[i] = W + (size_t)n * H + kbeg + lc;
+    xp[i] = X + ((size_t)b * DOMINO_T + j + 1) * H + kbeg + lc;
+  }
+  uint4 rw[2], rx[2];
+  auto fetch = [&](int sl) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      rw[i] = *reinterpret_cast<const uint4*>(wp[i] + (size_t)sl * kOfsSlice);
+      rx[i] = *reinterpret_cast<const uint4*>(xp[i] + (size_t)sl * kOfsSlice);
+    }
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<uint4*>(&lw[buf][(lr + 32 * i) * kOfsPitch + lc]) = rw[i];
+      *reinterpret_cast<uint4*>(&lx[buf][(lr + 32 * i) * kOfsPitch + lc]) = rx[i];
+    }
+  };
+  const int wn = wave & 1, wm = wave >> 1, fr = lane & 15, fq = lane >> 4;
+  v4f acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = v4f{0.f, 0.f, 0.f, 0.f};
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int sl = 0; sl < nsl; ++sl) {
+    const int buf = sl & 1;
+    fetch(min(sl + 1, nsl - 1));  // the last iteration reloads its own slice (unused)
+#pragma unroll
+    for (int ks = 0; ks < kOfsSlice / 32; ++ks) {
+      v8s a[2], bx[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = *reinterpret_cast<const v8s*>(
+            &lw[buf][(32 * wn + 16 * i + fr) * kOfsPitch + ks * 32 + 8 * fq]);
+        bx[i] = *reinterpret_cast<const v8s*>(
+            &lx[buf][(32 * wm + 16 * i + fr) * kOfsPitch + ks * 32 + 8 * fq]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mfma_bf16(a[i], bx[jj], acc[i][jj]);
+    }
+    // the other buffer was last read before the previous barrier
+    put(buf ^ 1);
+    __syncthreads();
+  }
+  // lane: row m = m0 + 32 wm + 16 jj + fr, units n = n0 + 32 wn + 16 i + 4 fq + 0..3
+  const bool whole = gridDim.z == 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int n = n0 + 32 * wn + 16 * i + 4 * fq;
+    if (n >= N) continue;  // N % 4 == 0, so n < N covers n + 3
+    float bias[4] = {0.f, 0.f, 0.f, 0.f};
+    if (whole) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bias[c] = bf16_to_f32(b1[n + c]);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int m = m0 + 32 * wm + 16 * jj + fr;
+      if (m >= M) continue;
+      float* o = out + ((size_t)split * M + m) * N + n;
+      *reinterpret_cast<float4*>(o) = make_float4(acc[i][jj][0] + bias[0], acc[i][jj][1] + bias[1],
+                                                  acc[i][jj][2] + bias[2], acc[i][jj][3] + bias[3]);
+    }
+  }
+}
+
+// s = sum of the split partials in split order, plus the bias
+__global__ __launch_bounds__(256) void offsets_combine_kernel(const float* __restrict__ part,
+                                                              const bf16_t* __restrict__ b1,
+                                                              float* __restrict__ s, int M, int N,
+                                                              int splits) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;  // one float4 of s
+  const size_t MN = (size_t)M * N;
+  if ((size_t)idx * 4 >= MN) return;
+  const int n = (int)(((size_t)idx * 4) % N);
+  float4 acc = reinterpret_cast<const float4*>(part)[idx];
+  for (int p = 1; p < splits; ++p) {
+    const float4 v = reinterpret_cast<const float4*>(part + p * MN)[idx];
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  acc.x += bf16_to_f32(b1[n]);
+  acc.y += bf16_to_f32(b1[n + 1]);
+  acc.z += bf16_to_f32(b1[n + 2]);
+  acc.w += bf16_to_f32(b1[n + 3]);
+  reinterpret_cast<float4*>(s)[idx] = acc;
+}
+
+// fp32 models: one thread per entry of s
+__global__ __launch_bounds__(256) void step_offsets_f32_kernel(const float* __restrict__ X,
+                                                               const float* __restrict__ W,
+                                                               const float* __restrict__ b1,
+                                                               float* __restrict__ s, int B, int H,
+                                                               int r) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= B * DOMINO_S * r) return;
+  const int b = idx / (DOMINO_S * r), rem = idx - b * (DOMINO_S * r);
+  const int j = rem / r, n = rem - j * r;
+  const float* x = X + ((size_t)b * DOMINO_T + j + 1) * H;
+  const float* wr = W + (size_t)n * H;
+  float acc = 0.f;
+  for (int i = 0; i < H; ++i) acc = fmaf(x[i], wr[i], acc);
+  s[idx] = acc + b1[n];
+}
+
+// k splits of the offsets product for a batch of B (1 when it is not tiled)
+int step_offsets_splits(int B, int H, int r) {
+  if (H % kOfsSlice != 0 || r % 4 != 0) return 1;
+  const int tiles = ((r + kOfsTile - 1) / kOfsTile) * ((B * DOMINO_S + kOfsTile - 1) / kOfsTile);
+  const int nsl = H / kOfsSlice;
+  int splits = 1;
+  while (splits * 2 * tiles <= kOfsTargetGroups && nsl % (splits * 2) == 0 &&
+         nsl / (splits * 2) >= kOfsMinSlices)
+    splits *= 2;
+  return splits;
+}
+
+size_t step_offsets_partial_floats(int Bmax, int H, int r) {
+  size_t most = 0;
+  for (int B = 1; B <= Bmax; ++B) {
+    const int sp = step_offsets_splits(B, H, r);
+    if (sp > 1) most = std::max(most, (size_t)sp * B * DOMINO_S * r);
+  }
+  return most;
+}
+
+void launch_step_offsets(const Shape& s, const DeviceWeights& w, const void* X, const Workspace& ws,
+                         int B, hipStream_t st) {
+  const int M = B * DOMINO_S, N = s.r, H = s.H, n = M * N;
+  if (s.bf16) {  // create() and run() guarantee H % 64 == 0, r % 32 == 0, 16-byte aligned rows
+    const int splits = step_offsets_splits(B, H, N);
+    const dim3 grid((N + kOfsTile - 1) / kOfsTile, (M + kOfsTile - 1) / kOfsTile, splits);
+    DLAUNCH(offsets_gemm_kernel, grid, dim3(256), 0, st, (const bf16_t*)w.fc1_x,
+            (const bf16_t*)X, (const bf16_t*)w.fc1_b, splits > 1 ? ws.s_tmp : ws.s, M, N, H,
+            H / splits);
+    if (splits > 1)
+      DLAUNCH(offsets_combine_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st,
+              (const float*)ws.s_tmp, (const bf16_t*)w.fc1_b, ws.s, M, N, splits);
+  } else {
+    DLAUNCH(step_offsets_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, (const float*)X,
+            (const float*)w.fc1_x, (const float*)w.fc1_b, ws.s, B, H, N);
   }
 }
 

@@ -28,6 +28,8 @@ struct DeviceWeights {
   const void* fc1;
   const void* fc2;
   const void* fc2_b;
+  const void* fc1_x;  // optional backbone-hidden half of projector layer 1 [r, H]
+  const void* fc1_b;  // optional projector layer 1 bias [r]
 };
 
 struct Shape {
@@ -51,6 +53,8 @@ struct Workspace {
   uint64_t* slots;     // [15, Bmax] argmax words
   int32_t* bad;        // [Bmax]
   float* partial;      // split-k partial sums of the GRU / fc1 products
+  float* s_tmp;        // [14 * Bmax, r] step-major products of the s computation
+  float* s;            // [Bmax, 14, r] per-step projector offsets formed in the library
 };
 
 // most workgroups per 16-unit tile along k in the MFMA GRU / fc1 products
@@ -65,7 +69,7 @@ struct StreamArgs {
   const uint16_t* act_hi;  // activation rows, bf16
   const uint16_t* act_lo;  // low halves (correction) or nullptr
   int ncols;               // activation columns (<= 128)
-  int col_B;               // > 0: column m reads row (m % col_B) * 15 + m / col_B
+  int col_B;               // > 0: column m reads row (m % col_B) * DOMINO_T + m / col_B
   int KS;                  // k slice staged in LDS (set by the launcher)
   float* out;              // store epilogue: [ncols, N]
   const uint16_t* b2;      // argmax epilogue: bias [N], base row [ncols, N], words [ncols]
@@ -147,6 +151,12 @@ void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace
                          hipStream_t st);
 void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
                          int K, hipStream_t st);
+// step_s[b, j, :] = fc1_x · X[b, j+1, :] + fc1_b into ws.s; the k-split
+// partials (when batches are small) go to ws.s_tmp, which holds
+// step_offsets_partial_floats(max_batch, H, r) floats
+size_t step_offsets_partial_floats(int Bmax, int H, int r);
+void launch_step_offsets(const Shape& s, const DeviceWeights& w, const void* X, const Workspace& ws,
+                         int B, hipStream_t st);
 // tokens and top-1 logits of proposals 1..P, [B, P]
 void launch_writeout(const Workspace& ws, int B, int P, int32_t* out_tokens, float* out_top1,
                      hipStream_t st);

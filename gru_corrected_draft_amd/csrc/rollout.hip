@@ -9,6 +9,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -43,8 +44,8 @@ struct GraphEntry {
   hipGraphExec_t exec;
 };
 
-constexpr int kPhases = 6;
-enum Phase { kLmHead = 0, kCorrect = 1, kGru = 2, kFc1 = 3, kPool = 4, kArgmax0 = 5 };
+constexpr int kPhases = 7;
+enum Phase { kLmHead = 0, kCorrect = 1, kGru = 2, kFc1 = 3, kPool = 4, kArgmax0 = 5, kOffsets = 6 };
 
 }  // namespace
 
@@ -58,6 +59,7 @@ struct domino_rollout {
   std::vector<GraphEntry> graphs;
   hipStream_t capture_stream = nullptr;
   int last_B = 0, last_K = 0;  // shape of the last enqueued run
+  bool last_s_internal = false;  // the last run formed step_s itself
   // measurement: kernel event pairs of the timed phases (see PhaseTimer)
   bool timing = false;
   bool capturing = false;
@@ -154,6 +156,14 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
       return DOMINO_ERR_INVALID_ARG;
     }
   }
+  if ((w->fc1_x_w == nullptr) != (w->fc1_b == nullptr)) {
+    set_global_err("create: fc1_x_w and fc1_b must be given together");
+    return DOMINO_ERR_INVALID_ARG;
+  }
+  if (w->fc1_x_w && ((uintptr_t)w->fc1_x_w & 15)) {
+    set_global_err("create: weight matrices must be 16-byte aligned");
+    return DOMINO_ERR_INVALID_ARG;
+  }
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     set_global_err("create: no HIP device");
@@ -171,7 +181,8 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
 
   domino_rollout* h = new domino_rollout();
   h->cfg = *cfg;
-  h->w = DeviceWeights{w->lm_head, w->embed, w->gru_w_ih, w->gru_w_hh, w->fc1_w, w->fc2_w, w->fc2_b};
+  h->w = DeviceWeights{w->lm_head, w->embed, w->gru_w_ih, w->gru_w_hh, w->fc1_w,
+                       w->fc2_w,   w->fc2_b, w->fc1_x_w,  w->fc1_b};
   h->shape = Shape{cfg->vocab, cfg->hidden, cfg->emb_dim, cfg->gru_hidden, cfg->proj_dim,
                    cfg->dtype == DOMINO_DTYPE_BF16};
   h->device = dev;
@@ -203,10 +214,16 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   // split-k partials: [16-unit tile][split][gate (GRU: 4, fc1: 1)][64 requests][16 units]
   const size_t tiles = (g > r ? g : r) / 16;
   ws.partial = (float*)alloc(tiles * kGemvSplit * 4 * 64 * 16 * sizeof(float));
+  if (h->w.fc1_x) {  // in-library step offsets
+    ws.s_tmp = (float*)alloc(std::max<size_t>(step_offsets_partial_floats((int)Bm, cfg->hidden, (int)r), 64) *
+                             sizeof(float));
+    ws.s = (float*)alloc((size_t)DOMINO_S * Bm * r * sizeof(float));
+  }
   for (void* p : {(void*)ws.base, (void*)ws.keys, (void*)ws.hist, (void*)ws.state, (void*)ws.counts,
                   (void*)ws.pool_ids, (void*)ws.pool_base, (void*)ws.h[0], (void*)ws.h[1],
                   (void*)ws.u, (void*)ws.u_hi, (void*)ws.u_lo, (void*)ws.slots, (void*)ws.bad,
-                  (void*)ws.partial}) {
+                  (void*)ws.partial, h->w.fc1_x ? (void*)ws.s : (void*)ws.partial,
+                  h->w.fc1_x ? (void*)ws.s_tmp : (void*)ws.partial}) {
     if (!p) {
       set_global_err("create: workspace allocation failed");
       domino_rollout_destroy(h);
@@ -258,8 +275,11 @@ extern "C" const char* domino_rollout_last_error(const domino_rollout_t* h) {
 static domino_status_t check_run_args(domino_rollout_t* h, const void* hidden, const float* s,
                                       const int32_t* ver, int32_t B, int32_t K, int32_t* out_tokens) {
   if (!h) return DOMINO_ERR_INVALID_ARG;
-  if (!hidden || !s || !ver || !out_tokens)
-    return h->fail(DOMINO_ERR_INVALID_ARG, "run: hidden, step_s, verified_tokens and out_tokens must be non-NULL");
+  if (!hidden || !ver || !out_tokens)
+    return h->fail(DOMINO_ERR_INVALID_ARG, "run: hidden, verified_tokens and out_tokens must be non-NULL");
+  if (!s && !h->w.fc1_x)
+    return h->fail(DOMINO_ERR_INVALID_ARG,
+                   "run: step_s is NULL and the handle holds no fc1_x_w / fc1_b to form it");
   if (((uintptr_t)hidden & 15) || ((uintptr_t)s & 3))
     return h->fail(DOMINO_ERR_INVALID_ARG, "run: base_hidden must be 16-byte aligned");
   if (B < 1 || B > h->cfg.max_batch)
@@ -327,6 +347,13 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
   h->last_B = B;
   h->last_K = pool ? K : 0;
   launch_reset(ws, B, pool ? K : 0, st);
+  h->last_s_internal = s == nullptr;
+  if (!s) {
+    // step offsets from the block's hiddens (projector layer 1, backbone half)
+    PhaseTimer t(h, kOffsets, st);
+    launch_step_offsets(sh, h->w, hidden, ws, B, st);
+    s = ws.s;
+  }
   const bool fused = sh.bf16 && B >= kFusedMinBatch && lmhead_fused_supported(sh.H);
   if (fused) {
     // base logits, pool-score keys and the first proposal in one pass
@@ -513,6 +540,9 @@ extern "C" domino_status_t domino_rollout_read_workspace(const domino_rollout_t*
   } else if (which == 1 && h->last_K > 0) {
     src = h->ws.pool_ids;
     n = (size_t)h->last_B * h->last_K * 4;
+  } else if (which == 2 && h->last_s_internal) {
+    src = h->ws.s;
+    n = (size_t)h->last_B * DOMINO_S * h->cfg.proj_dim * 4;
   } else {
     return DOMINO_ERR_INVALID_ARG;
   }

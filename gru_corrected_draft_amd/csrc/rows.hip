@@ -31,11 +31,13 @@ __device__ __forceinline__ void load4(const float* p, float (&w)[4]) {
 
 // 4 consecutive elements at k of a row of length n (n % 4 == 0), or zeros when
 // k >= n.  The address is clamped instead of branched on, so consecutive
-// loads issue back to back without a wait between them.
+// loads issue back to back without a wait between them; a masked lane reads
+// the row's first 4 elements, which exist for every row this file reads
+// (n may be 0 when the row is not used at all, e.g. W_hh with h = 0).
 template <typename T>
 __device__ __forceinline__ void load4z(const T* row, int k, int n, float (&w)[4]) {
   const bool ok = k < n;
-  load4(row + (ok ? k : n - 4), w);
+  load4(row + (ok ? k : 0), w);
 #pragma unroll
   for (int i = 0; i < 4; ++i) w[i] = ok ? w[i] : 0.f;
 }

@@ -31,7 +31,7 @@ EXPORTED = ("domino_rollout_create", "domino_rollout_run", "domino_rollout_run_g
             "domino_rollout_read_workspace", "domino_rollout_destroy",
             "domino_rollout_last_error", "domino_rollout_set_timing",
             "domino_rollout_kernel_times")
-PHASES = {"lmhead": 0, "correct": 1, "gru": 2, "fc1": 3, "pool": 4, "argmax0": 5}
+PHASES = {"lmhead": 0, "correct": 1, "gru": 2, "fc1": 3, "pool": 4, "argmax0": 5, "offsets": 6}
 
 
 class Config(ctypes.Structure):
@@ -44,10 +44,13 @@ class Config(ctypes.Structure):
 
 class WeightPtrs(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("lm_head", "embed", "gru_w_ih", "gru_w_hh", "fc1_w", "fc2_w", "fc2_b")]
+                ("lm_head", "embed", "gru_w_ih", "gru_w_hh", "fc1_w", "fc2_w", "fc2_b",
+                 "fc1_x_w", "fc1_b")]
 
 
-WEIGHT_NAMES = [n for n, _ in WeightPtrs._fields_]
+# required weights, and the optional pair that lets the library form step_s
+WEIGHT_NAMES = ["lm_head", "embed", "gru_w_ih", "gru_w_hh", "fc1_w", "fc2_w", "fc2_b"]
+OFFSET_WEIGHT_NAMES = ["fc1_x_w", "fc1_b"]
 
 _lib = None
 
@@ -122,7 +125,8 @@ class DominoRollout:
         dt = lm.dtype
         if dt not in (torch.bfloat16, torch.float32):
             raise TypeError("weights must be bfloat16 or float32")
-        for n in WEIGHT_NAMES:
+        self.has_offsets = all(n in weights for n in OFFSET_WEIGHT_NAMES)
+        for n in WEIGHT_NAMES + (OFFSET_WEIGHT_NAMES if self.has_offsets else []):
             t = weights[n]
             if t.dtype != dt or not t.is_cuda or not t.is_contiguous():
                 raise TypeError(f"weight {n} must be a contiguous {dt} device tensor")
@@ -135,7 +139,10 @@ class DominoRollout:
         self.cfg = make_config(V, H, e, g, r, max_batch, max_k,
                                DTYPE_BF16 if dt == torch.bfloat16 else DTYPE_FP32)
         self._weights = dict(weights)
-        wp = WeightPtrs(*[weights[n].data_ptr() for n in WEIGHT_NAMES])
+        names = WeightPtrs._fields_
+        wp = WeightPtrs(*[weights[n].data_ptr() if n in weights and
+                          (n not in OFFSET_WEIGHT_NAMES or self.has_offsets) else None
+                          for n, _ in names])
         h = ctypes.c_void_p()
         st = self.lib.domino_rollout_create(ctypes.byref(self.cfg), ctypes.byref(wp), ctypes.byref(h))
         if st != DOMINO_OK:
@@ -155,11 +162,14 @@ class DominoRollout:
         V, H, e, g, r = self.shape
         if hidden.shape != (B, N_PROPOSALS, H) or hidden.dtype != self.dtype:
             raise ValueError("hidden must be [B, 15, H] in the weights' dtype")
-        if step_s.shape != (B, N_STEPS, r) or step_s.dtype != torch.float32:
+        if step_s is None:
+            if not self.has_offsets:
+                raise ValueError("step_s is required: the handle holds no fc1_x_w / fc1_b")
+        elif step_s.shape != (B, N_STEPS, r) or step_s.dtype != torch.float32:
             raise ValueError("step_s must be [B, 14, r] float32")
         if verified.shape != (B,) or verified.dtype != torch.int32:
             raise ValueError("verified must be [B] int32")
-        for t in (hidden, step_s, verified):
+        for t in (hidden, verified) + (() if step_s is None else (step_s,)):
             if not t.is_cuda or not t.is_contiguous():
                 raise ValueError("inputs must be contiguous device tensors")
         dev = hidden.device
@@ -193,12 +203,13 @@ class DominoRollout:
 
     def read_workspace(self, which):
         """Copy of a workspace buffer of the last run: 0 = base logits
-        [15, B, V] fp32 (step-major), 1 = pool ids [B, K] int32."""
+        [15, B, V] fp32 (step-major), 1 = pool ids [B, K] int32, 2 = the step
+        offsets [B, 14, r] fp32 the library formed (runs with step_s=None)."""
         import torch
         n = ctypes.c_size_t()
         self._check(self.lib.domino_rollout_read_workspace(self.handle, which, None, 0,
                                                            ctypes.byref(n), None))
-        dt = torch.float32 if which == 0 else torch.int32
+        dt = torch.int32 if which == 1 else torch.float32
         out = torch.empty(n.value // 4, dtype=dt, device="cuda")
         st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self._check(self.lib.domino_rollout_read_workspace(self.handle, which, _ptr(out), n.value,
@@ -238,7 +249,7 @@ def device_weights(w, device="cuda"):
     import numpy as np
     import torch
     out = {}
-    for n in WEIGHT_NAMES:
+    for n in WEIGHT_NAMES + [n for n in OFFSET_WEIGHT_NAMES if n in w.raw]:
         a = w.raw[n]
         if a.dtype == np.uint16:
             t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)

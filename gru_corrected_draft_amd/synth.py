@@ -12,8 +12,10 @@ Recipe (every array is reproducible from its seeds alone):
   ``numpy.random.Generator(PCG64(SeedSequence([weight_seed, stream, j])))
   .standard_normal(float32)`` and multiplied by ``scale / sqrt(fan_in)``
   (fan_in = the tensor's second dimension, the PyTorch convention; the 1-D
-  fc2 bias uses the projector width).  The block split makes the stream
-  independent of how many threads fill it.
+  biases fc2_b and fc1_b use the projector width).  fc1_x_w [r, H] and fc1_b
+  are the backbone-hidden half of the projector's first layer and its bias,
+  used when the per-step offsets s are computed from the hiddens.  The block
+  split makes the stream independent of how many threads fill it.
 * bf16 tensors are the float32 draw rounded to bfloat16 with
   round-to-nearest-even, stored as uint16 bit patterns.
 * Per-trial inputs use ``SeedSequence([input_seed, 1 + trial, stream])``:
@@ -41,7 +43,7 @@ N_STEPS = BLOCK_SIZE - 2  # correction steps after the first proposal
 
 # stream ids of the weight tensors
 _STREAMS = {"lm_head": 1, "embed": 2, "gru_w_ih": 3, "gru_w_hh": 4,
-            "fc1_w": 5, "fc2_w": 6, "fc2_b": 7}
+            "fc1_w": 5, "fc2_w": 6, "fc2_b": 7, "fc1_x_w": 8, "fc1_b": 9}
 _INPUT_STREAMS = {"hidden": 1, "step_s": 2, "verified": 3}
 
 
@@ -59,7 +61,8 @@ class ModelShape:
     def tensor_shapes(self):
         V, H, e, g, r = self.vocab, self.hidden, self.emb_dim, self.gru_hidden, self.proj_dim
         return {"lm_head": (V, H), "embed": (V, e), "gru_w_ih": (3 * g, e),
-                "gru_w_hh": (3 * g, g), "fc1_w": (r, g), "fc2_w": (V, r), "fc2_b": (V,)}
+                "gru_w_hh": (3 * g, g), "fc1_w": (r, g), "fc2_w": (V, r), "fc2_b": (V,),
+                "fc1_x_w": (r, H), "fc1_b": (r,)}
 
     def fan_in(self, name):
         shp = self.tensor_shapes()[name]

@@ -88,6 +88,14 @@ typedef struct {
   const void* fc1_w;     /* [r, g]  projector layer 1 (GRU half)               */
   const void* fc2_w;     /* [V, r]  projector layer 2                          */
   const void* fc2_b;     /* [V]     projector layer 2 bias                     */
+  /* Optional (both or neither; NULL: the caller passes step_s to every run):
+   * the backbone-hidden half of projector layer 1 and that layer's bias.
+   * With them a run may pass step_s = NULL and the library forms
+   * step_s[b, j, :] = fc1_x_w · base_hidden[b, j+1, :] + fc1_b itself
+   * (projector input [backbone hidden | GRU state], "Add correctness-first
+   * Domino support to DFlash V2", commit text). */
+  const void* fc1_x_w;   /* [r, H]  projector layer 1 (backbone-hidden half)   */
+  const void* fc1_b;     /* [r]     projector layer 1 bias                     */
 } domino_weights_t;
 
 typedef struct domino_rollout domino_rollout_t;
@@ -104,7 +112,9 @@ domino_status_t domino_rollout_create(const domino_config_t* cfg, const domino_w
  * = the default stream).  Device pointers, caller-owned:
  *   base_hidden     [batch, 15, H]  dtype of the config: the block's draft hiddens
  *   step_s          [batch, 14, r]  fp32: the backbone-hidden half of the
- *                                   projector input plus the fc1 bias, per step
+ *                                   projector input plus the fc1 bias, per step;
+ *                                   NULL if the handle holds fc1_x_w / fc1_b
+ *                                   (the library then computes it)
  *   verified_tokens [batch]         int32 in [0, V)
  *   out_tokens      [batch, 15]     int32: proposals 1..15
  *   out_top1_logit  [batch, 15]     fp32 or NULL: the winning logit of each
@@ -158,7 +168,8 @@ domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const void* base_
 /* Copies a workspace buffer of the last run into dst (device memory of at
  * least dst_bytes), stream-ordered on `stream`.  which: 0 = base logits fp32
  * [15, batch, V] (step-major), 1 = pool ids int32 [batch, K] sorted
- * ascending (pool runs only).  *bytes receives the buffer's size for the
+ * ascending (pool runs only), 2 = step_s fp32 [batch, 14, r] as the library
+ * computed it (runs with step_s = NULL only).  *bytes receives the buffer's size for the
  * last run; with dst == NULL nothing is copied.  INVALID_ARG if which is
  * unknown, no run has happened, or dst_bytes is too small. */
 domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t which, void* dst,
@@ -173,8 +184,8 @@ domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t
  * instances of one phase: 0 = LM-head GEMM, 1 = correction + argmax (full
  * vocabulary or pool), 2 = GRU cell (with its split-sum kernel where used),
  * 3 = fc1 + SiLU (likewise), 4 = pool build (all its kernels), 5 =
- * first-proposal argmax.  which = -1 clears the totals.  Timing changes no
- * result. */
+ * first-proposal argmax, 6 = step offsets formed in the library.  which = -1
+ * clears the totals.  Timing changes no result. */
 domino_status_t domino_rollout_set_timing(domino_rollout_t* h, int32_t enable);
 domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int32_t which, double* total_ms,
                                             int64_t* launches);

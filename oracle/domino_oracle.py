@@ -130,6 +130,23 @@ def gru_cell(x: np.ndarray, h: np.ndarray, w_ih: np.ndarray, w_hh: np.ndarray) -
     return (F32(1.0) - z) * n + z * h
 
 
+def step_offsets(hidden: np.ndarray, fc1_x_w: np.ndarray, fc1_b: np.ndarray) -> np.ndarray:
+    """Per-step projector offsets s [B, 14, r] from the block's hiddens.
+
+    The projector's first layer reads [backbone hidden | GRU state] ("Add
+    correctness-first Domino support to DFlash V2", commit text); its GRU
+    half is fc1_w, applied to h inside the rollout, and this is the other
+    half plus the layer's bias: s row j of request b = fc1_x_w · X[b, j+1] +
+    fc1_b, j = 0..13.  Row j feeds correction step j+1, which scores base row
+    j+1, the LM-head row of that same hidden (step alignment of the rollout
+    loop below).  fp32 like the rest of the oracle.
+    """
+    X = np.asarray(hidden, F32)
+    W = np.asarray(fc1_x_w, F32)
+    b1 = np.asarray(fc1_b, F32)
+    return (X[:, 1:, :] @ W.T + b1).astype(F32)
+
+
 def rollout(weights: dict, hidden: np.ndarray, step_s: np.ndarray, verified: np.ndarray,
             K: int, forced: np.ndarray | None = None, record: dict | None = None,
             proposals: int | None = None) -> dict:

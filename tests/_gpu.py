@@ -23,7 +23,7 @@ def model(name_or_shape, scales_key=()):
     log(f"[gpu-test] generating weights for {shape.name} {dict(scales)}")
     w = synth.make_weights(shape, scales)
     dev = R.device_weights(w)
-    f32 = {n: w.f32(n) for n in R.WEIGHT_NAMES}
+    f32 = {n: w.f32(n) for n in R.WEIGHT_NAMES + R.OFFSET_WEIGHT_NAMES}
     return w, dev, f32
 
 

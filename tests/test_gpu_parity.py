@@ -259,6 +259,85 @@ def test_run_rejects_bad_scalars_without_launching():
     assert torch.all(out == 5)
 
 
+# ------------------------------------------------ step offsets in the library
+
+def _offsets_ref(model_key, B, seed, scales_key=()):
+    import oracle
+    shape = synth.MODELS[model_key] if isinstance(model_key, str) else model_key
+    _, _, f32 = G.model(model_key, scales_key)
+    inp = synth.make_inputs(shape, B, seed, 0)
+    X = inp.hidden_f32()
+    s = oracle.step_offsets(X, f32["fc1_x_w"], f32["fc1_b"])
+    # fp32 dot-product error bound of each entry (H terms)
+    Xa = np.abs(X[:, 1:, :].astype(np.float64))
+    bound = X.shape[2] * 2.0 ** -24 * 1.01 * (Xa @ np.abs(f32["fc1_x_w"].astype(np.float64)).T)
+    return inp, s, bound + 1e-6
+
+
+@pytest.mark.parametrize("shape_name,B", [("small", 1), ("small", 9), ("small", 10),
+                                          ("small", 64), ("deep", 1), ("deep", 9),
+                                          ("deep", 64)])
+def test_step_offsets_formed_in_library(shape_name, B):
+    """run(..., step_s=None) forms s = fc1_x_w . X[:, 1:] + fc1_b on the GPU:
+    s within the fp32 dot bound of the oracle's, and the rollout meets the
+    oracle run on that s.  SMALL (H = 256) takes the MFMA product whole; DEEP
+    (H = 1024) splits k over four workgroups and combines the partials."""
+    import oracle
+    import torch
+    shape = SMALL if shape_name == "small" else DEEP
+    seed = 970 + B
+    inp, s_ref, bound = _offsets_ref(shape, B, seed, STRONG)
+    h = G.handle(shape, 64, 2048, STRONG)
+    hid, _, ver = R.device_inputs(inp)
+    _, _, f32 = G.model(shape, STRONG)
+    for K in (0, 100):
+        G.log(f"[gpu-test] in-library step offsets {shape_name} B={B} K={K}")
+        tok, top = h.run(hid, None, ver, K)
+        torch.cuda.synchronize()
+        s_gpu = h.read_workspace(2).cpu().numpy().reshape(B, 14, -1)
+        assert np.all(np.abs(s_gpu.astype(np.float64) - s_ref) <= bound)
+        ref = oracle.rollout(f32, inp.hidden_f32(), s_ref, inp.verified, K)
+        compare(tok.cpu().numpy(), top.cpu().numpy(), ref, TOL["bf16"])
+
+
+def test_step_offsets_fp32_model():
+    import oracle
+    import torch
+    wl = synth.WORKLOADS["tiny_b1"]
+    inp, s_ref, bound = _offsets_ref("tiny", 1, wl.input_seed)
+    h = G.handle("tiny", 1, 256)
+    hid, _, ver = R.device_inputs(inp)
+    tok, top = h.run(hid, None, ver, 0)
+    torch.cuda.synchronize()
+    s_gpu = h.read_workspace(2).cpu().numpy().reshape(1, 14, -1)
+    assert np.all(np.abs(s_gpu.astype(np.float64) - s_ref) <= bound)
+    _, _, f32 = G.model("tiny")
+    ref = oracle.rollout(f32, inp.hidden_f32(), s_ref, inp.verified, 0)
+    compare(tok.cpu().numpy(), top.cpu().numpy(), ref, TOL["fp32"])
+
+
+def test_null_step_s_needs_offset_weights():
+    import ctypes
+    import torch
+    _, dev, _ = G.model(SMALL, STRONG)
+    bare = {k: v for k, v in dev.items() if k in R.WEIGHT_NAMES}
+    h = R.DominoRollout(bare, max_batch=4, max_k=16)
+    try:
+        inp = synth.make_inputs(SMALL, 2, 975, 0)
+        hid, s, ver = R.device_inputs(inp)
+        out = torch.full((2, 15), 3, dtype=torch.int32, device="cuda")
+        p = ctypes.c_void_p
+        st = h.lib.domino_rollout_run(h.handle, p(hid.data_ptr()), None, p(ver.data_ptr()), 2, 0,
+                                      p(out.data_ptr()), None, None)
+        assert st == R.DOMINO_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+        assert torch.all(out == 3)
+        with pytest.raises(ValueError):
+            h.run(hid, None, ver, 0)
+    finally:
+        h.close()
+
+
 # ------------------------------------------------------- truncated rollouts
 
 @pytest.mark.parametrize("B,K", [(1, 0), (5, 100), (17, 0), (64, 100)])
@@ -323,6 +402,21 @@ def test_truncated_rollout_errors():
 # ------------------------------------------------------------ full-size shapes
 
 FULL = [("8b_b1", 0), ("8b_b8", 2048), ("8b_b64", 0), ("8b_b64", 2048), ("27b_b64", 2048)]
+
+
+@pytest.mark.parametrize("name", ["8b_b8", "8b_b64"])
+def test_full_size_step_offsets(name):
+    """Library-formed s at full size (k split 8 ways at B = 8, whole at B = 64)."""
+    import torch
+    wl = synth.WORKLOADS[name]
+    inp, s_ref, bound = _offsets_ref(wl.model, wl.batch, wl.input_seed)
+    h = G.handle(wl.model, 64, 2048)
+    hid, _, ver = R.device_inputs(inp)
+    G.log(f"[gpu-test] {name} in-library step offsets")
+    h.run(hid, None, ver, 2048)
+    torch.cuda.synchronize()
+    s_gpu = h.read_workspace(2).cpu().numpy().reshape(wl.batch, 14, -1)
+    assert np.all(np.abs(s_gpu.astype(np.float64) - s_ref) <= bound)
 
 
 def test_full_size_truncated_b8():

@@ -116,6 +116,47 @@ def test_truncated_rollout_rejects_bad_counts():
             oracle.rollout(w, X, s, ver, 0, proposals=P)
 
 
+# ------------------------------------------------- per-step projector offsets
+
+def test_step_offsets_closed_forms_and_alignment():
+    """s row j = fc1_x_w . X[b, j+1] + fc1_b: a zero weight leaves the bias, and
+    a hidden that is one-hot at position k and unit i puts column i of the
+    weight (plus the bias) into row k-1 only."""
+    rng = np.random.default_rng(21)
+    B, H, r = 2, 6, 5
+    W = rng.standard_normal((r, H)).astype(F32)
+    b1 = rng.standard_normal(r).astype(F32)
+    X = rng.standard_normal((B, T, H)).astype(F32)
+    s0 = oracle.step_offsets(X, np.zeros_like(W), b1)
+    assert s0.shape == (B, S, r) and np.array_equal(s0, np.broadcast_to(b1, (B, S, r)))
+    for k in (1, 7, 14):
+        for i in (0, H - 1):
+            Xo = np.zeros((B, T, H), F32)
+            Xo[1, k, i] = 1.0
+            got = oracle.step_offsets(Xo, W, b1)
+            want = np.broadcast_to(b1, (B, S, r)).copy()
+            want[1, k - 1] += W[:, i]
+            assert np.allclose(got, want, atol=1e-6), (k, i)
+    # position 0 (the verified token's hidden) never reaches s
+    Xz = X.copy()
+    Xz[:, 0] = 1e3
+    assert np.array_equal(oracle.step_offsets(Xz, W, b1), oracle.step_offsets(X, W, b1))
+
+
+def test_step_offsets_match_float64_loops():
+    rng = np.random.default_rng(22)
+    B, H, r = 2, 7, 3
+    W = rng.standard_normal((r, H)).astype(F32)
+    b1 = rng.standard_normal(r).astype(F32)
+    X = rng.standard_normal((B, T, H)).astype(F32)
+    got = oracle.step_offsets(X, W, b1)
+    for b in range(B):
+        for j in range(S):
+            for n in range(r):
+                ref = float(b1[n]) + sum(float(W[n, i]) * float(X[b, j + 1, i]) for i in range(H))
+                assert abs(float(got[b, j, n]) - ref) < 1e-5
+
+
 # --------------------------------------------------------- library routines
 
 def test_gru_cell_matches_torch_grucell():
