@@ -111,17 +111,35 @@ __device__ __forceinline__ float load_w(const W_t<BF>* p) {
 // m = 14b + j, which is exactly the row order of step_s, so the epilogue
 // stores straight into [B, 14, r].  A workgroup computes 64 units n x 64 rows
 // m; its four waves own 32 x 32 each (2 x 2 tiles of 16x16x32).  k runs in
-// slices of 64 staged in LDS (two buffers, the next slice's 16-byte loads in
-// flight in registers while the current one is multiplied; rows padded to
-// 144 bytes so the fragment reads of 16 lanes hit distinct banks).  With few
-// tiles (small batches) k is split over up to 16 workgroups, each writing its
-// partial product, and a combine kernel adds the splits in a fixed order and
-// the bias.  fp32 models (small) take a direct kernel.
+// slices of 64 staged in LDS (two buffers, rows padded to 144 bytes so the
+// fragment reads of 16 lanes hit distinct banks), fed from four register
+// stages so each slice's 16-byte loads have three steps to land.  With
+// fewer tiles than CUs (small batches) k is split over workgroups until
+// about one per CU, each writing its partial product, and a combine kernel
+// adds the splits in a fixed order and the bias.  fp32 models (small) take a
+// direct kernel.
 constexpr int kOfsTile = 64;           // units and rows per workgroup
 constexpr int kOfsSlice = 64;          // k per LDS stage
 constexpr int kOfsPitch = 72;          // LDS row pitch in bf16 (144 bytes)
 constexpr int kOfsMinSlices = 4;       // k slices per split at least
 constexpr int kOfsTargetGroups = 256;  // split k until about this many workgroups
+
+// one 64-wide k slice of a wave's 32 x 32 block from LDS buffers lw / lx
+__device__ __forceinline__ void offsets_mma(const bf16_t* lw, const bf16_t* lx, int wn, int wm,
+                                            int fr, int fq, v4f (&acc)[2][2]) {
+#pragma unroll
+  for (int ks = 0; ks < kOfsSlice / 32; ++ks) {
+    const int c = ks * 32 + 8 * fq;
+    const v8s a0 = *reinterpret_cast<const v8s*>(lw + (32 * wn + fr) * kOfsPitch + c);
+    const v8s a1 = *reinterpret_cast<const v8s*>(lw + (32 * wn + 16 + fr) * kOfsPitch + c);
+    const v8s b0 = *reinterpret_cast<const v8s*>(lx + (32 * wm + fr) * kOfsPitch + c);
+    const v8s b1 = *reinterpret_cast<const v8s*>(lx + (32 * wm + 16 + fr) * kOfsPitch + c);
+    acc[0][0] = mfma_bf16(a0, b0, acc[0][0]);
+    acc[0][1] = mfma_bf16(a0, b1, acc[0][1]);
+    acc[1][0] = mfma_bf16(a1, b0, acc[1][0]);
+    acc[1][1] = mfma_bf16(a1, b1, acc[1][1]);
+  }
+}
 
 __global__ __launch_bounds__(256) void offsets_gemm_kernel(const bf16_t* __restrict__ W,
                                                            const bf16_t* __restrict__ X,
@@ -134,63 +152,70 @@ __global__ __launch_bounds__(256) void offsets_gemm_kernel(const bf16_t* __restr
   const int n0 = blockIdx.x * kOfsTile, m0 = blockIdx.y * kOfsTile, split = blockIdx.z;
   const int kbeg = split * kper, nsl = kper / kOfsSlice;
   // loader: thread t moves 16 bytes at column 8 (t % 8) of rows t / 8 and t / 8 + 32
+  // (rows past the end are clamped: loaded and dropped)
   const int lr = tid >> 3, lc = (tid & 7) * 8;
-  const bf16_t* wp[2];
-  const bf16_t* xp[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int n = min(n0 + lr + 32 * i, N - 1);  // rows past the end are loaded and dropped
-    const int m = min(m0 + lr + 32 * i, M - 1);
-    const int b = m / DOMINO_S, j = m - b * DOMINO_S;
-    wp[i] = W + (size_t)n * H + kbeg + lc;
-    xp[i] = X + ((size_t)b * DOMINO_T + j + 1) * H + kbeg + lc;
-  }
-  uint4 rw[2], rx[2];
-  auto fetch = [&](int sl) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      rw[i] = *reinterpret_cast<const uint4*>(wp[i] + (size_t)sl * kOfsSlice);
-      rx[i] = *reinterpret_cast<const uint4*>(xp[i] + (size_t)sl * kOfsSlice);
-    }
-  };
-  auto put = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      *reinterpret_cast<uint4*>(&lw[buf][(lr + 32 * i) * kOfsPitch + lc]) = rw[i];
-      *reinterpret_cast<uint4*>(&lx[buf][(lr + 32 * i) * kOfsPitch + lc]) = rx[i];
-    }
-  };
+  const int na = min(n0 + lr, N - 1), nb = min(n0 + lr + 32, N - 1);
+  const int ma = min(m0 + lr, M - 1), mb = min(m0 + lr + 32, M - 1);
+  const bf16_t* wpa = W + (size_t)na * H + kbeg + lc;
+  const bf16_t* wpb = W + (size_t)nb * H + kbeg + lc;
+  const bf16_t* xpa = X + ((size_t)(ma / DOMINO_S) * DOMINO_T + ma % DOMINO_S + 1) * H + kbeg + lc;
+  const bf16_t* xpb = X + ((size_t)(mb / DOMINO_S) * DOMINO_T + mb % DOMINO_S + 1) * H + kbeg + lc;
+  const int sta = lr * kOfsPitch + lc, stb = (lr + 32) * kOfsPitch + lc;
+  // four register stages (named, so they stay in registers): slice k is
+  // fetched into stage k % 4 three steps before it is put into LDS buffer
+  // k % 2, at the end of the step that multiplies slice k - 1
+  uint4 w0a, w0b, x0a, x0b, w1a, w1b, x1a, x1b, w2a, w2b, x2a, x2b, w3a, w3b, x3a, x3b;
+#define OFS_FETCH(S, SL)                                           \
+  do {                                                             \
+    const size_t o_ = (size_t)min(SL, nsl - 1) * kOfsSlice;        \
+    w##S##a = *reinterpret_cast<const uint4*>(wpa + o_);           \
+    w##S##b = *reinterpret_cast<const uint4*>(wpb + o_);           \
+    x##S##a = *reinterpret_cast<const uint4*>(xpa + o_);           \
+    x##S##b = *reinterpret_cast<const uint4*>(xpb + o_);           \
+  } while (0)
+#define OFS_PUT(BUF, S)                                            \
+  do {                                                             \
+    *reinterpret_cast<uint4*>(&lw[BUF][sta]) = w##S##a;            \
+    *reinterpret_cast<uint4*>(&lw[BUF][stb]) = w##S##b;            \
+    *reinterpret_cast<uint4*>(&lx[BUF][sta]) = x##S##a;            \
+    *reinterpret_cast<uint4*>(&lx[BUF][stb]) = x##S##b;            \
+  } while (0)
+  // step h (stage j = h % 4): fetch slice h + 3, multiply slice h from
+  // buffer h % 2, put slice h + 1 into the other buffer (last read before
+  // the previous barrier).  Slices past the end are clamped to the last one
+  // (loaded, never multiplied).
+#define OFS_STEP(H, FETCH_S, BUF, PUT_S)                            \
+  do {                                                             \
+    OFS_FETCH(FETCH_S, (H) + 3);                                   \
+    __builtin_amdgcn_sched_barrier(0);                             \
+    offsets_mma(lw[BUF], lx[BUF], wn, wm, fr, fq, acc);            \
+    OFS_PUT(BUF ^ 1, PUT_S);                                       \
+    __syncthreads();                                               \
+  } while (0)
   const int wn = wave & 1, wm = wave >> 1, fr = lane & 15, fq = lane >> 4;
   v4f acc[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) acc[i][jj] = v4f{0.f, 0.f, 0.f, 0.f};
-  fetch(0);
-  put(0);
+  OFS_FETCH(0, 0);
+  OFS_FETCH(1, 1);
+  OFS_FETCH(2, 2);
+  OFS_PUT(0, 0);
   __syncthreads();
-  for (int sl = 0; sl < nsl; ++sl) {
-    const int buf = sl & 1;
-    fetch(min(sl + 1, nsl - 1));  // the last iteration reloads its own slice (unused)
-#pragma unroll
-    for (int ks = 0; ks < kOfsSlice / 32; ++ks) {
-      v8s a[2], bx[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        a[i] = *reinterpret_cast<const v8s*>(
-            &lw[buf][(32 * wn + 16 * i + fr) * kOfsPitch + ks * 32 + 8 * fq]);
-        bx[i] = *reinterpret_cast<const v8s*>(
-            &lx[buf][(32 * wm + 16 * i + fr) * kOfsPitch + ks * 32 + 8 * fq]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) acc[i][jj] = mfma_bf16(a[i], bx[jj], acc[i][jj]);
-    }
-    // the other buffer was last read before the previous barrier
-    put(buf ^ 1);
-    __syncthreads();
+  int h = 0;
+  for (; h + 4 <= nsl; h += 4) {
+    OFS_STEP(h, 3, 0, 1);
+    OFS_STEP(h + 1, 0, 1, 2);
+    OFS_STEP(h + 2, 1, 0, 3);
+    OFS_STEP(h + 3, 2, 1, 0);
   }
+  if (h < nsl) OFS_STEP(h, 3, 0, 1);
+  if (h + 1 < nsl) OFS_STEP(h + 1, 0, 1, 2);
+  if (h + 2 < nsl) OFS_STEP(h + 2, 1, 0, 3);
+#undef OFS_STEP
+#undef OFS_FETCH
+#undef OFS_PUT
   // lane: row m = m0 + 32 wm + 16 jj + fr, units n = n0 + 32 wn + 16 i + 4 fq + 0..3
   const bool whole = gridDim.z == 1;
 #pragma unroll
