@@ -502,10 +502,12 @@ __global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restr
   }
 }
 
+// umask (or nullptr): the selected ids also set their request's bit in the
+// member mask of its group (union stream)
 __global__ __launch_bounds__(256) void pool_compact_kernel(
     const uint32_t* __restrict__ keys, const float* __restrict__ base, int V, int B, int K,
     const uint32_t* __restrict__ state, const uint32_t* __restrict__ counts, int nch,
-    int32_t* __restrict__ pool_ids, float* __restrict__ pool_base) {
+    int32_t* __restrict__ pool_ids, float* __restrict__ pool_base, uint32_t* __restrict__ umask) {
   __shared__ int lds[4];
   const int b = blockIdx.y, chunk = blockIdx.x;
   const uint32_t T = state[2 * b];
@@ -549,13 +551,106 @@ __global__ __launch_bounds__(256) void pool_compact_kernel(
       pool_ids[(size_t)b * K + pos] = v;
       for (int t = 1; t < DOMINO_T; ++t)
         pool_base[((size_t)(t - 1) * B + b) * K + pos] = base[((size_t)t * B + b) * V + v];
+      if (umask)
+        atomicOr(&umask[(size_t)(b / kUnionGroup) * V + v], 1u << (b % kUnionGroup));
     }
     ++pos;
   }
 }
 
-void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, bool keys_ready,
-                       hipStream_t st) {
+// ------------------------------------------------------ pool row unions
+// For each group of kUnionGroup requests, the union of their pools in id
+// order: one row per id that some request of the group selected, with the
+// bits of the requests that did.  A row's members take consecutive slots of
+// the group's member arrays (row order, then request order), so the base
+// value of (row, request) sits at the row's first slot plus the number of
+// lower member bits.
+
+// union rows and members per (group, id chunk)
+__global__ __launch_bounds__(256) void union_count_kernel(const uint32_t* __restrict__ umask,
+                                                          int V, uint32_t* __restrict__ ucounts,
+                                                          int nch) {
+  __shared__ int lds[4];
+  const int g = blockIdx.y, v0 = blockIdx.x * kPoolChunk;
+  int rows = 0, mem = 0;
+#pragma unroll
+  for (int j = 0; j < kPoolChunk / 256; ++j) {
+    const int v = v0 + j * 256 + threadIdx.x;
+    const uint32_t m = v < V ? umask[(size_t)g * V + v] : 0u;
+    rows += m != 0u;
+    mem += __popc(m);
+  }
+  rows = block_sum_256(rows, lds);
+  mem = block_sum_256(mem, lds);
+  if (threadIdx.x == 0) {
+    ucounts[((size_t)g * nch + blockIdx.x) * 2] = (uint32_t)rows;
+    ucounts[((size_t)g * nch + blockIdx.x) * 2 + 1] = (uint32_t)mem;
+  }
+}
+
+// union rows in id order: row list, records, id -> row map; clears the masks
+__global__ __launch_bounds__(256) void union_compact_kernel(
+    uint32_t* __restrict__ umask, const bf16_t* __restrict__ b2, int V,
+    const uint32_t* __restrict__ ucounts, int nch, int32_t* __restrict__ uid,
+    uint4* __restrict__ urec, int32_t* __restrict__ uidx, int32_t* __restrict__ un, int umax) {
+  __shared__ int lds[4];
+  const int g = blockIdx.y, chunk = blockIdx.x;
+  int rows_b = 0, mem_b = 0;
+  for (int c = threadIdx.x; c < chunk; c += 256) {
+    rows_b += (int)ucounts[((size_t)g * nch + c) * 2];
+    mem_b += (int)ucounts[((size_t)g * nch + c) * 2 + 1];
+  }
+  rows_b = block_sum_256(rows_b, lds);
+  mem_b = block_sum_256(mem_b, lds);
+  // four consecutive ids per thread keep the scan order equal to id order
+  const int v0 = chunk * kPoolChunk + threadIdx.x * 4;
+  uint32_t m[4];
+  int my_rows = 0, my_mem = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int v = v0 + j;
+    m[j] = v < V ? umask[(size_t)g * V + v] : 0u;
+    my_rows += m[j] != 0u;
+    my_mem += __popc(m[j]);
+  }
+  int tot_rows = 0;
+  int rpos = rows_b + block_excl_scan_256(my_rows, lds, &tot_rows);
+  int mpos = mem_b + block_excl_scan_256(my_mem, lds, nullptr);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (m[j] == 0u) continue;
+    const int v = v0 + j;
+    if (rpos < umax) {  // always: a group's union has at most kUnionGroup * K <= umax rows
+      uid[(size_t)g * umax + rpos] = v;
+      urec[(size_t)g * umax + rpos] =
+          make_uint4((uint32_t)v, __float_as_uint(bf16_to_f32(b2[v])), (uint32_t)mpos, m[j]);
+      uidx[(size_t)g * V + v] = rpos;
+    }
+    umask[(size_t)g * V + v] = 0u;
+    ++rpos;
+    mpos += __popc(m[j]);
+  }
+  if (chunk == nch - 1 && threadIdx.x == 0) un[g] = rows_b + tot_rows;
+}
+
+// base logits of steps 1..14 at every member, in the group's slot order
+__global__ __launch_bounds__(256) void union_members_kernel(
+    const int32_t* __restrict__ pool_ids, const float* __restrict__ pool_base, int B, int K, int V,
+    const int32_t* __restrict__ uidx, const uint4* __restrict__ urec, int umax,
+    float* __restrict__ mb, int mstride) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= B * K) return;
+  const int b = idx / K, j = idx - b * K;
+  const int g = b / kUnionGroup, bl = b % kUnionGroup;
+  const int v = pool_ids[idx];
+  const uint4 rc = urec[(size_t)g * umax + uidx[(size_t)g * V + v]];
+  const uint32_t slot = rc.z + __popc(rc.w & ((1u << bl) - 1u));
+  for (int t = 0; t < DOMINO_S; ++t)
+    mb[((size_t)t * 2 + g) * mstride + slot] = pool_base[((size_t)t * B + b) * K + j];
+}
+
+void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
+                       bool keys_ready, hipStream_t st) {
   const int nch = (s.V + kPoolChunk - 1) / kPoolChunk;
   const dim3 grid(nch, B), blk(256);
   if (keys_ready)
@@ -568,8 +663,17 @@ void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, bool k
   DLAUNCH(pool_hist_kernel<2>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
   DLAUNCH(pool_select_kernel<2>, dim3(B), blk, 0, st, ws.hist, ws.state);
   DLAUNCH(pool_count_kernel, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.counts, nch);
+  const bool uni = pool_union(s, ws, B);
   DLAUNCH(pool_compact_kernel, grid, blk, 0, st, ws.keys, ws.base, s.V, B, K, ws.state,
-                     ws.counts, nch, ws.pool_ids, ws.pool_base);
+          ws.counts, nch, ws.pool_ids, ws.pool_base, uni ? ws.umask : nullptr);
+  if (uni) {
+    const dim3 ug(nch, (B + kUnionGroup - 1) / kUnionGroup);
+    DLAUNCH(union_count_kernel, ug, blk, 0, st, ws.umask, s.V, ws.ucounts, nch);
+    DLAUNCH(union_compact_kernel, ug, blk, 0, st, ws.umask, (const bf16_t*)fc2_b, s.V,
+            ws.ucounts, nch, ws.uid, ws.urec, ws.uidx, ws.un, ws.umax);
+    DLAUNCH(union_members_kernel, dim3((B * K + 255) / 256), blk, 0, st, ws.pool_ids,
+            ws.pool_base, B, K, s.V, ws.uidx, ws.urec, ws.umax, ws.mb, ws.mstride);
+  }
 }
 
 // ---------------------------------------------------------------- GRU cell
@@ -1170,6 +1274,15 @@ __global__ __launch_bounds__(256) void correct_pool_split_kernel(PoolArgs<true> 
 constexpr int kPoolRT = 2;
 constexpr int kPoolSplitMaxBatch = 16;
 
+// Above the small-batch split kernel, bf16 pools are corrected by streaming
+// each request group's union of pool rows once through the persistent
+// kernel (every pool row is read once per group instead of once per request
+// holding it; the group's products come from one pass over the row).
+bool pool_union(const Shape& s, const Workspace& ws, int B) {
+  return s.bf16 && ws.umask != nullptr && B > kPoolSplitMaxBatch && B <= 2 * kUnionGroup &&
+         rowstream_union_supported(s.r);
+}
+
 void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
                          int K, hipStream_t st) {
   const int tiles = (K + 15) / 16;
@@ -1178,6 +1291,18 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
   const dim3 grid((units + 3) / 4);
   const float* pb = ws.pool_base + (size_t)(k - 1) * B * K;
   uint64_t* slot_k = ws.slots + (size_t)k * B;
+  if (pool_union(s, ws, B)) {
+    StreamArgs a{(const uint16_t*)w.fc2, 0, s.r, ws.u_hi, ws.u_lo, B, 0, 0, nullptr,
+                 nullptr, nullptr, slot_k, kReverseOddSteps ? (k & 1) : 0};
+    a.uid = ws.uid;
+    a.urec = ws.urec;
+    a.un = ws.un;
+    a.mb_k = ws.mb + (size_t)(k - 1) * 2 * ws.mstride;
+    a.ustride = ws.umax;
+    a.mstride = ws.mstride;
+    launch_rowstream_union(a, st);
+    return;
+  }
   // small batches are latency bound: spread each request's pool over many workgroups
   if (s.bf16 && B <= kPoolSplitMaxBatch && s.r % 32 == 0 && s.r <= 32 * 4 * 12) {
     PoolArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,

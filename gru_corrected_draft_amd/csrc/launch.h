@@ -53,9 +53,22 @@ struct Workspace {
   uint64_t* slots;     // [15, Bmax] argmax words
   int32_t* bad;        // [Bmax]
   float* partial;      // split-k partial sums of the GRU / fc1 products
-  float* s_tmp;        // [14 * Bmax, r] step-major products of the s computation
+  float* s_tmp;        // k-split partials of the step-offset product
   float* s;            // [Bmax, 14, r] per-step projector offsets formed in the library
+  // pool rows streamed once per group of kUnionGroup requests (bf16, large batches)
+  uint32_t* umask;     // [2, V] member bits of each id per group; zero between runs
+  uint32_t* ucounts;   // [2, nchunks, 2] (union rows, members) per id chunk
+  int32_t* uid;        // [2, Umax] union row ids per group, in id order
+  uint4* urec;         // [2, Umax] {id, b2 as float bits, first member slot, member bits}
+  int32_t* uidx;       // [2, V] union row of an id (valid for the group's members)
+  int32_t* un;         // [2] union sizes
+  float* mb;           // [14, 2, mstride] base logits of the members, union order
+  int umax;            // Umax: rows per group list, min(V, kUnionGroup * Kmax)
+  int mstride;         // member slots per group, kUnionGroup * Kmax
 };
+
+// requests per union group (one 32-bit member mask per union row)
+constexpr int kUnionGroup = 32;
 
 // most workgroups per 16-unit tile along k in the MFMA GRU / fc1 products
 constexpr int kGemvSplit = 4;
@@ -78,11 +91,21 @@ struct StreamArgs {
   int reverse;             // walk k from the end (alternated between steps)
   int groups;              // column groups (set by the launcher)
   int gcols;               // columns per group (set by the launcher)
+  // union epilogue: group g streams the rows uid[g * ustride ..] (un[g] of
+  // them) and folds only member pairs, with base values from mb_k
+  const int32_t* uid;
+  const uint4* urec;
+  const int32_t* un;
+  const float* mb_k;       // [groups, mstride] for this step
+  int ustride, mstride;
 };
 bool rowstream_supported(int K, int ncols);
 void rowstream_prepare();
 void launch_rowstream_store(StreamArgs a, hipStream_t st);
 void launch_rowstream_argmax(StreamArgs a, hipStream_t st);
+// whether the union stream runs for r-wide rows (its 32-request panel fits)
+bool rowstream_union_supported(int K);
+void launch_rowstream_union(StreamArgs a, hipStream_t st);
 
 // one-wave-per-row GRU / fc1 (rows.hip), bf16 weights
 struct GruArgs16 {
@@ -134,13 +157,16 @@ bool rows_supported(int e, int g, int r);
 void launch_gru_rows(const GruArgs16& a, hipStream_t st);
 void launch_fc1_rows(const Fc1Args16& a, hipStream_t st);
 
-void lmhead_prepare();  // once per process: raise the tiled kernel's LDS limit
 void launch_reset(const Workspace& ws, int B, int K, hipStream_t st);
 void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int B, hipStream_t st);
 void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st);
-// keys_ready: the per-id scores were already written by the fused LM-head
-void launch_pool_build(const Shape& s, const Workspace& ws, int B, int K, bool keys_ready,
-                       hipStream_t st);
+// Whether a pool correction of B requests streams each request group's
+// union of pool rows once (instead of gathering every request's rows).
+bool pool_union(const Shape& s, const Workspace& ws, int B);
+// keys_ready: the per-id scores were already written by the fused LM-head;
+// with pool_union(), also the per-group unions and member base values
+void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
+                       bool keys_ready, hipStream_t st);
 // token source: exactly one of tok_i32 (element b*stride) or tok_key (argmax word b)
 void launch_gru(const Shape& s, const DeviceWeights& w, const float* h_in, float* h_out,
                 const int32_t* tok_i32, int tok_stride, const uint64_t* tok_key, int32_t* bad,

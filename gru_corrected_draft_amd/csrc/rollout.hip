@@ -219,6 +219,23 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
                              sizeof(float));
     ws.s = (float*)alloc((size_t)DOMINO_S * Bm * r * sizeof(float));
   }
+  const bool unions = h->shape.bf16 && Bm > 16;  // pool_union() needs more than 16 requests
+  if (unions) {
+    ws.umax = (int)std::min<size_t>(V, (size_t)kUnionGroup * Km);
+    ws.mstride = kUnionGroup * (int)Km;
+    ws.umask = (uint32_t*)alloc(2 * V * 4);
+    ws.ucounts = (uint32_t*)alloc(2 * nch * 2 * 4);
+    ws.uid = (int32_t*)alloc(2 * (size_t)ws.umax * 4);
+    ws.urec = (uint4*)alloc(2 * (size_t)ws.umax * sizeof(uint4));
+    ws.uidx = (int32_t*)alloc(2 * V * 4);
+    ws.un = (int32_t*)alloc(2 * 4);
+    ws.mb = (float*)alloc((size_t)DOMINO_S * 2 * ws.mstride * 4);
+    if (!ws.umask || !ws.ucounts || !ws.uid || !ws.urec || !ws.uidx || !ws.un || !ws.mb) {
+      set_global_err("create: workspace allocation failed");
+      domino_rollout_destroy(h);
+      return DOMINO_ERR_OUT_OF_MEMORY;
+    }
+  }
   for (void* p : {(void*)ws.base, (void*)ws.keys, (void*)ws.hist, (void*)ws.state, (void*)ws.counts,
                   (void*)ws.pool_ids, (void*)ws.pool_base, (void*)ws.h[0], (void*)ws.h[1],
                   (void*)ws.u, (void*)ws.u_hi, (void*)ws.u_lo, (void*)ws.slots, (void*)ws.bad,
@@ -234,7 +251,8 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   for (size_t i = 0; i < h->allocations.size(); ++i) {
     if (hipMemset(h->allocations[i], 0, 256) != hipSuccess) break;
   }
-  if (hipMemset(ws.pool_ids, 0, Bm * Km * 4) != hipSuccess ||
+  if ((unions && hipMemset(ws.umask, 0, 2 * V * 4) != hipSuccess) ||
+      hipMemset(ws.pool_ids, 0, Bm * Km * 4) != hipSuccess ||
       hipMemset(ws.base, 0, DOMINO_T * Bm * V * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     set_global_err("create: workspace initialisation failed");
     domino_rollout_destroy(h);
@@ -242,7 +260,6 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   }
   static std::once_flag once;
   std::call_once(once, [] {
-    lmhead_prepare();
     rowstream_prepare();
     lmhead_fused_prepare();
   });
@@ -371,7 +388,7 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
   }
   if (pool) {
     PhaseTimer t(h, kPool, st);
-    launch_pool_build(sh, ws, B, K, fused, st);
+    launch_pool_build(sh, ws, h->w.fc2_b, B, K, fused, st);
   }
   // two-token prefix: h = GRU(E[verified], 0); h = GRU(E[p1], h).  It runs
   // for every P: the first cell is where an invalid verified token is flagged.

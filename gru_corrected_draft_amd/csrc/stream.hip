@@ -21,7 +21,7 @@
 
 namespace {
 
-enum { kEpiStore = 0, kEpiArgmax = 1 };
+enum { kEpiStore = 0, kEpiArgmax = 1, kEpiUnion = 2 };
 
 constexpr int kSC = 128;  // k per super-chunk (4 MFMA k-slices of 32)
 constexpr bool kStraightWalk = true;
@@ -232,16 +232,22 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
 // unit are consecutive on one XCD and read the unit through its L2.
 // Epilogues: store the unit's logits (LM-head), or fold y = base + (W.u + b2)
 // into one packed argmax key per request held in registers, published once
-// per block at the end (correction).
-template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI>
-__global__ __launch_bounds__(256) void rowpersist_kernel(StreamArgs a) {
+// per block at the end (correction).  The union epilogue streams, for each
+// group of requests, only the union of their pools (rows taken through the
+// group's id list) and folds a (row, request) pair only when the row is in
+// that request's pool, with the base value from the members' compact array.  WV waves per block share the panel (8
+// when the panel allows one block per CU, so two waves per SIMD overlap
+// their products with their loads).
+template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI, int WV>
+__global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
   extern __shared__ __align__(16) bf16_t sact[];
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
-  const int N = a.N, K = a.K, G = a.groups;
+  const int K = a.K, G = a.groups;
   const int ldsrow = K + 8;
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int grp = local % G;
+  const int N = EPI == kEpiUnion ? a.un[grp] : a.N;  // >= 1
   const int parts = gridDim.x / G;  // the grid is a multiple of 8 * G
   const int part = (local / G) * 8 + xcd;
   const int c0 = grp * a.gcols;
@@ -249,7 +255,7 @@ __global__ __launch_bounds__(256) void rowpersist_kernel(StreamArgs a) {
 
   {  // the group's panel: hi plane rows [0, ncl), lo plane rows [ncl, 2 ncl)
     const int per_row = K / 8;
-    for (int idx = threadIdx.x; idx < ncl * per_row; idx += 256) {
+    for (int idx = threadIdx.x; idx < ncl * per_row; idx += WV * 64) {
       const int c = idx / per_row, p = idx - c * per_row;
       const int m = c0 + c;
       const int arow = a.col_B ? (m % a.col_B) * DOMINO_T + m / a.col_B : m;
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(256) void rowpersist_kernel(StreamArgs a) {
 
   // this wave's row units: w, w + stride, ... (walked backwards when reversed)
   const int units = ((N + 15) / 16 + RT - 1) / RT;
-  const int w = part * 4 + wave, stride = parts * 4;
+  const int w = part * WV + wave, stride = parts * WV;
   const int my_n = units > w ? (units - w + stride - 1) / stride : 0;
   const bool rev = a.reverse != 0;
   const int nsc = K / kSC;
@@ -276,22 +282,32 @@ __global__ __launch_bounds__(256) void rowpersist_kernel(StreamArgs a) {
   // consumer.  Past this wave's last unit (or for a wave without units) the
   // rows are clamped into [0, N), so every load stays inside W; such loads
   // are never consumed.  D divides nsc, so super-chunk ci of any unit sits
-  // in ring slot ci % D.
+  // in ring slot ci % D.  prow: the lane's weight row in each tile of the
+  // cursor's unit (union: looked up in the group's row list).
+  const int32_t* uid_g = EPI == kEpiUnion ? a.uid + (size_t)grp * a.ustride : nullptr;
   int pj = 0, pci = 0;
+  int prow0 = 0, prow1 = 0;
+  static_assert(RT <= 2, "row cursor holds two tiles");
+  auto set_rows = [&](int u) {
+    const int r0 = min(max((u * RT) * 16 + row, 0), N - 1);
+    const int r1 = min(max((u * RT + 1) * 16 + row, 0), N - 1);
+    prow0 = EPI == kEpiUnion ? uid_g[r0] : r0;
+    prow1 = EPI == kEpiUnion && RT > 1 ? uid_g[r1] : r1;
+  };
+  set_rows(unit_of(0));
   v8s A[D][RT][4];
   auto load_next = [&](v8s (&dst)[RT][4]) {
-    const int u = unit_of(pj);
     const int k = kchunk(pci) * kSC + q * 8;
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-      const int r = min(max((u * RT + t) * 16 + row, 0), N - 1);
-      const bf16_t* p = a.W + (size_t)r * K + k;
+      const bf16_t* p = a.W + (size_t)(t == 0 ? prow0 : prow1) * K + k;
 #pragma unroll
       for (int c = 0; c < 4; ++c) dst[t][c] = load_frag_bf16(p + c * 32);
     }
     if (++pci == nsc) {
       pci = 0;
       ++pj;
+      set_rows(unit_of(pj));
     }
   };
 
@@ -316,7 +332,28 @@ __global__ __launch_bounds__(256) void rowpersist_kernel(StreamArgs a) {
     // lane come in one load (rows past N are clamped and masked at the fold)
     uint32_t rbias[RT][4];
     float ebase[NB][RT][4];
-    if (EPI == kEpiArgmax && VEC) {
+    uint4 urc[RT][4];  // union: {id, b2 bits, first member slot, member bits} of the lane's rows
+    if (EPI == kEpiUnion) {
+      const uint4* rec_g = a.urec + (size_t)grp * a.ustride;
+      const float* mb_g = a.mb_k + (size_t)grp * a.mstride;
+#pragma unroll
+      for (int t = 0; t < RT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) urc[t][i] = rec_g[min((u * RT + t) * 16 + 4 * q + i, N - 1)];
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) {
+        const int bl = cb * 16 + row;  // < 32
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint32_t m = urc[t][i].w;
+            const bool mem = (m >> bl) & 1u;
+            const uint32_t slot = urc[t][i].z + __popc(m & ((1u << bl) - 1u));
+            ebase[cb][t][i] = mb_g[mem ? slot : 0u];  // non-members read one shared word
+          }
+      }
+    } else if (EPI == kEpiArgmax && VEC) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int v = min((u * RT + t) * 16 + 4 * q, N - 4);
@@ -403,6 +440,18 @@ __global__ __launch_bounds__(256) void rowpersist_kernel(StreamArgs a) {
             const uint64_t key = pack_key(y, (uint32_t)c);
             best[cb] = (b < ncl && c < N) ? umax64(best[cb], key) : best[cb];
           }
+      } else if (EPI == kEpiUnion) {
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int c = (u * RT + t) * 16 + 4 * q + i;
+            const uint4 rc = urc[t][i];
+            const bool mem = c < N && ((rc.w >> b) & 1u);
+            const float y = ebase[cb][t][i] + (acc[t][cb][i] + __uint_as_float(rc.y));
+            const uint64_t key = pack_key(y, rc.x);
+            best[cb] = mem ? umax64(best[cb], key) : best[cb];
+          }
       } else if (b < ncl) {
         float* orow = a.out + (size_t)(c0 + b) * N;
 #pragma unroll
@@ -423,14 +472,14 @@ __global__ __launch_bounds__(256) void rowpersist_kernel(StreamArgs a) {
       for (int t = 0; t < RT; ++t) acc[t][cb] = zero4();
     }
   }
-  if (EPI != kEpiArgmax) return;  // no barrier follows
+  if (EPI == kEpiStore) return;  // no barrier follows
 
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 16));
     best[cb] = umax64(best[cb], shfl_xor_u64(best[cb], 32));
   }
-  __shared__ uint64_t wb[4][NB][16];
+  __shared__ uint64_t wb[WV][NB][16];
   if (q == 0)
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) wb[wave][cb][row] = best[cb];
@@ -438,13 +487,14 @@ __global__ __launch_bounds__(256) void rowpersist_kernel(StreamArgs a) {
   if (threadIdx.x < NB * 16) {
     const int cb = threadIdx.x >> 4, n = threadIdx.x & 15;
     const int b = cb * 16 + n;
-    if (b < ncl)
-      publish_max(&a.slot_k[c0 + b], umax64(umax64(wb[0][cb][n], wb[1][cb][n]),
-                                            umax64(wb[2][cb][n], wb[3][cb][n])));
+    uint64_t m = wb[0][cb][n];
+#pragma unroll
+    for (int v = 1; v < WV; ++v) m = umax64(m, wb[v][cb][n]);
+    if (b < ncl) publish_max(&a.slot_k[c0 + b], m);
   }
 }
 
-template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI>
+template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI, int WV>
 void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
   static int per_cu = -1, cus = 0;  // resident blocks per CU at this panel size
   static size_t per_cu_lds = 0;
@@ -454,7 +504,7 @@ void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI>, 256, lds) != hipSuccess)
+            &n, rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI, WV>, WV * 64, lds) != hipSuccess)
       n = 1;
     per_cu = n < 1 ? 1 : n;
   }
@@ -462,8 +512,8 @@ void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
   const int unit = 8 * a.groups;
   const int want = (cus > 0 ? cus : 256) * per_cu;
   const int grid = ((want + unit - 1) / unit) * unit;
-  DLAUNCH((rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI>), dim3(grid), dim3(256), lds,
-                     st, a);
+  DLAUNCH((rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI, WV>), dim3(grid), dim3(WV * 64), lds,
+          st, a);
 }
 
 // panel bytes of one group of `cols` columns over all of K
@@ -472,7 +522,7 @@ size_t persist_lds(int K, int cols, bool split) {
 }
 
 // gcols: activation columns per group (at most NB * 16)
-template <int NB, int RT, int D, bool SPLIT, int EPI>
+template <int NB, int RT, int D, bool SPLIT, int EPI, int WV>
 void launch_persist(StreamArgs a, int gcols, hipStream_t st) {
   a.gcols = gcols;
   a.groups = (a.ncols + gcols - 1) / gcols;
@@ -483,9 +533,9 @@ void launch_persist(StreamArgs a, int gcols, hipStream_t st) {
                             (reinterpret_cast<uintptr_t>(a.base_k) & 15) == 0)
                          : (reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
   if (vec)
-    launch_persist_t<NB, RT, D, true, SPLIT, EPI>(a, lds, st);
+    launch_persist_t<NB, RT, D, true, SPLIT, EPI, WV>(a, lds, st);
   else
-    launch_persist_t<NB, RT, D, false, SPLIT, EPI>(a, lds, st);
+    launch_persist_t<NB, RT, D, false, SPLIT, EPI, WV>(a, lds, st);
 }
 
 template <int NB, int RT, bool SPLIT, int EPI, int D>
@@ -542,23 +592,39 @@ void dispatch_store(StreamArgs a, hipStream_t st) {
 // persistent stream; panels that do not fit run the sliced kernel.
 constexpr int kArgmaxRT = 2;
 constexpr int kArgmaxD = 2;
+constexpr int kArgmaxWV1 = 4;  // waves per block, groups of up to 16 requests
+constexpr int kArgmaxWV2 = 8;  // waves per block, 32-request groups (one block per CU)
 void dispatch_argmax(StreamArgs a, hipStream_t st) {
   if (a.ncols <= 16 && persist_fits<kArgmaxD>(a.K, a.ncols, true)) {
-    launch_persist<1, kArgmaxRT, kArgmaxD, true, kEpiArgmax>(a, a.ncols, st);
+    launch_persist<1, kArgmaxRT, kArgmaxD, true, kEpiArgmax, kArgmaxWV1>(a, a.ncols, st);
   } else if (a.ncols <= 16) {
     a.KS = pick_slice(a.K, a.ncols, 2, 32 * 1024);
     launch_t<1, 2, true, kEpiArgmax, 2>(a, st);
   } else if (persist_fits<kArgmaxD>(a.K, 32, true)) {
-    launch_persist<2, kArgmaxRT, kArgmaxD, true, kEpiArgmax>(a, 32, st);
+    launch_persist<2, kArgmaxRT, kArgmaxD, true, kEpiArgmax, kArgmaxWV2>(a, 32, st);
   } else {
     a.KS = pick_slice(a.K, min(a.ncols, 64), 2, 32 * 1024);
     launch_t<4, 2, true, kEpiArgmax, 2>(a, st);
   }
 }
 
+// Union stream: groups of 32 requests, each over its own row list.
+void dispatch_union(StreamArgs a, hipStream_t st) {
+  a.gcols = kUnionGroup;
+  a.groups = (a.ncols + kUnionGroup - 1) / kUnionGroup;
+  const size_t lds = persist_lds(a.K, min(a.ncols, kUnionGroup), true);
+  launch_persist_t<2, kArgmaxRT, kArgmaxD, false, true, kEpiUnion, kArgmaxWV2>(a, lds, st);
+}
+
 }  // namespace
 
 bool rowstream_supported(int K, int ncols) { return K % kSC == 0 && ncols >= 1 && ncols <= 128; }
+
+bool rowstream_union_supported(int K) {
+  return K % kSC == 0 && persist_fits<kArgmaxD>(K, kUnionGroup, true);
+}
+
+void launch_rowstream_union(StreamArgs a, hipStream_t st) { dispatch_union(a, st); }
 
 void launch_rowstream_store(StreamArgs a, hipStream_t st) { dispatch_store(a, st); }
 
@@ -576,12 +642,13 @@ void rowstream_prepare() {
   SET(7, 1, false, kEpiStore, 2); SET(8, 1, false, kEpiStore, 2);
   SET(1, 2, true, kEpiArgmax, 2); SET(4, 2, true, kEpiArgmax, 2);
 #undef SET
-#define SETP(NB, RT, D, VEC, SP, EP)                                                             \
-  (void)hipFuncSetAttribute((const void*)rowpersist_kernel<NB, RT, D, VEC, SP, EP>,              \
+#define SETP(NB, RT, D, VEC, SP, EP, WV)                                                         \
+  (void)hipFuncSetAttribute((const void*)rowpersist_kernel<NB, RT, D, VEC, SP, EP, WV>,          \
                             hipFuncAttributeMaxDynamicSharedMemorySize, kPersistBudget)
-  SETP(1, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax);
-  SETP(1, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax);
-  SETP(2, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax);
-  SETP(2, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax);
+  SETP(1, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax, kArgmaxWV1);
+  SETP(1, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax, kArgmaxWV1);
+  SETP(2, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax, kArgmaxWV2);
+  SETP(2, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax, kArgmaxWV2);
+  SETP(2, kArgmaxRT, kArgmaxD, false, true, kEpiUnion, kArgmaxWV2);
 #undef SETP
 }

@@ -259,6 +259,49 @@ def test_run_rejects_bad_scalars_without_launching():
     assert torch.all(out == 5)
 
 
+# ------------------------------------------------------------- pool unions
+
+@pytest.mark.parametrize("B,K", [(17, 1), (32, 100), (33, 100), (64, 2048)])
+def test_pool_union_stream(B, K):
+    """Above 16 requests a pool correction streams, for each group of 32
+    requests, the union of their pools once: group edges (one request alone
+    in the second group at B = 33), one-id pools, and pools covering most of
+    the vocabulary (2048 of 5003 ids)."""
+    G.log(f"[gpu-test] pool union B={B} K={K}")
+    tok, top, h = G.gpu_run(SMALL, B, 600 + B, 0, K, max_batch=64, max_k=2048, scales_key=STRONG)
+    ref = G.oracle_run(SMALL, B, 600 + B, 0, K, scales_key=STRONG)
+    c, _ = compare(tok, top, ref, TOL["bf16"])
+    compare(tok, top, ref, TOL["bf16"], margin_min=TIGHT_MARGIN)
+    assert c > 0
+    ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
+    for b in range(B):
+        assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
+    # the masks clear themselves: a second run repeats the first bit for bit
+    tok2, top2, _ = G.gpu_run(SMALL, B, 600 + B, 0, K, max_batch=64, max_k=2048,
+                              scales_key=STRONG)
+    assert np.array_equal(tok, tok2) and np.array_equal(top.view(np.uint32), top2.view(np.uint32))
+
+
+def test_pool_union_shared_pools():
+    """64 copies of one request share one pool, so every union row holds all
+    32 members of its group (member slots up to rank 31): every request gives
+    the oracle's proposals for that request, bit-identical across copies."""
+    import torch
+    B, K = 64, 300
+    one = synth.make_inputs(SMALL, 1, 611, 0)
+    inp = synth.Inputs(np.repeat(one.hidden, B, axis=0), np.repeat(one.step_s, B, axis=0),
+                       np.repeat(one.verified, B, axis=0))
+    h = G.handle(SMALL, 64, 2048, STRONG)
+    hid, s, ver = R.device_inputs(inp)
+    G.log(f"[gpu-test] pool union, shared pools B={B} K={K}")
+    tok, top = h.run(hid, s, ver, K)
+    torch.cuda.synchronize()
+    tok, top = tok.cpu().numpy(), top.cpu().numpy()
+    ref = G.oracle_run(SMALL, 1, 611, 0, K, scales_key=STRONG)
+    compare(tok[:1], top[:1], ref, TOL["bf16"])
+    assert np.all(tok == tok[:1]) and np.all(top.view(np.uint32) == top[:1].view(np.uint32))
+
+
 # ------------------------------------------------ step offsets in the library
 
 def _offsets_ref(model_key, B, seed, scales_key=()):
