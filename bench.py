@@ -40,13 +40,19 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic(shape, B, K):
+def algorithmic(shape, B, K, union_sizes=None):
     """Algorithmic bytes / flops per launch of each kernel class (the unit
-    figures of the design notes times the units one launch processes)."""
+    figures of the design notes times the units one launch processes).
+    union_sizes: rows of each request group's pool union when the pool
+    correction streams the unions."""
     V, H, e, g, r = shape.vocab, shape.hidden, shape.emb_dim, shape.gru_hidden, shape.proj_dim
     wb = 2 if shape.dtype == "bf16" else 4
     pool = 0 < K < V
-    if pool:
+    if pool and union_sizes is not None:
+        # each group's union rows (fc2 row + 16-byte record), the members'
+        # base values, u as hi/lo planes
+        correct_bytes = sum(int(n) for n in union_sizes) * (r * wb + 16) + B * K * 4 + B * r * 4
+    elif pool:
         # gathered fc2 rows + their biases, compact base values, pool ids, u
         correct_bytes = B * K * (r * wb + wb + 4 + 4) + B * r * 4
     else:
@@ -129,6 +135,9 @@ def main():
     ap.add_argument("--in-library-s", action="store_true",
                     help="form the per-step projector offsets in the library from the hiddens "
                          "(run without step_s)")
+    ap.add_argument("--pool-strategy", type=int, default=0, choices=(0, 1, 2),
+                    help="pool correction at 17-64 requests: 0 automatic, 1 per-request "
+                         "gather, 2 group unions")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -169,6 +178,7 @@ def main():
     hid, s, ver = R.device_inputs(inp)
     log(f"[bench] {args.workload} B={B} K={K}: inputs ready in {time.time() - t0:.1f}s")
     h = R.DominoRollout(dev, max_batch=B, max_k=max(K, 1))
+    h.set_pool_strategy(args.pool_strategy)
     P = args.proposals
     prop = None if P == 15 else P
     if args.in_library_s:
@@ -209,7 +219,13 @@ def main():
     avg = {k: (ms / n if n else None) for k, (ms, n) in kt.items()}
     log("[bench] per-launch ms: " + ", ".join(f"{k}={v:.4f}" for k, v in avg.items() if v))
 
-    alg = algorithmic(shape, B, K)
+    union_sizes = None
+    if 0 < K < shape.vocab:
+        try:
+            union_sizes = h.read_workspace(3).cpu().tolist()
+        except R.DominoError:
+            union_sizes = None
+    alg = algorithmic(shape, B, K, union_sizes)
     digest = kernel_source_digest()
     corr_ms = avg["correct"]
     lm_ms = avg["lmhead"]
@@ -230,7 +246,8 @@ def main():
         dominant_ms = lm_ms
     else:
         achieved = alg["correct_bytes"] / (corr_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "correct_" + ("pool" if 0 < K < shape.vocab else "full"),
+        kind = ("union" if union_sizes is not None else "pool") if 0 < K < shape.vocab else "full"
+        roof = {"bound": "hbm", "kernel": "correct_" + kind,
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": read_traffic("correct", f"{args.workload}_k{K}", digest)}
@@ -258,6 +275,7 @@ def main():
                    "emb_dim": shape.emb_dim, "gru_hidden": shape.gru_hidden,
                    "proj_dim": shape.proj_dim, "block_size": 16, "proposals": P,
                    "step_offsets": "in library" if args.in_library_s else "input",
+                   "pool_strategy": ("auto", "gather", "unions")[args.pool_strategy],
                    "accumulate": "fp32",
                    "mode": "hip graph replay"},
         "roofline": roof,
@@ -271,6 +289,8 @@ def main():
                                             args.in_library_s)
     else:
         line["cpu_baseline"] = None
+    if union_sizes is not None:
+        line["pool_union_rows"] = union_sizes
     h.close()
     print(json.dumps(line), flush=True)
 

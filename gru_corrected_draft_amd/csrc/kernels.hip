@@ -588,11 +588,10 @@ __global__ __launch_bounds__(256) void union_count_kernel(const uint32_t* __rest
   }
 }
 
-// union rows in id order: row list, records, id -> row map; clears the masks
+// union rows in id order: records and the id -> row map; clears the masks
 __global__ __launch_bounds__(256) void union_compact_kernel(
     uint32_t* __restrict__ umask, const bf16_t* __restrict__ b2, int V,
-    const uint32_t* __restrict__ ucounts, int nch, int32_t* __restrict__ uid,
-    uint4* __restrict__ urec, int32_t* __restrict__ uidx, int32_t* __restrict__ un, int umax) {
+    const uint32_t* __restrict__ ucounts, int nch, uint4* __restrict__ urec, int32_t* __restrict__ uidx, int32_t* __restrict__ un, int umax) {
   __shared__ int lds[4];
   const int g = blockIdx.y, chunk = blockIdx.x;
   int rows_b = 0, mem_b = 0;
@@ -621,7 +620,6 @@ __global__ __launch_bounds__(256) void union_compact_kernel(
     if (m[j] == 0u) continue;
     const int v = v0 + j;
     if (rpos < umax) {  // always: a group's union has at most kUnionGroup * K <= umax rows
-      uid[(size_t)g * umax + rpos] = v;
       urec[(size_t)g * umax + rpos] =
           make_uint4((uint32_t)v, __float_as_uint(bf16_to_f32(b2[v])), (uint32_t)mpos, m[j]);
       uidx[(size_t)g * V + v] = rpos;
@@ -663,14 +661,14 @@ void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, i
   DLAUNCH(pool_hist_kernel<2>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
   DLAUNCH(pool_select_kernel<2>, dim3(B), blk, 0, st, ws.hist, ws.state);
   DLAUNCH(pool_count_kernel, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.counts, nch);
-  const bool uni = pool_union(s, ws, B);
+  const bool uni = pool_union(s, ws, B, K);
   DLAUNCH(pool_compact_kernel, grid, blk, 0, st, ws.keys, ws.base, s.V, B, K, ws.state,
           ws.counts, nch, ws.pool_ids, ws.pool_base, uni ? ws.umask : nullptr);
   if (uni) {
     const dim3 ug(nch, (B + kUnionGroup - 1) / kUnionGroup);
     DLAUNCH(union_count_kernel, ug, blk, 0, st, ws.umask, s.V, ws.ucounts, nch);
     DLAUNCH(union_compact_kernel, ug, blk, 0, st, ws.umask, (const bf16_t*)fc2_b, s.V,
-            ws.ucounts, nch, ws.uid, ws.urec, ws.uidx, ws.un, ws.umax);
+            ws.ucounts, nch, ws.urec, ws.uidx, ws.un, ws.umax);
     DLAUNCH(union_members_kernel, dim3((B * K + 255) / 256), blk, 0, st, ws.pool_ids,
             ws.pool_base, B, K, s.V, ws.uidx, ws.urec, ws.umax, ws.mb, ws.mstride);
   }
@@ -1274,13 +1272,25 @@ __global__ __launch_bounds__(256) void correct_pool_split_kernel(PoolArgs<true> 
 constexpr int kPoolRT = 2;
 constexpr int kPoolSplitMaxBatch = 16;
 
-// Above the small-batch split kernel, bf16 pools are corrected by streaming
-// each request group's union of pool rows once through the persistent
-// kernel (every pool row is read once per group instead of once per request
-// holding it; the group's products come from one pass over the row).
-bool pool_union(const Shape& s, const Workspace& ws, int B) {
-  return s.bf16 && ws.umask != nullptr && B > kPoolSplitMaxBatch && B <= 2 * kUnionGroup &&
-         rowstream_union_supported(s.r);
+// Above the small-batch split kernel, bf16 pools can be corrected by
+// streaming each request group's union of pool rows once through the
+// persistent kernel (every pool row is read once per group instead of once
+// per request holding it; the group's products come from one pass over the
+// row).  Building the unions costs ~20 us per block, so the automatic choice
+// takes them once the per-request gather would read kUnionMinGatherBytes per
+// step (measured at 8B shapes, B = 64: the gather wins at K <= 512, the
+// unions from K = 1024 on).
+constexpr long long kUnionMinGatherBytes = 96ll << 20;
+static int union_bound(const Shape& s, int K) {
+  return (int)std::min<long long>(s.V, (long long)kUnionGroup * K);
+}
+
+bool pool_union(const Shape& s, const Workspace& ws, int B, int K) {
+  if (!(s.bf16 && ws.umask != nullptr && B > kPoolSplitMaxBatch && B <= 2 * kUnionGroup &&
+        rowstream_union_supported(s.r, B, union_bound(s, K))) ||
+      ws.pool_strategy == 1)
+    return false;
+  return ws.pool_strategy == 2 || (long long)B * K * s.r * 2 >= kUnionMinGatherBytes;
 }
 
 void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
@@ -1291,16 +1301,15 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
   const dim3 grid((units + 3) / 4);
   const float* pb = ws.pool_base + (size_t)(k - 1) * B * K;
   uint64_t* slot_k = ws.slots + (size_t)k * B;
-  if (pool_union(s, ws, B)) {
+  if (pool_union(s, ws, B, K)) {
     StreamArgs a{(const uint16_t*)w.fc2, 0, s.r, ws.u_hi, ws.u_lo, B, 0, 0, nullptr,
                  nullptr, nullptr, slot_k, kReverseOddSteps ? (k & 1) : 0};
-    a.uid = ws.uid;
     a.urec = ws.urec;
     a.un = ws.un;
     a.mb_k = ws.mb + (size_t)(k - 1) * 2 * ws.mstride;
     a.ustride = ws.umax;
     a.mstride = ws.mstride;
-    launch_rowstream_union(a, st);
+    launch_rowstream_union(a, union_bound(s, K), st);
     return;
   }
   // small batches are latency bound: spread each request's pool over many workgroups

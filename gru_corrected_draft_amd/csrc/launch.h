@@ -58,13 +58,14 @@ struct Workspace {
   // pool rows streamed once per group of kUnionGroup requests (bf16, large batches)
   uint32_t* umask;     // [2, V] member bits of each id per group; zero between runs
   uint32_t* ucounts;   // [2, nchunks, 2] (union rows, members) per id chunk
-  int32_t* uid;        // [2, Umax] union row ids per group, in id order
-  uint4* urec;         // [2, Umax] {id, b2 as float bits, first member slot, member bits}
+  uint4* urec;         // [2, Umax] union rows in id order: {id, b2 as float bits,
+                       // first member slot, member bits}
   int32_t* uidx;       // [2, V] union row of an id (valid for the group's members)
   int32_t* un;         // [2] union sizes
   float* mb;           // [14, 2, mstride] base logits of the members, union order
   int umax;            // Umax: rows per group list, min(V, kUnionGroup * Kmax)
   int mstride;         // member slots per group, kUnionGroup * Kmax
+  int pool_strategy;   // 0 automatic, 1 per-request gather, 2 group unions where supported
 };
 
 // requests per union group (one 32-bit member mask per union row)
@@ -91,21 +92,22 @@ struct StreamArgs {
   int reverse;             // walk k from the end (alternated between steps)
   int groups;              // column groups (set by the launcher)
   int gcols;               // columns per group (set by the launcher)
-  // union epilogue: group g streams the rows uid[g * ustride ..] (un[g] of
-  // them) and folds only member pairs, with base values from mb_k
-  const int32_t* uid;
+  // union epilogue: group g streams the rows of urec[g * ustride ..] (un[g]
+  // of them) and folds only member pairs, with base values from mb_k
   const uint4* urec;
   const int32_t* un;
   const float* mb_k;       // [groups, mstride] for this step
   int ustride, mstride;
+  int umaxu;               // units per wave staged in LDS (set by the launcher)
 };
 bool rowstream_supported(int K, int ncols);
 void rowstream_prepare();
 void launch_rowstream_store(StreamArgs a, hipStream_t st);
 void launch_rowstream_argmax(StreamArgs a, hipStream_t st);
-// whether the union stream runs for r-wide rows (its 32-request panel fits)
-bool rowstream_union_supported(int K);
-void launch_rowstream_union(StreamArgs a, hipStream_t st);
+// whether the union stream runs for K-wide rows, ncols requests and row
+// lists of at most ubound rows (its 32-request panel and staged records fit)
+bool rowstream_union_supported(int K, int ncols, int ubound);
+void launch_rowstream_union(StreamArgs a, int ubound, hipStream_t st);
 
 // one-wave-per-row GRU / fc1 (rows.hip), bf16 weights
 struct GruArgs16 {
@@ -162,7 +164,7 @@ void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int
 void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st);
 // Whether a pool correction of B requests streams each request group's
 // union of pool rows once (instead of gathering every request's rows).
-bool pool_union(const Shape& s, const Workspace& ws, int B);
+bool pool_union(const Shape& s, const Workspace& ws, int B, int K);
 // keys_ready: the per-id scores were already written by the fused LM-head;
 // with pool_union(), also the per-group unions and member base values
 void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,

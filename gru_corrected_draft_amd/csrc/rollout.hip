@@ -60,6 +60,7 @@ struct domino_rollout {
   hipStream_t capture_stream = nullptr;
   int last_B = 0, last_K = 0;  // shape of the last enqueued run
   bool last_s_internal = false;  // the last run formed step_s itself
+  bool last_union = false;       // the last run streamed the pool rows as group unions
   // measurement: kernel event pairs of the timed phases (see PhaseTimer)
   bool timing = false;
   bool capturing = false;
@@ -225,12 +226,11 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
     ws.mstride = kUnionGroup * (int)Km;
     ws.umask = (uint32_t*)alloc(2 * V * 4);
     ws.ucounts = (uint32_t*)alloc(2 * nch * 2 * 4);
-    ws.uid = (int32_t*)alloc(2 * (size_t)ws.umax * 4);
     ws.urec = (uint4*)alloc(2 * (size_t)ws.umax * sizeof(uint4));
     ws.uidx = (int32_t*)alloc(2 * V * 4);
     ws.un = (int32_t*)alloc(2 * 4);
     ws.mb = (float*)alloc((size_t)DOMINO_S * 2 * ws.mstride * 4);
-    if (!ws.umask || !ws.ucounts || !ws.uid || !ws.urec || !ws.uidx || !ws.un || !ws.mb) {
+    if (!ws.umask || !ws.ucounts || !ws.urec || !ws.uidx || !ws.un || !ws.mb) {
       set_global_err("create: workspace allocation failed");
       domino_rollout_destroy(h);
       return DOMINO_ERR_OUT_OF_MEMORY;
@@ -363,6 +363,7 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
   const bool pool = K > 0 && K < sh.V;
   h->last_B = B;
   h->last_K = pool ? K : 0;
+  h->last_union = pool && pool_union(sh, ws, B, K);
   launch_reset(ws, B, pool ? K : 0, st);
   h->last_s_internal = s == nullptr;
   if (!s) {
@@ -560,6 +561,9 @@ extern "C" domino_status_t domino_rollout_read_workspace(const domino_rollout_t*
   } else if (which == 2 && h->last_s_internal) {
     src = h->ws.s;
     n = (size_t)h->last_B * DOMINO_S * h->cfg.proj_dim * 4;
+  } else if (which == 3 && h->last_union) {
+    src = h->ws.un;
+    n = (size_t)((h->last_B + kUnionGroup - 1) / kUnionGroup) * 4;
   } else {
     return DOMINO_ERR_INVALID_ARG;
   }
@@ -569,6 +573,22 @@ extern "C" domino_status_t domino_rollout_read_workspace(const domino_rollout_t*
   DeviceGuard dg(h->device);
   if (hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, (hipStream_t)stream) != hipSuccess)
     return DOMINO_ERR_HIP;
+  return DOMINO_OK;
+}
+
+extern "C" domino_status_t domino_rollout_set_pool_strategy(domino_rollout_t* h,
+                                                            int32_t strategy) {
+  if (!h) return DOMINO_ERR_INVALID_ARG;
+  if (strategy < 0 || strategy > 2)
+    return h->fail(DOMINO_ERR_INVALID_ARG, "set_pool_strategy: strategy must be 0, 1 or 2");
+  if (strategy != h->ws.pool_strategy) {
+    DeviceGuard dg(h->device);
+    if (hipDeviceSynchronize() != hipSuccess)
+      return h->fail(DOMINO_ERR_HIP, "set_pool_strategy: synchronize failed");
+    for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);  // captured the old strategy
+    h->graphs.clear();
+    h->ws.pool_strategy = strategy;
+  }
   return DOMINO_OK;
 }
 

@@ -22,6 +22,7 @@
 namespace {
 
 enum { kEpiStore = 0, kEpiArgmax = 1, kEpiUnion = 2 };
+constexpr int kUnionUnitRows = 32;  // rows per unit of the union stream (two 16-row tiles)
 
 constexpr int kSC = 128;  // k per super-chunk (4 MFMA k-slices of 32)
 constexpr bool kStraightWalk = true;
@@ -253,6 +254,30 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
   const int c0 = grp * a.gcols;
   const int ncl = min(a.gcols, a.ncols - c0);  // 1 .. NB * 16
 
+  // this wave's row units: w, w + stride, ... (walked backwards when reversed)
+  const int units = ((N + 15) / 16 + RT - 1) / RT;
+  const int w = part * WV + wave, stride = parts * WV;
+  int my_n = units > w ? (units - w + stride - 1) / stride : 0;
+  if (EPI == kEpiUnion) my_n = min(my_n, a.umaxu);  // the launch sizes umaxu to cover my_n
+  const bool rev = a.reverse != 0;
+  const int nsc = K / kSC;
+  auto unit_of = [&](int j) { return w + (rev ? my_n - 1 - j : j) * stride; };
+  auto kchunk = [&](int ci) { return rev ? nsc - 1 - ci : ci; };
+
+  // union: the records of this wave's rows, staged in LDS behind the panel
+  // (kUnionUnitRows per unit) so that row ids and epilogue operands are LDS
+  // reads, which never wait on the weight stream's loads
+  static_assert(EPI != kEpiUnion || RT * 16 == kUnionUnitRows, "union unit rows");
+  uint4* srec = nullptr;
+  if (EPI == kEpiUnion) {
+    srec = reinterpret_cast<uint4*>(sact + 2 * ncl * ldsrow) + (size_t)wave * a.umaxu * kUnionUnitRows;
+    const uint4* rec_g = a.urec + (size_t)grp * a.ustride;
+    for (int e = lane; e < my_n * kUnionUnitRows; e += 64) {
+      const int j = e / kUnionUnitRows, rr = e % kUnionUnitRows;
+      srec[e] = rec_g[min(unit_of(j) * kUnionUnitRows + rr, N - 1)];
+    }
+  }
+
   {  // the group's panel: hi plane rows [0, ncl), lo plane rows [ncl, 2 ncl)
     const int per_row = K / 8;
     for (int idx = threadIdx.x; idx < ncl * per_row; idx += WV * 64) {
@@ -269,32 +294,28 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
     __syncthreads();
   }
 
-  // this wave's row units: w, w + stride, ... (walked backwards when reversed)
-  const int units = ((N + 15) / 16 + RT - 1) / RT;
-  const int w = part * WV + wave, stride = parts * WV;
-  const int my_n = units > w ? (units - w + stride - 1) / stride : 0;
-  const bool rev = a.reverse != 0;
-  const int nsc = K / kSC;
-  auto unit_of = [&](int j) { return w + (rev ? my_n - 1 - j : j) * stride; };
-  auto kchunk = [&](int ci) { return rev ? nsc - 1 - ci : ci; };
-
   // Prefetch cursor (unit pj, chunk pci), D - 1 super-chunks ahead of the
   // consumer.  Past this wave's last unit (or for a wave without units) the
   // rows are clamped into [0, N), so every load stays inside W; such loads
   // are never consumed.  D divides nsc, so super-chunk ci of any unit sits
   // in ring slot ci % D.  prow: the lane's weight row in each tile of the
-  // cursor's unit (union: looked up in the group's row list).
-  const int32_t* uid_g = EPI == kEpiUnion ? a.uid + (size_t)grp * a.ustride : nullptr;
+  // cursor's unit j (union: the staged record's id; a wave without units
+  // reads row 0).
   int pj = 0, pci = 0;
   int prow0 = 0, prow1 = 0;
   static_assert(RT <= 2, "row cursor holds two tiles");
-  auto set_rows = [&](int u) {
-    const int r0 = min(max((u * RT) * 16 + row, 0), N - 1);
-    const int r1 = min(max((u * RT + 1) * 16 + row, 0), N - 1);
-    prow0 = EPI == kEpiUnion ? uid_g[r0] : r0;
-    prow1 = EPI == kEpiUnion && RT > 1 ? uid_g[r1] : r1;
+  auto set_rows = [&](int j) {
+    if (EPI == kEpiUnion) {
+      const int jj = min(j, my_n - 1);
+      prow0 = jj >= 0 ? (int)srec[jj * kUnionUnitRows + row].x : 0;
+      prow1 = jj >= 0 ? (int)srec[jj * kUnionUnitRows + 16 + row].x : 0;
+    } else {
+      const int u = unit_of(j);
+      prow0 = min(max((u * RT) * 16 + row, 0), N - 1);
+      prow1 = min(max((u * RT + 1) * 16 + row, 0), N - 1);
+    }
   };
-  set_rows(unit_of(0));
+  set_rows(0);
   v8s A[D][RT][4];
   auto load_next = [&](v8s (&dst)[RT][4]) {
     const int k = kchunk(pci) * kSC + q * 8;
@@ -307,7 +328,7 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
     if (++pci == nsc) {
       pci = 0;
       ++pj;
-      set_rows(unit_of(pj));
+      set_rows(pj);
     }
   };
 
@@ -334,12 +355,11 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
     float ebase[NB][RT][4];
     uint4 urc[RT][4];  // union: {id, b2 bits, first member slot, member bits} of the lane's rows
     if (EPI == kEpiUnion) {
-      const uint4* rec_g = a.urec + (size_t)grp * a.ustride;
       const float* mb_g = a.mb_k + (size_t)grp * a.mstride;
 #pragma unroll
       for (int t = 0; t < RT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) urc[t][i] = rec_g[min((u * RT + t) * 16 + 4 * q + i, N - 1)];
+        for (int i = 0; i < 4; ++i) urc[t][i] = srec[j * kUnionUnitRows + t * 16 + 4 * q + i];
 #pragma unroll
       for (int cb = 0; cb < NB; ++cb) {
         const int bl = cb * 16 + row;  // < 32
@@ -608,23 +628,51 @@ void dispatch_argmax(StreamArgs a, hipStream_t st) {
   }
 }
 
-// Union stream: groups of 32 requests, each over its own row list.
-void dispatch_union(StreamArgs a, hipStream_t st) {
+// Union stream: groups of 32 requests, each over its own row list of at
+// most `ubound` rows.  Each wave stages the records of its units in LDS
+// behind the panel; the count per wave is bounded with the smallest grid the
+// launch can choose (one block per CU).
+constexpr size_t kUnionLdsLimit = 156 * 1024;
+int union_units_per_wave(int groups, int ubound) {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+  }
+  const int unit = 8 * groups;
+  const int parts = ((cus + unit - 1) / unit) * unit / groups;
+  const int units = ((ubound + 15) / 16 + kArgmaxRT - 1) / kArgmaxRT;
+  const int waves = parts * kArgmaxWV2;
+  return max(1, (units + waves - 1) / waves);
+}
+size_t union_lds(int K, int ncols, int ubound) {
+  const int groups = (ncols + kUnionGroup - 1) / kUnionGroup;
+  return persist_lds(K, min(ncols, kUnionGroup), true) +
+         (size_t)kArgmaxWV2 * union_units_per_wave(groups, ubound) * kUnionUnitRows * sizeof(uint4);
+}
+void dispatch_union(StreamArgs a, int ubound, hipStream_t st) {
   a.gcols = kUnionGroup;
   a.groups = (a.ncols + kUnionGroup - 1) / kUnionGroup;
-  const size_t lds = persist_lds(a.K, min(a.ncols, kUnionGroup), true);
-  launch_persist_t<2, kArgmaxRT, kArgmaxD, false, true, kEpiUnion, kArgmaxWV2>(a, lds, st);
+  a.umaxu = union_units_per_wave(a.groups, ubound);
+  launch_persist_t<2, kArgmaxRT, kArgmaxD, false, true, kEpiUnion, kArgmaxWV2>(
+      a, union_lds(a.K, a.ncols, ubound), st);
 }
 
 }  // namespace
 
 bool rowstream_supported(int K, int ncols) { return K % kSC == 0 && ncols >= 1 && ncols <= 128; }
 
-bool rowstream_union_supported(int K) {
-  return K % kSC == 0 && persist_fits<kArgmaxD>(K, kUnionGroup, true);
+bool rowstream_union_supported(int K, int ncols, int ubound) {
+  return K % kSC == 0 && (K / kSC) % kArgmaxD == 0 && ncols >= 1 && ncols <= 2 * kUnionGroup &&
+         union_lds(K, ncols, ubound) <= kUnionLdsLimit;
 }
 
-void launch_rowstream_union(StreamArgs a, hipStream_t st) { dispatch_union(a, st); }
+void launch_rowstream_union(StreamArgs a, int ubound, hipStream_t st) {
+  dispatch_union(a, ubound, st);
+}
 
 void launch_rowstream_store(StreamArgs a, hipStream_t st) { dispatch_store(a, st); }
 
@@ -649,6 +697,8 @@ void rowstream_prepare() {
   SETP(1, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax, kArgmaxWV1);
   SETP(2, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax, kArgmaxWV2);
   SETP(2, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax, kArgmaxWV2);
-  SETP(2, kArgmaxRT, kArgmaxD, false, true, kEpiUnion, kArgmaxWV2);
+  (void)hipFuncSetAttribute(
+      (const void*)rowpersist_kernel<2, kArgmaxRT, kArgmaxD, false, true, kEpiUnion, kArgmaxWV2>,
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kUnionLdsLimit);
 #undef SETP
 }

@@ -30,7 +30,7 @@ EXPORTED = ("domino_rollout_create", "domino_rollout_run", "domino_rollout_run_g
             "domino_rollout_run_prefix", "domino_rollout_run_forced",
             "domino_rollout_read_workspace", "domino_rollout_destroy",
             "domino_rollout_last_error", "domino_rollout_set_timing",
-            "domino_rollout_kernel_times")
+            "domino_rollout_kernel_times", "domino_rollout_set_pool_strategy")
 PHASES = {"lmhead": 0, "correct": 1, "gru": 2, "fc1": 3, "pool": 4, "argmax0": 5, "offsets": 6}
 
 
@@ -90,6 +90,8 @@ def load_library():
     lib.domino_rollout_last_error.restype = ctypes.c_char_p
     lib.domino_rollout_set_timing.argtypes = [vp, i32]
     lib.domino_rollout_set_timing.restype = ctypes.c_int
+    lib.domino_rollout_set_pool_strategy.argtypes = [vp, i32]
+    lib.domino_rollout_set_pool_strategy.restype = ctypes.c_int
     lib.domino_rollout_kernel_times.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_int64)]
     lib.domino_rollout_kernel_times.restype = ctypes.c_int
@@ -204,17 +206,22 @@ class DominoRollout:
     def read_workspace(self, which):
         """Copy of a workspace buffer of the last run: 0 = base logits
         [15, B, V] fp32 (step-major), 1 = pool ids [B, K] int32, 2 = the step
-        offsets [B, 14, r] fp32 the library formed (runs with step_s=None)."""
+        offsets [B, 14, r] fp32 the library formed (runs with step_s=None),
+        3 = the pool union size of each group of 32 requests, int32."""
         import torch
         n = ctypes.c_size_t()
         self._check(self.lib.domino_rollout_read_workspace(self.handle, which, None, 0,
                                                            ctypes.byref(n), None))
-        dt = torch.int32 if which == 1 else torch.float32
+        dt = torch.int32 if which in (1, 3) else torch.float32
         out = torch.empty(n.value // 4, dtype=dt, device="cuda")
         st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self._check(self.lib.domino_rollout_read_workspace(self.handle, which, _ptr(out), n.value,
                                                            ctypes.byref(n), st))
         return out
+
+    def set_pool_strategy(self, strategy):
+        """0 automatic, 1 per-request gather, 2 group unions where supported."""
+        self._check(self.lib.domino_rollout_set_pool_strategy(self.handle, int(strategy)))
 
     def set_timing(self, enable):
         self._check(self.lib.domino_rollout_set_timing(self.handle, 1 if enable else 0))

@@ -169,9 +169,12 @@ domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const void* base_
  * least dst_bytes), stream-ordered on `stream`.  which: 0 = base logits fp32
  * [15, batch, V] (step-major), 1 = pool ids int32 [batch, K] sorted
  * ascending (pool runs only), 2 = step_s fp32 [batch, 14, r] as the library
- * computed it (runs with step_s = NULL only).  *bytes receives the buffer's size for the
- * last run; with dst == NULL nothing is copied.  INVALID_ARG if which is
- * unknown, no run has happened, or dst_bytes is too small. */
+ * computed it (runs with step_s = NULL only), 3 = int32 [ceil(batch / 32)]
+ * sizes of the pool unions of each group of 32 requests (pool runs that
+ * streamed the unions: bf16 weights, 17 <= batch <= 64).  *bytes receives
+ * the buffer's size for the last run; with dst == NULL nothing is copied.
+ * INVALID_ARG if which is unknown or not available for the last run, no run
+ * has happened, or dst_bytes is too small. */
 domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t which, void* dst,
                                               size_t dst_bytes, size_t* bytes, void* stream);
 
@@ -187,6 +190,20 @@ domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t
  * first-proposal argmax, 6 = step offsets formed in the library.  which = -1
  * clears the totals.  Timing changes no result. */
 domino_status_t domino_rollout_set_timing(domino_rollout_t* h, int32_t enable);
+
+/* How pool corrections (0 < K < V) read the fc2 rows when the batch has 17
+ * to 64 requests and the weights are bf16: 0 = automatic (the default: group
+ * unions once the per-request gather would read 96 MB or more per step),
+ * 1 = every request gathers its own K rows, 2 = each group of 32 requests
+ * streams the union of its pools once (where the projector width allows it:
+ * r a multiple of 256 whose 32-request panel fits in LDS; otherwise the
+ * gather).  Both score the same candidates; their dot products are summed in
+ * different orders, so top-1 values may differ in the last bits.  Changing
+ * the strategy waits for the device and drops the handle's cached graphs.
+ * INVALID_ARG for any other value.  ("feat: support tensor-parallel Domino
+ * rollout", "Rollout performance": the candidate pool's gain shrinks at
+ * batch 64, where the pools of a batch cover much of the vocabulary.) */
+domino_status_t domino_rollout_set_pool_strategy(domino_rollout_t* h, int32_t strategy);
 domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int32_t which, double* total_ms,
                                             int64_t* launches);
 

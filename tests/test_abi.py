@@ -95,4 +95,6 @@ def test_null_handle_is_rejected(lib):
     n = ctypes.c_size_t()
     assert lib.domino_rollout_read_workspace(None, 0, None, 0, ctypes.byref(n), None) == \
         R.DOMINO_ERR_INVALID_ARG
+    assert lib.domino_rollout_set_pool_strategy(None, 0) == R.DOMINO_ERR_INVALID_ARG
+    assert lib.domino_rollout_set_timing(None, 1) == R.DOMINO_ERR_INVALID_ARG
     lib.domino_rollout_destroy(None)   # no-op

@@ -7,6 +7,8 @@ vocabulary (5003 ids: several tiles plus a tail) and a strong GRU path, and
 the full Qwen3-8B-shaped and 27B-class workloads in the launch configuration
 the benchmark times.
 """
+import contextlib
+
 import numpy as np
 import pytest
 
@@ -260,25 +262,47 @@ def test_run_rejects_bad_scalars_without_launching():
 
 
 # ------------------------------------------------------------- pool unions
+# The union stream runs for 17..64 requests when r is a multiple of 256
+# (WIDE, r = 512); the automatic choice takes it only for large pools, so
+# these tests force it with set_pool_strategy(2).
+
+@contextlib.contextmanager
+def _pool_strategy(h, strategy):
+    h.set_pool_strategy(strategy)
+    try:
+        yield h
+    finally:
+        h.set_pool_strategy(0)
+
 
 @pytest.mark.parametrize("B,K", [(17, 1), (32, 100), (33, 100), (64, 2048)])
 def test_pool_union_stream(B, K):
-    """Above 16 requests a pool correction streams, for each group of 32
+    """Above 16 requests a pool correction can stream, for each group of 32
     requests, the union of their pools once: group edges (one request alone
-    in the second group at B = 33), one-id pools, and pools covering most of
-    the vocabulary (2048 of 5003 ids)."""
+    in the second group at B = 33), one-id pools, and pools covering nearly
+    the whole vocabulary (2048 of 2053 ids)."""
     G.log(f"[gpu-test] pool union B={B} K={K}")
-    tok, top, h = G.gpu_run(SMALL, B, 600 + B, 0, K, max_batch=64, max_k=2048, scales_key=STRONG)
-    ref = G.oracle_run(SMALL, B, 600 + B, 0, K, scales_key=STRONG)
+    with _pool_strategy(G.handle(WIDE, 64, 2048, STRONG), 2):
+        tok, top, h = G.gpu_run(WIDE, B, 600 + B, 0, K, max_batch=64, max_k=2048,
+                                scales_key=STRONG)
+        un = h.read_workspace(3).cpu().numpy()
+        ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
+        # the masks clear themselves: a second run repeats the first bit for bit
+        tok2, top2, _ = G.gpu_run(WIDE, B, 600 + B, 0, K, max_batch=64, max_k=2048,
+                                  scales_key=STRONG)
+    ref = G.oracle_run(WIDE, B, 600 + B, 0, K, scales_key=STRONG)
     c, _ = compare(tok, top, ref, TOL["bf16"])
     compare(tok, top, ref, TOL["bf16"], margin_min=TIGHT_MARGIN)
     assert c > 0
-    ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
     for b in range(B):
         assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
-    # the masks clear themselves: a second run repeats the first bit for bit
-    tok2, top2, _ = G.gpu_run(SMALL, B, 600 + B, 0, K, max_batch=64, max_k=2048,
-                              scales_key=STRONG)
+    # each group streamed exactly the union of its requests' pools
+    assert un.shape == ((B + 31) // 32,)
+    for g in range((B + 31) // 32):
+        want = set()
+        for b in range(32 * g, min(B, 32 * g + 32)):
+            want.update(ref["pools"][b].tolist())
+        assert int(un[g]) == len(want), f"union of group {g}"
     assert np.array_equal(tok, tok2) and np.array_equal(top.view(np.uint32), top2.view(np.uint32))
 
 
@@ -288,18 +312,58 @@ def test_pool_union_shared_pools():
     the oracle's proposals for that request, bit-identical across copies."""
     import torch
     B, K = 64, 300
-    one = synth.make_inputs(SMALL, 1, 611, 0)
+    one = synth.make_inputs(WIDE, 1, 611, 0)
     inp = synth.Inputs(np.repeat(one.hidden, B, axis=0), np.repeat(one.step_s, B, axis=0),
                        np.repeat(one.verified, B, axis=0))
-    h = G.handle(SMALL, 64, 2048, STRONG)
     hid, s, ver = R.device_inputs(inp)
     G.log(f"[gpu-test] pool union, shared pools B={B} K={K}")
-    tok, top = h.run(hid, s, ver, K)
-    torch.cuda.synchronize()
+    with _pool_strategy(G.handle(WIDE, 64, 2048, STRONG), 2) as h:
+        tok, top = h.run(hid, s, ver, K)
+        torch.cuda.synchronize()
+        un = h.read_workspace(3).cpu().numpy()
     tok, top = tok.cpu().numpy(), top.cpu().numpy()
-    ref = G.oracle_run(SMALL, 1, 611, 0, K, scales_key=STRONG)
+    ref = G.oracle_run(WIDE, 1, 611, 0, K, scales_key=STRONG)
     compare(tok[:1], top[:1], ref, TOL["bf16"])
     assert np.all(tok == tok[:1]) and np.all(top.view(np.uint32) == top[:1].view(np.uint32))
+    assert np.array_equal(un, [K, K])
+
+
+def test_pool_strategy_choices():
+    """Automatic and forced gather read every request's rows (no unions
+    reported), forced unions stream them; all three meet the oracle, graph
+    replays follow a strategy change, and other values are rejected."""
+    B, K = 40, 100
+    h = G.handle(WIDE, 64, 2048, STRONG)
+    ref = G.oracle_run(WIDE, B, 650, 0, K, scales_key=STRONG)
+    for strategy, unions in ((0, False), (1, False), (2, True)):
+        with _pool_strategy(h, strategy):
+            for graph in (False, True):
+                G.log(f"[gpu-test] pool strategy {strategy} graph={graph}")
+                tok, top, _ = G.gpu_run(WIDE, B, 650, 0, K, max_batch=64, max_k=2048,
+                                        scales_key=STRONG, graph=graph)
+                compare(tok, top, ref, TOL["bf16"])
+                if unions:
+                    assert h.read_workspace(3).cpu().numpy().shape == (2,)
+                else:
+                    with pytest.raises(R.DominoError):
+                        h.read_workspace(3)
+    for bad in (-1, 3):
+        with pytest.raises(R.DominoError):
+            h.set_pool_strategy(bad)
+
+
+def test_small_projector_keeps_gather():
+    """r = 128 is one 128-wide chunk per row, too short for the union
+    stream's ring: even when unions are asked for, the pool correction
+    gathers per request and reports no unions."""
+    G.log("[gpu-test] pool gather at B=40, r=128")
+    with _pool_strategy(G.handle(SMALL, 64, 2048, STRONG), 2):
+        tok, top, h = G.gpu_run(SMALL, 40, 640, 0, 100, max_batch=64, max_k=2048,
+                                scales_key=STRONG)
+        with pytest.raises(R.DominoError):
+            h.read_workspace(3)
+    ref = G.oracle_run(SMALL, 40, 640, 0, 100, scales_key=STRONG)
+    compare(tok, top, ref, TOL["bf16"])
 
 
 # ------------------------------------------------ step offsets in the library
