@@ -505,9 +505,9 @@ __global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restr
 // umask (or nullptr): the selected ids also set their request's bit in the
 // member mask of its group (union stream)
 __global__ __launch_bounds__(256) void pool_compact_kernel(
-    const uint32_t* __restrict__ keys, const float* __restrict__ base, int V, int B, int K,
-    const uint32_t* __restrict__ state, const uint32_t* __restrict__ counts, int nch,
-    int32_t* __restrict__ pool_ids, float* __restrict__ pool_base, uint32_t* __restrict__ umask) {
+    const uint32_t* __restrict__ keys, int V, int K, const uint32_t* __restrict__ state,
+    const uint32_t* __restrict__ counts, int nch, int32_t* __restrict__ pool_ids,
+    uint32_t* __restrict__ umask) {
   __shared__ int lds[4];
   const int b = blockIdx.y, chunk = blockIdx.x;
   const uint32_t T = state[2 * b];
@@ -549,8 +549,6 @@ __global__ __launch_bounds__(256) void pool_compact_kernel(
     const int v = v0 + j;
     if (pos < K) {
       pool_ids[(size_t)b * K + pos] = v;
-      for (int t = 1; t < DOMINO_T; ++t)
-        pool_base[((size_t)(t - 1) * B + b) * K + pos] = base[((size_t)t * B + b) * V + v];
       if (umask)
         atomicOr(&umask[(size_t)(b / kUnionGroup) * V + v], 1u << (b % kUnionGroup));
     }
@@ -565,6 +563,22 @@ __global__ __launch_bounds__(256) void pool_compact_kernel(
 // the group's member arrays (row order, then request order), so the base
 // value of (row, request) sits at the row's first slot plus the number of
 // lower member bits.
+
+// base logits of steps 1..14 at the pool ids, [14, B, K]: one thread per
+// entry (ids ascend along a request's pool, so neighbouring threads read
+// nearby ids of the same base row)
+__global__ __launch_bounds__(256) void pool_gather_kernel(const int32_t* __restrict__ pool_ids,
+                                                          const float* __restrict__ base, int V,
+                                                          int B, int K,
+                                                          float* __restrict__ pool_base) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t n = (size_t)B * K;
+  if (idx >= n * DOMINO_S) return;
+  const int t = (int)(idx / n);
+  const size_t bj = idx - (size_t)t * n;  // b * K + j
+  const int b = (int)(bj / K);
+  pool_base[idx] = base[((size_t)(t + 1) * B + b) * V + pool_ids[bj]];
+}
 
 // union rows and members per (group, id chunk)
 __global__ __launch_bounds__(256) void union_count_kernel(const uint32_t* __restrict__ umask,
@@ -631,20 +645,24 @@ __global__ __launch_bounds__(256) void union_compact_kernel(
   if (chunk == nch - 1 && threadIdx.x == 0) un[g] = rows_b + tot_rows;
 }
 
-// base logits of steps 1..14 at every member, in the group's slot order
+// base logits of steps 1..14 at every member, in the group's slot order,
+// read straight from the base logits (all 14 loads issued before the stores)
 __global__ __launch_bounds__(256) void union_members_kernel(
-    const int32_t* __restrict__ pool_ids, const float* __restrict__ pool_base, int B, int K, int V,
+    const int32_t* __restrict__ pool_ids, const float* __restrict__ base, int B, int K, int V,
     const int32_t* __restrict__ uidx, const uint4* __restrict__ urec, int umax,
     float* __restrict__ mb, int mstride) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= B * K) return;
-  const int b = idx / K, j = idx - b * K;
+  const int b = idx / K;
   const int g = b / kUnionGroup, bl = b % kUnionGroup;
   const int v = pool_ids[idx];
+  float vals[DOMINO_S];
+#pragma unroll
+  for (int t = 0; t < DOMINO_S; ++t) vals[t] = base[((size_t)(t + 1) * B + b) * V + v];
   const uint4 rc = urec[(size_t)g * umax + uidx[(size_t)g * V + v]];
   const uint32_t slot = rc.z + __popc(rc.w & ((1u << bl) - 1u));
-  for (int t = 0; t < DOMINO_S; ++t)
-    mb[((size_t)t * 2 + g) * mstride + slot] = pool_base[((size_t)t * B + b) * K + j];
+#pragma unroll
+  for (int t = 0; t < DOMINO_S; ++t) mb[((size_t)t * 2 + g) * mstride + slot] = vals[t];
 }
 
 void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
@@ -662,15 +680,19 @@ void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, i
   DLAUNCH(pool_select_kernel<2>, dim3(B), blk, 0, st, ws.hist, ws.state);
   DLAUNCH(pool_count_kernel, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.counts, nch);
   const bool uni = pool_union(s, ws, B, K);
-  DLAUNCH(pool_compact_kernel, grid, blk, 0, st, ws.keys, ws.base, s.V, B, K, ws.state,
-          ws.counts, nch, ws.pool_ids, ws.pool_base, uni ? ws.umask : nullptr);
+  DLAUNCH(pool_compact_kernel, grid, blk, 0, st, ws.keys, s.V, K, ws.state, ws.counts, nch,
+          ws.pool_ids, uni ? ws.umask : nullptr);
   if (uni) {
     const dim3 ug(nch, (B + kUnionGroup - 1) / kUnionGroup);
     DLAUNCH(union_count_kernel, ug, blk, 0, st, ws.umask, s.V, ws.ucounts, nch);
     DLAUNCH(union_compact_kernel, ug, blk, 0, st, ws.umask, (const bf16_t*)fc2_b, s.V,
             ws.ucounts, nch, ws.urec, ws.uidx, ws.un, ws.umax);
-    DLAUNCH(union_members_kernel, dim3((B * K + 255) / 256), blk, 0, st, ws.pool_ids,
-            ws.pool_base, B, K, s.V, ws.uidx, ws.urec, ws.umax, ws.mb, ws.mstride);
+    DLAUNCH(union_members_kernel, dim3((B * K + 255) / 256), blk, 0, st, ws.pool_ids, ws.base, B,
+            K, s.V, ws.uidx, ws.urec, ws.umax, ws.mb, ws.mstride);
+  } else {
+    const size_t n = (size_t)B * K * DOMINO_S;
+    DLAUNCH(pool_gather_kernel, dim3((unsigned)((n + 255) / 256)), blk, 0, st, ws.pool_ids,
+            ws.base, s.V, B, K, ws.pool_base);
   }
 }
 
@@ -1277,20 +1299,24 @@ constexpr int kPoolSplitMaxBatch = 16;
 // persistent kernel (every pool row is read once per group instead of once
 // per request holding it; the group's products come from one pass over the
 // row).  Building the unions costs ~20 us per block, so the automatic choice
-// takes them once the per-request gather would read kUnionMinGatherBytes per
-// step (measured at 8B shapes, B = 64: the gather wins at K <= 512, the
-// unions from K = 1024 on).
+// takes them once the per-request gather would read enough per step:
+// kUnionMinGatherBytes above 16 requests (measured at 8B shapes, B = 64: the
+// gather wins at K <= 512, the unions from K = 1024 on), half of it for the
+// latency-bound small-batch gather (B = 16, K = 2048: unions 1.13 against
+// 1.27 ms per block; B = 8: even).
 constexpr long long kUnionMinGatherBytes = 96ll << 20;
 static int union_bound(const Shape& s, int K) {
   return (int)std::min<long long>(s.V, (long long)kUnionGroup * K);
 }
 
 bool pool_union(const Shape& s, const Workspace& ws, int B, int K) {
-  if (!(s.bf16 && ws.umask != nullptr && B > kPoolSplitMaxBatch && B <= 2 * kUnionGroup &&
+  if (!(s.bf16 && ws.umask != nullptr && B <= 2 * kUnionGroup &&
         rowstream_union_supported(s.r, B, union_bound(s, K))) ||
       ws.pool_strategy == 1)
     return false;
-  return ws.pool_strategy == 2 || (long long)B * K * s.r * 2 >= kUnionMinGatherBytes;
+  const long long gather = (long long)B * K * s.r * 2;
+  return ws.pool_strategy == 2 ||
+         gather >= (B > kPoolSplitMaxBatch ? kUnionMinGatherBytes : kUnionMinGatherBytes / 2);
 }
 
 void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,

@@ -220,7 +220,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
                              sizeof(float));
     ws.s = (float*)alloc((size_t)DOMINO_S * Bm * r * sizeof(float));
   }
-  const bool unions = h->shape.bf16 && Bm > 16;  // pool_union() needs more than 16 requests
+  const bool unions = h->shape.bf16;  // pool unions (pool_union())
   if (unions) {
     ws.umax = (int)std::min<size_t>(V, (size_t)kUnionGroup * Km);
     ws.mstride = kUnionGroup * (int)Km;

@@ -191,13 +191,13 @@ domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t
  * clears the totals.  Timing changes no result. */
 domino_status_t domino_rollout_set_timing(domino_rollout_t* h, int32_t enable);
 
-/* How pool corrections (0 < K < V) read the fc2 rows when the batch has 17
- * to 64 requests and the weights are bf16: 0 = automatic (the default: group
- * unions once the per-request gather would read 96 MB or more per step),
- * 1 = every request gathers its own K rows, 2 = each group of 32 requests
- * streams the union of its pools once (where the projector width allows it:
- * r a multiple of 256 whose 32-request panel fits in LDS; otherwise the
- * gather).  Both score the same candidates; their dot products are summed in
+/* How pool corrections (0 < K < V) read the fc2 rows when the batch has at
+ * most 64 requests and the weights are bf16: 0 = automatic (the default:
+ * group unions once the per-request gather would read 96 MB or more per step,
+ * 48 MB at 16 requests or fewer), 1 = every request gathers its own K rows,
+ * 2 = each group of 32 requests streams the union of its pools once (where
+ * the projector width allows it: r a multiple of 256 whose 32-request panel
+ * fits in LDS; otherwise the gather).  Both score the same candidates; their dot products are summed in
  * different orders, so top-1 values may differ in the last bits.  Changing
  * the strategy waits for the device and drops the handle's cached graphs.
  * INVALID_ARG for any other value.  ("feat: support tensor-parallel Domino

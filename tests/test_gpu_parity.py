@@ -275,7 +275,7 @@ def _pool_strategy(h, strategy):
         h.set_pool_strategy(0)
 
 
-@pytest.mark.parametrize("B,K", [(17, 1), (32, 100), (33, 100), (64, 2048)])
+@pytest.mark.parametrize("B,K", [(1, 100), (5, 300), (17, 1), (32, 100), (33, 100), (64, 2048)])
 def test_pool_union_stream(B, K):
     """Above 16 requests a pool correction can stream, for each group of 32
     requests, the union of their pools once: group edges (one request alone
