@@ -148,10 +148,11 @@ struct FusedArgs {
   uint64_t* slots;     // argmax words of position 0 [B]
   int V, H, B;
 };
-// Below this batch the LM-head streams lm_head once through the row kernel
-// (more workgroups, measured faster up to 4 requests); from it on, the fused
-// GEMM with the pool-key and first-proposal epilogue.
-constexpr int kFusedMinBatch = 5;
+// A single request streams lm_head once through the row kernel (8B, per
+// block: 1.117 against 1.152 ms fused); from two requests on, the fused
+// GEMM with the pool-key and first-proposal epilogue (B = 2: even at K0,
+// 0.622 against 0.632 ms at K = 2048; B = 3: 1.223 against 1.232 ms).
+constexpr int kFusedMinBatch = 2;
 void lmhead_fused_prepare();
 bool lmhead_fused_supported(int H);
 void launch_lmhead_fused(const FusedArgs& a, hipStream_t st);

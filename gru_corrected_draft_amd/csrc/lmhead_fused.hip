@@ -331,6 +331,203 @@ __global__ __launch_bounds__(256) void lmhead_lines_kernel(FusedArgs a) {
   fused_epilogue(a, acc, ring, v0, b0, wave, row, q, tid);
 }
 
+// ------------------------------------------------- 32x32x16 matrix products
+// A workgroup computes 256 vocabulary rows against 8 requests x 16 draft
+// positions (position 15 is padding: its rows repeat position 14 and are
+// dropped).  The activation rows are the A operand and the lm_head rows the
+// B operand of V_MFMA_F32_32X32X16_BF16, so lane l of an output tile holds
+// vocabulary id l % 32 and 16 activation rows 8 (i / 4) + 4 (l / 32) + i % 4:
+// each request's positions sit in one lane pair (l, l + 32), a base-logit
+// store writes two whole 128-byte lines, the block max of a (request, id) is
+// one shuffle away and position 0 is register 0 / 8 of lanes 0..31.  Each of
+// the four waves owns 64 vocabulary rows and all 128 activation rows (4 x 2
+// tiles, 128 accumulators).  Operands reach LDS as the line kernel's: 8 rows
+// x 128 B per copy, 64-wide k stages, 16-byte chunk c of a row at position
+// c ^ ((r >> 1) & 7) (r = the row's index in its 32-row tile), so the 16
+// lanes of a fragment read hit distinct banks; both rings are three stages
+// deep (two in flight, 144 KB).
+//
+// Measured against the line kernel at 8B shapes (LM-head ms): B = 5 0.344 /
+// 0.396, 8 0.363 / 0.413, 16 0.431 / 0.458, 24 0.652 / 0.661, 32 0.838 /
+// 0.668, 48 1.187 / 0.975.  Its loop alone (no copies) runs at ~1 PFLOP/s: the
+// compiler waits for all outstanding LDS reads twice per stage and one wave
+// per SIMD cannot cover those stalls, so above 24 requests the line kernel's
+// higher fragment reuse wins.
+typedef float v16f __attribute__((ext_vector_type(16)));
+constexpr int kM32MaxBatch = 24;
+constexpr int kMR = 8;                         // requests per workgroup
+constexpr int kMRows = kMR * 16;               // activation rows per workgroup
+constexpr int kMK = 64;                        // k per stage
+constexpr int kMXStage = kMRows * kMK * 2;     // 16 KB
+constexpr int kMXCopies = kMRows / 8 / 4;      // 4 per wave
+constexpr int kMWindow = 6;                    // fragment reads ahead of the products
+// TV vocabulary tiles of 32 rows per wave (workgroup: 128 TV rows); ring
+// depth R stages per operand
+template <int TV>
+struct M32 {
+  static constexpr int kMV = 128 * TV;
+  static constexpr int kR = TV == 2 ? 3 : 4;
+  static constexpr int kVStage = kMV * kMK * 2;
+  static constexpr size_t kLds = (size_t)kR * (kVStage + kMXStage);  // 144 / 128 KB
+  static constexpr int kVCopies = kMV / 8 / 4;
+};
+
+__device__ __forceinline__ v16f mfma32(v8s a, v8s b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int TV>
+__global__ __launch_bounds__(256) void lmhead_m32_kernel(FusedArgs a) {
+  using C = M32<TV>;
+  constexpr int kMV = C::kMV, kMRing = C::kR, kMVStage = C::kVStage, kMVCopies = C::kVCopies;
+  const int V = a.V, H = a.H, B = a.B;
+  const int nvt = (V + kMV - 1) / kMV, ngrp = (B + kMR - 1) / kMR;
+  const int j = blockIdx.x, xcd = j & 7, local = j >> 3;
+  const int vt = (local / ngrp) * 8 + xcd, grp = local % ngrp;
+  if (vt >= nvt) return;  // uniform per workgroup, before any barrier
+  const int v0 = vt * kMV, b0 = grp * kMR;
+  extern __shared__ __align__(1024) unsigned char ring[];
+  unsigned char* const wring = ring;
+  unsigned char* const xring = ring + kMRing * kMVStage;
+  const int lane = threadIdx.x & 63, wave = wave_index();
+
+  // copy duties: lm_head blocks wave + 4i (i < kMVCopies) and activation
+  // blocks wave + 4i (i < 4) of 8 rows; lane (rr = lane / 8, pp = lane % 8)
+  // fetches logical chunk pp ^ ((r >> 1) & 7) of row rr of its block
+  const char* const Wb = reinterpret_cast<const char*>(a.W);
+  const char* const Xb = reinterpret_cast<const char*>(a.X);
+  const int rr = lane >> 3, pp = lane & 7;
+  uint32_t woff[kMVCopies], xoff[kMXCopies];
+#pragma unroll
+  for (int i = 0; i < kMVCopies; ++i) {
+    const int blk = wave + 4 * i;
+    const int r = (blk & 3) * 8 + rr;
+    const int v = min(v0 + blk * 8 + rr, V - 1);
+    woff[i] = ((uint32_t)v * (uint32_t)H + (uint32_t)(pp ^ ((r >> 1) & 7)) * 8u) * 2u;
+  }
+#pragma unroll
+  for (int i = 0; i < kMXCopies; ++i) {
+    const int blk = wave + 4 * i;
+    const int R = blk * 8 + rr;  // activation row of the workgroup
+    const int r = R & 31;
+    const int req = min(b0 + (R >> 4), B - 1);
+    const int pos = min(R & 15, DOMINO_T - 1);
+    xoff[i] = (((uint32_t)req * DOMINO_T + (uint32_t)pos) * (uint32_t)H +
+               (uint32_t)(pp ^ ((r >> 1) & 7)) * 8u) * 2u;
+  }
+  auto issue = [&](int s) {
+    unsigned char* ws = wring + (s % kMRing) * kMVStage;
+    unsigned char* xs = xring + (s % kMRing) * kMXStage;
+    const uint32_t kb = (uint32_t)s * (kMK * 2);
+#pragma unroll
+    for (int i = 0; i < kMVCopies; ++i) dma16(Wb + (woff[i] + kb), ws + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < kMXCopies; ++i) dma16(Xb + (xoff[i] + kb), xs + (wave + 4 * i) * 1024);
+  };
+
+  v16f acc[4][TV];
+#pragma unroll
+  for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+    for (int tv = 0; tv < TV; ++tv)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[ta][tv][i] = 0.f;
+
+  // fragment of this lane in a 32-row tile: row lane % 32, chunk 2 k16 + lane / 32
+  const int frow = lane & 31, fhi = lane >> 5, fsw = (frow >> 1) & 7;
+  const int ns = H / kMK;
+#pragma unroll
+  for (int p = 0; p < kMRing - 1; ++p)
+    if (p < ns) issue(p);
+  for (int s = 0; s < ns; ++s) {
+    // this wave's newest copies are the stages after s (up to kMRing - 2 of them)
+    const int ahead = min(ns - 1 - s, kMRing - 2);
+    if (ahead >= 2) wait_vm<2 * (kMVCopies + kMXCopies)>();
+    else if (ahead == 1) wait_vm<kMVCopies + kMXCopies>();
+    else wait_vm<0>();
+    lds_barrier();  // everyone's stage s landed; stage s - 1 is consumed
+    if (s + kMRing - 1 < ns) issue(s + kMRing - 1);
+    const unsigned char* wsb = wring + (s % kMRing) * kMVStage + wave * (TV * 4096) + frow * 128;
+    const unsigned char* xsb = xring + (s % kMRing) * kMXStage + frow * 128;
+    // The stage's fragment reads (per 16-wide k step: TV lm_head, then 4
+    // activation fragments) run as one stream kMWindow reads ahead of the
+    // products; the scheduling barriers keep it.
+    constexpr int kPer = TV + 4;
+    constexpr int kF = kPer * (kMK / 16);
+    v8s fr[kF];
+    auto rd = [&](int k) {
+      const int k16 = k / kPer, idx = k % kPer;
+      const int cofs = ((2 * k16 + fhi) ^ fsw) * 16;
+      fr[k] = idx < TV ? *reinterpret_cast<const v8s*>(wsb + idx * 4096 + cofs)
+                       : *reinterpret_cast<const v8s*>(xsb + (idx - TV) * 4096 + cofs);
+    };
+    int issued = 0;
+#pragma unroll
+    for (int k16 = 0; k16 < kMK / 16; ++k16) {
+      const int upto = min(k16 * kPer + kPer - 1 + kMWindow, kF - 1);
+#pragma unroll
+      for (int k = 0; k < kF; ++k)
+        if (k >= issued && k <= upto) rd(k);
+      issued = max(issued, upto + 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+        for (int tv = 0; tv < TV; ++tv)
+          acc[ta][tv] = mfma32(fr[k16 * kPer + TV + ta], fr[k16 * kPer + tv], acc[ta][tv]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // epilogue: base logits (step-major), pool score keys, first-proposal argmax
+  const int vl = lane & 31, hh = lane >> 5;
+  uint64_t best[kMR];
+#pragma unroll
+  for (int r = 0; r < kMR; ++r) best[r] = 0;
+#pragma unroll
+  for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+    for (int tv = 0; tv < TV; ++tv) {
+      const int v = v0 + wave * (TV * 32) + tv * 32 + vl;
+      const bool vok = v < V;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int req = b0 + 2 * ta + jj;
+        const bool ok = vok && req < B;
+        float m = -INFINITY;
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int i = jj * 8 + ii;
+          const int pos = 8 * ((i >> 2) & 1) + 4 * hh + (i & 3);
+          const float y = acc[ta][tv][i];
+          if (pos < DOMINO_T) {
+            m = fmaxf(m, y);
+            if (ok) a.base[((size_t)pos * B + req) * V + v] = y;
+          }
+        }
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (a.keys && hh == 0 && ok) a.keys[(size_t)req * V + v] = orderable(m);
+        const uint64_t k0 = pack_key(acc[ta][tv][jj * 8], (uint32_t)v);  // position 0 on hh == 0
+        best[2 * ta + jj] = (hh == 0 && vok) ? umax64(best[2 * ta + jj], k0) : best[2 * ta + jj];
+      }
+    }
+#pragma unroll
+  for (int r = 0; r < kMR; ++r) best[r] = wave_max_u64(best[r]);
+  __shared__ uint64_t wb[4][kMR];
+  if (lane == 0)
+#pragma unroll
+    for (int r = 0; r < kMR; ++r) wb[wave][r] = best[r];
+  __syncthreads();
+  if (threadIdx.x < kMR && b0 + (int)threadIdx.x < B) {
+    const int r = threadIdx.x;
+    publish_max(&a.slots[b0 + r], umax64(umax64(wb[0][r], wb[1][r]), umax64(wb[2][r], wb[3][r])));
+  }
+}
+
+// vocabulary tiles per wave by batch: the 128-row workgroup tile doubles the
+// workgroup count where lm_head streaming, not the products, bounds the time
+constexpr int kM32SmallBatch = 8;
+
 constexpr size_t kLds = (size_t)kStages * kSliceBytes;
 // line-copy kernel whenever H is a multiple of its 64-wide stage
 
@@ -338,6 +535,10 @@ constexpr size_t kLds = (size_t)kStages * kSliceBytes;
 }  // namespace
 
 void lmhead_fused_prepare() {
+  (void)hipFuncSetAttribute((const void*)lmhead_m32_kernel<2>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)M32<2>::kLds);
+  (void)hipFuncSetAttribute((const void*)lmhead_m32_kernel<1>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)M32<1>::kLds);
   (void)hipFuncSetAttribute((const void*)lmhead_fused_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   (void)hipFuncSetAttribute((const void*)lmhead_lines_kernel,
@@ -347,6 +548,22 @@ void lmhead_fused_prepare() {
 bool lmhead_fused_supported(int H) { return H % 32 == 0; }
 
 void launch_lmhead_fused(const FusedArgs& a, hipStream_t st) {
+  // 32-bit byte offsets of the line copies
+  const bool offsets32 = (uint64_t)a.V * a.H * 2 < (1ull << 32) &&
+                         (uint64_t)a.B * DOMINO_T * a.H * 2 < (1ull << 32);
+  if (a.B <= kM32MaxBatch && a.H % kMK == 0 && offsets32) {
+    const int ngrp = (a.B + kMR - 1) / kMR;
+    if (a.B <= kM32SmallBatch) {
+      const int nvt = (a.V + M32<1>::kMV - 1) / M32<1>::kMV;
+      DLAUNCH(lmhead_m32_kernel<1>, dim3(8 * ((nvt + 7) / 8) * ngrp), dim3(256), M32<1>::kLds, st,
+              a);
+    } else {
+      const int nvt = (a.V + M32<2>::kMV - 1) / M32<2>::kMV;
+      DLAUNCH(lmhead_m32_kernel<2>, dim3(8 * ((nvt + 7) / 8) * ngrp), dim3(256), M32<2>::kLds, st,
+              a);
+    }
+    return;
+  }
   const int nvt = (a.V + kBN - 1) / kBN, ngrp = (a.B + kBJ - 1) / kBJ;
   const int grid = 8 * ((nvt + 7) / 8) * ngrp;
   if (a.H % kStageK == 0)
