@@ -135,6 +135,9 @@ def main():
     ap.add_argument("--in-library-s", action="store_true",
                     help="form the per-step projector offsets in the library from the hiddens "
                          "(run without step_s)")
+    ap.add_argument("--step-path", type=int, default=0, choices=(0, 1, 2, 3),
+                    help="GRU/projector step: 0 auto, 1 fused gates + rows, 2 gate kernel + rows, "
+                         "3 gate kernel + matrix cores")
     ap.add_argument("--pool-strategy", type=int, default=0, choices=(0, 1, 2),
                     help="pool correction at 17-64 requests: 0 automatic, 1 per-request "
                          "gather, 2 group unions")
@@ -179,6 +182,7 @@ def main():
     log(f"[bench] {args.workload} B={B} K={K}: inputs ready in {time.time() - t0:.1f}s")
     h = R.DominoRollout(dev, max_batch=B, max_k=max(K, 1))
     h.set_pool_strategy(args.pool_strategy)
+    h.set_step_path(args.step_path)
     P = args.proposals
     prop = None if P == 15 else P
     if args.in_library_s:
@@ -276,6 +280,7 @@ def main():
                    "proj_dim": shape.proj_dim, "block_size": 16, "proposals": P,
                    "step_offsets": "in library" if args.in_library_s else "input",
                    "pool_strategy": ("auto", "gather", "unions")[args.pool_strategy],
+                   "step_path": ("auto", "fused", "gates+rows", "gates+mfma")[args.step_path],
                    "accumulate": "fp32",
                    "mode": "hip graph replay"},
         "roofline": roof,

@@ -19,86 +19,7 @@
 #include "common.h"
 #include "launch.h"
 
-template <bool BF>
-using W_t = typename std::conditional<BF, bf16_t, float>::type;
-
-// ---------------------------------------------------------------- fragments
-// Weight-side (A operand) fragment: 8 consecutive elements of one row.
-template <bool BF>
-struct WFrag;
-template <>
-struct WFrag<true> {
-  v8s f;
-  __device__ __forceinline__ void load(const bf16_t* p) { f = load_frag_bf16(p); }
-};
-template <>
-struct WFrag<false> {
-  F8 f;
-  __device__ __forceinline__ void load(const float* p) { f = load8_f32(p); }
-};
-
-// Activation (B operand) fragment of values exactly representable in the
-// weight type (embedding rows, draft hiddens).
-template <bool BF>
-struct XFrag;
-template <>
-struct XFrag<true> {
-  v8s f;
-  __device__ __forceinline__ void load(const bf16_t* p, bool ok) { f = ok ? load_frag_bf16(p) : zero_frag(); }
-};
-template <>
-struct XFrag<false> {
-  F8 f;
-  __device__ __forceinline__ void load(const float* p, bool ok) { f = ok ? load8_f32(p) : zero8(); }
-};
-
-// Activation fragment of fp32 values (GRU state, projector output).
-template <bool BF>
-struct HFrag;
-template <>
-struct HFrag<true> {
-  v8s hi, lo;
-  __device__ __forceinline__ void load(const float* p, bool ok) {
-    if (ok) {
-      split_hi_lo(load8_f32(p), hi, lo);
-    } else {
-      hi = zero_frag();
-      lo = zero_frag();
-    }
-  }
-};
-template <>
-struct HFrag<false> {
-  F8 f;
-  __device__ __forceinline__ void load(const float* p, bool ok) { f = ok ? load8_f32(p) : zero8(); }
-};
-
-__device__ __forceinline__ v4f mma(const WFrag<true>& a, const XFrag<true>& x, v4f c) {
-  return mfma_bf16(a.f, x.f, c);
-}
-__device__ __forceinline__ v4f mma(const WFrag<false>& a, const XFrag<false>& x, v4f c) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c = mfma_f32(a.f.v[i], x.f.v[i], c);
-  return c;
-}
-__device__ __forceinline__ v4f mma(const WFrag<true>& a, const HFrag<true>& x, v4f c) {
-  c = mfma_bf16(a.f, x.hi, c);
-  return mfma_bf16(a.f, x.lo, c);
-}
-__device__ __forceinline__ v4f mma(const WFrag<false>& a, const HFrag<false>& x, v4f c) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) c = mfma_f32(a.f.v[i], x.f.v[i], c);
-  return c;
-}
-
-template <bool BF>
-__device__ __forceinline__ float load_w(const W_t<BF>* p) {
-  if constexpr (BF) {
-    return bf16_to_f32(*p);
-  } else {
-    return *p;
-  }
-}
+#include "frag.h"
 
 // ------------------------------------------------ per-step projector offsets
 // step_s[b, j, n] = fc1_x[n, :] . X[b, j+1, :] + fc1_b[n], j = 0..13: the
@@ -118,6 +39,11 @@ __device__ __forceinline__ float load_w(const W_t<BF>* p) {
 // about one per CU, each writing its partial product, and a combine kernel
 // adds the splits in a fixed order and the bias.  fp32 models (small) take a
 // direct kernel.
+//
+// The same product forms the GRU input-projection table G[v, :] = W_ih E[v]
+// when a handle is created: row m of the activations is then simply E[m]
+// (the row map below with one row per group), the units are W_ih's 3g rows
+// and there is no bias.
 constexpr int kOfsTile = 64;           // units and rows per workgroup
 constexpr int kOfsSlice = 64;          // k per LDS stage
 constexpr int kOfsPitch = 72;          // LDS row pitch in bf16 (144 bytes)
@@ -145,21 +71,24 @@ __global__ __launch_bounds__(256) void offsets_gemm_kernel(const bf16_t* __restr
                                                            const bf16_t* __restrict__ X,
                                                            const bf16_t* __restrict__ b1,
                                                            float* __restrict__ out, int M, int N,
-                                                           int H, int kper) {
+                                                           int H, int kper, int rpg, int gstride,
+                                                           int roff) {
   __shared__ __attribute__((aligned(16))) bf16_t lw[2][kOfsTile * kOfsPitch];
   __shared__ __attribute__((aligned(16))) bf16_t lx[2][kOfsTile * kOfsPitch];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int n0 = blockIdx.x * kOfsTile, m0 = blockIdx.y * kOfsTile, split = blockIdx.z;
   const int kbeg = split * kper, nsl = kper / kOfsSlice;
   // loader: thread t moves 16 bytes at column 8 (t % 8) of rows t / 8 and t / 8 + 32
-  // (rows past the end are clamped: loaded and dropped)
+  // (rows past the end are clamped: loaded and dropped).  Activation row m is
+  // row (m / rpg) * gstride + m % rpg + roff of X (step offsets: the hiddens
+  // of positions 1..14 of each request; the G table: E row m).  b1 may be NULL.
   const int lr = tid >> 3, lc = (tid & 7) * 8;
   const int na = min(n0 + lr, N - 1), nb = min(n0 + lr + 32, N - 1);
   const int ma = min(m0 + lr, M - 1), mb = min(m0 + lr + 32, M - 1);
   const bf16_t* wpa = W + (size_t)na * H + kbeg + lc;
   const bf16_t* wpb = W + (size_t)nb * H + kbeg + lc;
-  const bf16_t* xpa = X + ((size_t)(ma / DOMINO_S) * DOMINO_T + ma % DOMINO_S + 1) * H + kbeg + lc;
-  const bf16_t* xpb = X + ((size_t)(mb / DOMINO_S) * DOMINO_T + mb % DOMINO_S + 1) * H + kbeg + lc;
+  const bf16_t* xpa = X + ((size_t)(ma / rpg) * gstride + ma % rpg + roff) * H + kbeg + lc;
+  const bf16_t* xpb = X + ((size_t)(mb / rpg) * gstride + mb % rpg + roff) * H + kbeg + lc;
   const int sta = lr * kOfsPitch + lc, stb = (lr + 32) * kOfsPitch + lc;
   // four register stages (named, so they stay in registers): slice k is
   // fetched into stage k % 4 three steps before it is put into LDS buffer
@@ -223,7 +152,7 @@ __global__ __launch_bounds__(256) void offsets_gemm_kernel(const bf16_t* __restr
     const int n = n0 + 32 * wn + 16 * i + 4 * fq;
     if (n >= N) continue;  // N % 4 == 0, so n < N covers n + 3
     float bias[4] = {0.f, 0.f, 0.f, 0.f};
-    if (whole) {
+    if (whole && b1) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) bias[c] = bf16_to_f32(b1[n + c]);
     }
@@ -308,13 +237,52 @@ void launch_step_offsets(const Shape& s, const DeviceWeights& w, const void* X, 
     const dim3 grid((N + kOfsTile - 1) / kOfsTile, (M + kOfsTile - 1) / kOfsTile, splits);
     DLAUNCH(offsets_gemm_kernel, grid, dim3(256), 0, st, (const bf16_t*)w.fc1_x,
             (const bf16_t*)X, (const bf16_t*)w.fc1_b, splits > 1 ? ws.s_tmp : ws.s, M, N, H,
-            H / splits);
+            H / splits, DOMINO_S, DOMINO_T, 1);
     if (splits > 1)
       DLAUNCH(offsets_combine_kernel, dim3((n / 4 + 255) / 256), dim3(256), 0, st,
               (const float*)ws.s_tmp, (const bf16_t*)w.fc1_b, ws.s, M, N, splits);
   } else {
     DLAUNCH(step_offsets_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, st, (const float*)X,
             (const float*)w.fc1_x, (const float*)w.fc1_b, ws.s, B, H, N);
+  }
+}
+
+// ------------------------------------------------ GRU input-projection table
+// G[v, n] = sum_i W_ih[n, i] E[v, i] for every vocabulary id v and gate row n
+// (3g rows ordered r, z, n), fp32.  Formed once per handle; a GRU update of
+// token x then reads row G[x] instead of multiplying W_ih by E[x].
+template <bool BF>
+__global__ __launch_bounds__(256) void gru_table_direct_kernel(const W_t<BF>* __restrict__ E,
+                                                               const W_t<BF>* __restrict__ w_ih,
+                                                               float* __restrict__ G, int V, int n3,
+                                                               int e) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)V * n3) return;
+  const int v = (int)(idx / n3), n = (int)(idx - (size_t)v * n3);
+  const W_t<BF>* x = E + (size_t)v * e;
+  const W_t<BF>* wr = w_ih + (size_t)n * e;
+  float acc = 0.f;
+  for (int i = 0; i < e; ++i) acc = fmaf(load_w<BF>(x + i), load_w<BF>(wr + i), acc);
+  G[idx] = acc;
+}
+
+void launch_gru_table(const Shape& s, const DeviceWeights& w, float* G, hipStream_t st) {
+  const int n3 = 3 * s.g;
+  if (s.bf16 && s.e % kOfsSlice == 0) {
+    // 64 x 64 tiles; units (W_ih rows) fastest, so the W_ih panel stays in L2
+    const dim3 grid((n3 + kOfsTile - 1) / kOfsTile, (s.V + kOfsTile - 1) / kOfsTile, 1);
+    hipLaunchKernelGGL(offsets_gemm_kernel, grid, dim3(256), 0, st, (const bf16_t*)w.w_ih,
+                       (const bf16_t*)w.embed, (const bf16_t*)nullptr, G, s.V, n3, s.e, s.e, 1, 1,
+                       0);
+  } else {
+    const size_t n = (size_t)s.V * n3;
+    const dim3 grid((unsigned)((n + 255) / 256));
+    if (s.bf16)
+      hipLaunchKernelGGL((gru_table_direct_kernel<true>), grid, dim3(256), 0, st,
+                         (const bf16_t*)w.embed, (const bf16_t*)w.w_ih, G, s.V, n3, s.e);
+    else
+      hipLaunchKernelGGL((gru_table_direct_kernel<false>), grid, dim3(256), 0, st,
+                         (const float*)w.embed, (const float*)w.w_ih, G, s.V, n3, s.e);
   }
 }
 
@@ -693,335 +661,6 @@ void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, i
     const size_t n = (size_t)B * K * DOMINO_S;
     DLAUNCH(pool_gather_kernel, dim3((unsigned)((n + 255) / 256)), blk, 0, st, ws.pool_ids,
             ws.base, s.V, B, K, ws.pool_base);
-  }
-}
-
-// ---------------------------------------------------------------- GRU cell
-// One workgroup owns 16 hidden units j0..j0+15 and all B requests.  Its four
-// waves split the reduction dimension (32-wide slices, round robin); the
-// r and z gates accumulate W_ih·x and W_hh·h into one register tile, the n
-// gate keeps a_n and c_n apart.  The partial tiles meet in LDS in a fixed
-// order, so the result does not depend on scheduling.
-template <bool BF>
-struct GruArgs {
-  const W_t<BF>* E;
-  const W_t<BF>* w_ih;
-  const W_t<BF>* w_hh;
-  const float* h_in;       // nullptr: h = 0
-  float* h_out;
-  const int32_t* tok_i32;  // token of request b at tok_i32[b * tok_stride]
-  int tok_stride;
-  const uint64_t* tok_key; // or the argmax word of request b
-  int32_t* bad;
-  int B, V, e, g;
-  float* partial;          // [tiles][splits][4][64][16] when split over workgroups
-};
-
-// floats per (tile, split, gate) block of split partials: 64 requests x 16 units
-constexpr int kPartGate = 64 * 16;
-
-// h' = (1 - z) * n + z * h from the four pre-activation sums of one unit
-template <bool BF>
-__device__ __forceinline__ void gru_finish(const GruArgs<BF>& a, int b, int j, float sr, float sz,
-                                           float an, float cn) {
-  const float hold = a.h_in ? a.h_in[(size_t)b * a.g + j] : 0.0f;
-  const float rg = sigmoidf_(sr);
-  const float zg = sigmoidf_(sz);
-  const float ng = tanhf(an + rg * cn);
-  a.h_out[(size_t)b * a.g + j] = (1.0f - zg) * ng + zg * hold;
-}
-
-template <bool BF, int NB>
-__global__ __launch_bounds__(256) void gru_kernel(GruArgs<BF> a) {
-  const int lane = threadIdx.x & 63, wave = wave_index();
-  const int row = lane & 15, q = lane >> 4;
-  const int j0 = blockIdx.x * 16;
-  const int e = a.e, g = a.g;
-
-  const W_t<BF>* xrow[NB];
-  bool cv[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    const int b = cb * 16 + row;
-    cv[cb] = b < a.B;
-    int tok = 0;
-    if (cv[cb]) {
-      tok = a.tok_key ? key_id(a.tok_key[b]) : a.tok_i32[(size_t)b * a.tok_stride];
-      if (tok < 0 || tok >= a.V) {
-        a.bad[b] = 1;
-        tok = 0;
-      }
-    }
-    xrow[cb] = a.E + (size_t)tok * e + q * 8;
-  }
-
-  v4f ar[NB], az[NB], an[NB], cn[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) ar[cb] = az[cb] = an[cb] = cn[cb] = zero4();
-
-  {
-    const W_t<BF>* pr = a.w_ih + (size_t)(j0 + row) * e + q * 8;
-    const W_t<BF>* pz = pr + (size_t)g * e;
-    const W_t<BF>* pn = pz + (size_t)g * e;
-    for (int c = blockIdx.y * 4 + wave; c < e / 32; c += 4 * gridDim.y) {
-      const int k = c * 32;
-      WFrag<BF> A_r, A_z, A_n;
-      A_r.load(pr + k);
-      A_z.load(pz + k);
-      A_n.load(pn + k);
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        XFrag<BF> x;
-        x.load(xrow[cb] + k, cv[cb]);
-        ar[cb] = mma(A_r, x, ar[cb]);
-        az[cb] = mma(A_z, x, az[cb]);
-        an[cb] = mma(A_n, x, an[cb]);
-      }
-    }
-  }
-  if (a.h_in) {
-    const W_t<BF>* pr = a.w_hh + (size_t)(j0 + row) * g + q * 8;
-    const W_t<BF>* pz = pr + (size_t)g * g;
-    const W_t<BF>* pn = pz + (size_t)g * g;
-    for (int c = blockIdx.y * 4 + wave; c < g / 32; c += 4 * gridDim.y) {
-      const int k = c * 32;
-      WFrag<BF> A_r, A_z, A_n;
-      A_r.load(pr + k);
-      A_z.load(pz + k);
-      A_n.load(pn + k);
-#pragma unroll
-      for (int cb = 0; cb < NB; ++cb) {
-        HFrag<BF> hf;
-        hf.load(a.h_in + (size_t)(cb * 16 + row) * g + q * 8 + k, cv[cb]);
-        ar[cb] = mma(A_r, hf, ar[cb]);
-        az[cb] = mma(A_z, hf, az[cb]);
-        cn[cb] = mma(A_n, hf, cn[cb]);
-      }
-    }
-  }
-
-  __shared__ float red[4][4][NB][256];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      red[wave][0][cb][i * 64 + lane] = ar[cb][i];
-      red[wave][1][cb][i * 64 + lane] = az[cb][i];
-      red[wave][2][cb][i * 64 + lane] = an[cb][i];
-      red[wave][3][cb][i * 64 + lane] = cn[cb][i];
-    }
-  __syncthreads();
-  // thread t finishes register i = t / 64 of lane l = t % 64 of every tile
-  const int l = threadIdx.x & 63, i = threadIdx.x >> 6;
-  const int jj = 4 * (l >> 4) + i, j = j0 + jj;
-  const int nsplit = gridDim.y;
-  float S[NB][4];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-    for (int gt = 0; gt < 4; ++gt)
-      S[cb][gt] = ((red[0][gt][cb][threadIdx.x] + red[1][gt][cb][threadIdx.x]) +
-                   red[2][gt][cb][threadIdx.x]) + red[3][gt][cb][threadIdx.x];
-  if (nsplit > 1) {
-    // partial[tile][split][gate][b][jj]; gru_combine_kernel finishes the units
-    float* mine = a.partial + ((size_t)blockIdx.x * nsplit + blockIdx.y) * 4 * kPartGate;
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-      for (int gt = 0; gt < 4; ++gt)
-        mine[(size_t)gt * kPartGate + (cb * 16 + (l & 15)) * 16 + jj] = S[cb][gt];
-    return;
-  }
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    const int b = cb * 16 + (l & 15);
-    if (b < a.B) gru_finish(a, b, j, S[cb][0], S[cb][1], S[cb][2], S[cb][3]);
-  }
-}
-
-// Sums the split partials of every (request, unit) in split order and applies
-// the gates; one thread per output, units fastest.
-template <bool BF>
-__global__ __launch_bounds__(256) void gru_combine_kernel(GruArgs<BF> a, int nsplit) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= a.B * a.g) return;
-  const int b = t / a.g, j = t - b * a.g;
-  const float* p = a.partial + (size_t)(j >> 4) * nsplit * 4 * kPartGate + b * 16 + (j & 15);
-  float S[4];
-#pragma unroll
-  for (int gt = 0; gt < 4; ++gt) {
-    float acc_s = p[gt * kPartGate];
-    for (int sp = 1; sp < nsplit; ++sp) acc_s += p[((size_t)sp * 4 + gt) * kPartGate];
-    S[gt] = acc_s;
-  }
-  gru_finish(a, b, j, S[0], S[1], S[2], S[3]);
-}
-
-// workgroups per tile along k: at least one 32-wide chunk per wave
-static int gemv_splits(int kdim) {
-  const int n = (kdim / 32) / 4;
-  return n < 1 ? 1 : (n > kGemvSplit ? kGemvSplit : n);
-}
-
-template <bool BF, int NB>
-static void gru_launch(const GruArgs<BF>& a, hipStream_t st) {
-  const int ns = a.partial ? gemv_splits(a.e < a.g ? a.e : a.g) : 1;
-  DLAUNCH((gru_kernel<BF, NB>), dim3(a.g / 16, ns), dim3(256), 0, st, a);
-  if (ns > 1)
-    DLAUNCH((gru_combine_kernel<BF>), dim3((a.B * a.g + 255) / 256), dim3(256), 0, st, a,
-                       ns);
-}
-
-template <bool BF>
-static void gru_dispatch(const GruArgs<BF>& a, hipStream_t st) {
-  switch ((a.B + 15) / 16) {
-    case 1: gru_launch<BF, 1>(a, st); break;
-    case 2: gru_launch<BF, 2>(a, st); break;
-    case 3: gru_launch<BF, 3>(a, st); break;
-    default: gru_launch<BF, 4>(a, st); break;
-  }
-}
-
-void launch_gru(const Shape& s, const DeviceWeights& w, const float* h_in, float* h_out,
-                const int32_t* tok_i32, int tok_stride, const uint64_t* tok_key, int32_t* bad,
-                int B, const Workspace& ws, hipStream_t st) {
-  if (s.bf16 && B <= kRowsGruMaxBatch && rows_supported(s.e, s.g, s.r)) {
-    GruArgs16 a{(const uint16_t*)w.embed, (const uint16_t*)w.w_ih, (const uint16_t*)w.w_hh, h_in,
-                h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g};
-    launch_gru_rows(a, st);
-  } else if (s.bf16) {
-    GruArgs<true> a{(const bf16_t*)w.embed, (const bf16_t*)w.w_ih, (const bf16_t*)w.w_hh, h_in,
-                    h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g, ws.partial};
-    gru_dispatch<true>(a, st);
-  } else {
-    GruArgs<false> a{(const float*)w.embed, (const float*)w.w_ih, (const float*)w.w_hh, h_in,
-                     h_out, tok_i32, tok_stride, tok_key, bad, B, s.V, s.e, s.g, nullptr};
-    gru_dispatch<false>(a, st);
-  }
-}
-
-// ---------------------------------------------------------------- fc1 + SiLU
-// u = SiLU(fc1·h + s_step).  One workgroup per 16 projector units, waves split
-// the GRU width; bf16 models also store u as a hi/lo bf16 pair for fc2.
-template <bool BF>
-struct Fc1Args {
-  const W_t<BF>* F1;
-  const float* h;
-  const float* s;  // [B, 14, r]
-  int step;        // s row (k - 1)
-  float* u;
-  uint16_t* u_hi;
-  uint16_t* u_lo;
-  int B, g, r;
-  float* partial;   // [tiles][splits][64][16]
-};
-
-// u = SiLU(z + s) of one projector unit, with its bf16 hi/lo planes
-template <bool BF>
-__device__ __forceinline__ void fc1_finish(const Fc1Args<BF>& a, int b, int iu, float z) {
-  const int r = a.r;
-  const float v = z + a.s[((size_t)b * DOMINO_S + a.step) * r + iu];
-  const float uu = v * sigmoidf_(v);
-  a.u[(size_t)b * r + iu] = uu;
-  if (BF) {
-    const uint32_t hi = f32_to_bf16(uu);
-    a.u_hi[(size_t)b * r + iu] = (uint16_t)hi;
-    a.u_lo[(size_t)b * r + iu] = (uint16_t)f32_to_bf16(uu - bf16_to_f32(hi));
-  }
-}
-
-template <bool BF, int NB>
-__global__ __launch_bounds__(256) void fc1_kernel(Fc1Args<BF> a) {
-  const int lane = threadIdx.x & 63, wave = wave_index();
-  const int row = lane & 15, q = lane >> 4;
-  const int i0 = blockIdx.x * 16;
-  const int g = a.g, r = a.r;
-  v4f acc[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) acc[cb] = zero4();
-  const W_t<BF>* pw = a.F1 + (size_t)(i0 + row) * g + q * 8;
-  for (int c = blockIdx.y * 4 + wave; c < g / 32; c += 4 * gridDim.y) {
-    const int k = c * 32;
-    WFrag<BF> A;
-    A.load(pw + k);
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-      const int b = cb * 16 + row;
-      HFrag<BF> hf;
-      hf.load(a.h + (size_t)b * g + q * 8 + k, b < a.B);
-      acc[cb] = mma(A, hf, acc[cb]);
-    }
-  }
-  __shared__ float red[4][NB][256];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][cb][i * 64 + lane] = acc[cb][i];
-  __syncthreads();
-  const int l = threadIdx.x & 63, i = threadIdx.x >> 6;
-  const int ii = 4 * (l >> 4) + i, iu = i0 + ii;
-  const int nsplit = gridDim.y;
-  float Z[NB];
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb)
-    Z[cb] = ((red[0][cb][threadIdx.x] + red[1][cb][threadIdx.x]) + red[2][cb][threadIdx.x]) +
-            red[3][cb][threadIdx.x];
-  if (nsplit > 1) {
-    // partial[tile][split][b][ii]; fc1_combine_kernel finishes the units
-    float* mine = a.partial + ((size_t)blockIdx.x * nsplit + blockIdx.y) * kPartGate;
-#pragma unroll
-    for (int cb = 0; cb < NB; ++cb) mine[(cb * 16 + (l & 15)) * 16 + ii] = Z[cb];
-    return;
-  }
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb) {
-    const int b = cb * 16 + (l & 15);
-    if (b < a.B) fc1_finish(a, b, iu, Z[cb]);
-  }
-}
-
-template <bool BF>
-__global__ __launch_bounds__(256) void fc1_combine_kernel(Fc1Args<BF> a, int nsplit) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= a.B * a.r) return;
-  const int b = t / a.r, iu = t - b * a.r;
-  const float* p = a.partial + (size_t)(iu >> 4) * nsplit * kPartGate + b * 16 + (iu & 15);
-  float z = p[0];
-  for (int sp = 1; sp < nsplit; ++sp) z += p[(size_t)sp * kPartGate];
-  fc1_finish(a, b, iu, z);
-}
-
-template <bool BF, int NB>
-static void fc1_launch(const Fc1Args<BF>& a, hipStream_t st) {
-  const int ns = a.partial ? gemv_splits(a.g) : 1;
-  DLAUNCH((fc1_kernel<BF, NB>), dim3(a.r / 16, ns), dim3(256), 0, st, a);
-  if (ns > 1)
-    DLAUNCH((fc1_combine_kernel<BF>), dim3((a.B * a.r + 255) / 256), dim3(256), 0, st, a,
-                       ns);
-}
-template <bool BF>
-static void fc1_dispatch(const Fc1Args<BF>& a, hipStream_t st) {
-  switch ((a.B + 15) / 16) {
-    case 1: fc1_launch<BF, 1>(a, st); break;
-    case 2: fc1_launch<BF, 2>(a, st); break;
-    case 3: fc1_launch<BF, 3>(a, st); break;
-    default: fc1_launch<BF, 4>(a, st); break;
-  }
-}
-
-void launch_fc1(const Shape& s, const DeviceWeights& w, const float* h, const float* step_s,
-                int step, const Workspace& ws, int B, hipStream_t st) {
-  if (s.bf16 && B <= kRowsFc1MaxBatch && rows_supported(s.e, s.g, s.r)) {
-    Fc1Args16 a{(const uint16_t*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r};
-    launch_fc1_rows(a, st);
-  } else if (s.bf16) {
-    Fc1Args<true> a{(const bf16_t*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r,
-                    ws.partial};
-    fc1_dispatch<true>(a, st);
-  } else {
-    Fc1Args<false> a{(const float*)w.fc1, h, step_s, step, ws.u, ws.u_hi, ws.u_lo, B, s.g, s.r,
-                     nullptr};
-    fc1_dispatch<false>(a, st);
   }
 }
 

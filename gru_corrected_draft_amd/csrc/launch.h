@@ -47,12 +47,14 @@ struct Workspace {
   int32_t* pool_ids;   // [Bmax, Kmax]
   float* pool_base;    // [14, Bmax, Kmax]
   float* h[2];         // [Bmax, g] ping-pong GRU state
+  float* c[2];         // [Bmax, 3g] W_hh h of the matching state
+  float* G;            // [V, 3g] GRU input projection of every id (built at create)
   float* u;            // [Bmax, r]
   uint16_t* u_hi;      // [Bmax, r]
   uint16_t* u_lo;      // [Bmax, r]
   uint64_t* slots;     // [15, Bmax] argmax words
   int32_t* bad;        // [Bmax]
-  float* partial;      // split-k partial sums of the GRU / fc1 products
+  float* partial;      // split partial tiles of the step product
   float* s_tmp;        // k-split partials of the step-offset product
   float* s;            // [Bmax, 14, r] per-step projector offsets formed in the library
   // pool rows streamed once per group of kUnionGroup requests (bf16, large batches)
@@ -70,9 +72,6 @@ struct Workspace {
 
 // requests per union group (one 32-bit member mask per union row)
 constexpr int kUnionGroup = 32;
-
-// most workgroups per 16-unit tile along k in the MFMA GRU / fc1 products
-constexpr int kGemvSplit = 4;
 
 constexpr int kPoolChunk = 1024;
 
@@ -109,35 +108,57 @@ void launch_rowstream_argmax(StreamArgs a, hipStream_t st);
 bool rowstream_union_supported(int K, int ncols, int ubound);
 void launch_rowstream_union(StreamArgs a, int ubound, hipStream_t st);
 
-// one-wave-per-row GRU / fc1 (rows.hip), bf16 weights
-struct GruArgs16 {
-  const uint16_t* E;
-  const uint16_t* w_ih;
-  const uint16_t* w_hh;
-  const float* h_in;
-  float* h_out;
-  const int32_t* tok_i32;
+// GRU update and projector layer 1 of one correction step (gru_step.hip).
+// Stacked rows [fc1 (r rows); W_hh (3g rows)] are multiplied by the new state
+// h: rows < r give u = SiLU(z + s) (and its bf16 hi/lo planes), the others
+// c = W_hh h for the next step's gates.  The gates read a = W_ih E[token] from
+// the table G built at create().
+struct StepArgs {
+  const void* F1;          // [r, g] projector layer 1 (GRU half), weight dtype
+  const void* W_hh;        // [3g, g]
+  const float* G;          // [V, 3g] W_ih E[v] for every id v
+  const float* h_prev;     // [B, g] state before the update; nullptr: zero state
+  const float* c_prev;     // [B, 3g] W_hh h_prev (ignored when h_prev is nullptr)
+  float* h_new;            // [B, g] state after the update
+  float* c_new;            // [B, 3g] W_hh h_new (written by the W_hh rows)
+  const int32_t* tok_i32;  // token of request b at tok_i32[b * tok_stride] ...
   int tok_stride;
-  const uint64_t* tok_key;
-  int32_t* bad;
-  int B, V, e, g;
-};
-struct Fc1Args16 {
-  const uint16_t* F1;
-  const float* h;
-  const float* s;
-  int step;
-  float* u;
-  uint16_t* u_hi;
+  const uint64_t* tok_key; // ... or the argmax word of request b
+  int32_t* bad;            // [B]: set to 1 for a token outside [0, V)
+  const float* s;          // [B, 14, r] projector offsets
+  int step;                // s row (k - 1)
+  float* u;                // [B, r]
+  uint16_t* u_hi;          // [B, r] (bf16 models)
   uint16_t* u_lo;
-  int B, g, r;
+  int row0, nrows;         // stacked rows [row0, row0 + nrows); multiples of 16
+  float* partial;          // split partial tiles of the matrix-core path
+  int B, V, g, r;
 };
-constexpr int kRowsMaxBatch = 16;  // the rows kernels take at most this many requests
-// measured crossovers to the split MFMA products (8B shapes: GRU rows win up
-// to 4 requests, fc1 rows up to 12)
-constexpr int kRowsGruMaxBatch = 4;
-constexpr int kRowsFc1MaxBatch = 12;
-static_assert(kRowsGruMaxBatch <= kRowsMaxBatch && kRowsFc1MaxBatch <= kRowsMaxBatch, "rows kernels");
+// arrangements of a step (see gru_step.hip)
+constexpr int kStepAuto = 0;
+constexpr int kStepFused = 1;  // gates evaluated inside the row kernel: one launch
+constexpr int kStepRows = 2;   // gate kernel + row kernel
+constexpr int kStepMfma = 3;   // gate kernel + matrix-core kernel
+constexpr int kStepRowsMaxBatch = 16;      // the row kernels take at most this many requests
+constexpr int kStepFusedMaxBatch = 8;      // ... and with the gates inside, this many
+// Automatic choice, from a sweep at the 8B shapes (per-launch us, fused | gate + rows | gate +
+// matrix cores): B = 1: 5.1 | 4.0 + 4.1 | 4.0 + 4.7; B = 2: 7.0 | 4.3 + 4.5 | 4.2 + 4.7;
+// B = 4: 10.7 | 4.3 + 6.1 | 4.2 + 5.3; B = 8: 18.6 | 4.2 + 9.8 | 4.0 + 5.5.  The fused kernel
+// repeats every request's gate arithmetic in each workgroup, so it wins only while that is
+// cheaper than a launch; the row product never wins and is kept for forced use.
+constexpr int kStepFusedAutoMaxBatch = 2;  // fused up to this batch, then matrix cores
+constexpr int kStepRowsAutoMaxBatch = 0;
+constexpr int kStepMaxSplit = 4;           // workgroups per 16-row tile along g, at most
+// which arrangement runs for B requests (forced: one of the constants above;
+// a forced row path falls back to the matrix cores where rows are unsupported)
+int step_path(const Shape& s, int B, int forced);
+// floats of split partials the matrix-core path may write
+size_t step_partial_floats(int g, int r);
+void step_prepare();
+void launch_gru_gates(const StepArgs& a, hipStream_t st);
+void launch_step_product(const Shape& s, const StepArgs& a, int path, hipStream_t st);
+// G[v, :] = W_ih E[v], [V, 3g] fp32 (kernels.hip)
+void launch_gru_table(const Shape& s, const DeviceWeights& w, float* G, hipStream_t st);
 
 // LM-head GEMM with fused pool-score keys and first-proposal argmax (lmhead_fused.hip)
 struct FusedArgs {
@@ -156,9 +177,6 @@ constexpr int kFusedMinBatch = 2;
 void lmhead_fused_prepare();
 bool lmhead_fused_supported(int H);
 void launch_lmhead_fused(const FusedArgs& a, hipStream_t st);
-bool rows_supported(int e, int g, int r);
-void launch_gru_rows(const GruArgs16& a, hipStream_t st);
-void launch_fc1_rows(const Fc1Args16& a, hipStream_t st);
 
 void launch_reset(const Workspace& ws, int B, int K, hipStream_t st);
 void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int B, hipStream_t st);
@@ -170,12 +188,6 @@ bool pool_union(const Shape& s, const Workspace& ws, int B, int K);
 // with pool_union(), also the per-group unions and member base values
 void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
                        bool keys_ready, hipStream_t st);
-// token source: exactly one of tok_i32 (element b*stride) or tok_key (argmax word b)
-void launch_gru(const Shape& s, const DeviceWeights& w, const float* h_in, float* h_out,
-                const int32_t* tok_i32, int tok_stride, const uint64_t* tok_key, int32_t* bad,
-                int B, const Workspace& ws, hipStream_t st);
-void launch_fc1(const Shape& s, const DeviceWeights& w, const float* h, const float* step_s,
-                int step, const Workspace& ws, int B, hipStream_t st);
 void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
                          hipStream_t st);
 void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,

@@ -5,6 +5,10 @@
 //   -> [pool of K ids]  -> GRU(verified) -> GRU(p1)
 //   -> 14 x { u = SiLU(fc1 h + s) ; corrected argmax ; GRU(new token) }
 // with no GRU update after the last step (2 prefix + 13 feedback updates).
+// On the GPU each GRU update is evaluated in the launch that needs its
+// result (gru_step.hip): the prefix launch forms GRU(verified) and W_hh of
+// it, and correction step k's first launch forms the update by p_k, then
+// projector layer 1 and W_hh of the new state.
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -61,6 +65,7 @@ struct domino_rollout {
   int last_B = 0, last_K = 0;  // shape of the last enqueued run
   bool last_s_internal = false;  // the last run formed step_s itself
   bool last_union = false;       // the last run streamed the pool rows as group unions
+  int step_path = kStepAuto;     // arrangement of the GRU / projector step (set_step_path)
   // measurement: kernel event pairs of the timed phases (see PhaseTimer)
   bool timing = false;
   bool capturing = false;
@@ -207,14 +212,15 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   ws.pool_base = (float*)alloc(DOMINO_S * Bm * Km * 4);
   ws.h[0] = (float*)alloc(Bm * g * 4);
   ws.h[1] = (float*)alloc(Bm * g * 4);
+  ws.c[0] = (float*)alloc(Bm * 3 * g * 4);
+  ws.c[1] = (float*)alloc(Bm * 3 * g * 4);
+  ws.G = (float*)alloc(V * 3 * g * 4);
   ws.u = (float*)alloc(Bm * r * 4);
   ws.u_hi = (uint16_t*)alloc(Bm * r * 2);
   ws.u_lo = (uint16_t*)alloc(Bm * r * 2);
   ws.slots = (uint64_t*)alloc(DOMINO_T * Bm * 8);
   ws.bad = (int32_t*)alloc(Bm * 4);
-  // split-k partials: [16-unit tile][split][gate (GRU: 4, fc1: 1)][64 requests][16 units]
-  const size_t tiles = (g > r ? g : r) / 16;
-  ws.partial = (float*)alloc(tiles * kGemvSplit * 4 * 64 * 16 * sizeof(float));
+  ws.partial = (float*)alloc(step_partial_floats((int)g, (int)r) * sizeof(float));
   if (h->w.fc1_x) {  // in-library step offsets
     ws.s_tmp = (float*)alloc(std::max<size_t>(step_offsets_partial_floats((int)Bm, cfg->hidden, (int)r), 64) *
                              sizeof(float));
@@ -238,6 +244,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   }
   for (void* p : {(void*)ws.base, (void*)ws.keys, (void*)ws.hist, (void*)ws.state, (void*)ws.counts,
                   (void*)ws.pool_ids, (void*)ws.pool_base, (void*)ws.h[0], (void*)ws.h[1],
+                  (void*)ws.c[0], (void*)ws.c[1], (void*)ws.G,
                   (void*)ws.u, (void*)ws.u_hi, (void*)ws.u_lo, (void*)ws.slots, (void*)ws.bad,
                   (void*)ws.partial, h->w.fc1_x ? (void*)ws.s : (void*)ws.partial,
                   h->w.fc1_x ? (void*)ws.s_tmp : (void*)ws.partial}) {
@@ -262,7 +269,16 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   std::call_once(once, [] {
     rowstream_prepare();
     lmhead_fused_prepare();
+    step_prepare();
   });
+  // GRU input projection of every id, G[v, :] = W_ih E[v]; E and W_ih are
+  // borrowed and must not change for the handle's life
+  launch_gru_table(h->shape, h->w, ws.G, nullptr);
+  if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+    set_global_err("create: building the GRU input-projection table failed");
+    domino_rollout_destroy(h);
+    return DOMINO_ERR_HIP;
+  }
   *out = h;
   return DOMINO_OK;
 }
@@ -391,42 +407,70 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
     PhaseTimer t(h, kPool, st);
     launch_pool_build(sh, ws, h->w.fc2_b, B, K, fused, st);
   }
-  // two-token prefix: h = GRU(E[verified], 0); h = GRU(E[p1], h).  It runs
-  // for every P: the first cell is where an invalid verified token is flagged.
-  {
-    PhaseTimer t(h, kGru, st);
-    launch_gru(sh, h->w, nullptr, ws.h[0], ver, 1, nullptr, ws.bad, B, ws, st);
-  }
-  {
-    PhaseTimer t(h, kGru, st);
-    if (forced)
-      launch_gru(sh, h->w, ws.h[0], ws.h[1], forced, DOMINO_T, nullptr, ws.bad, B, ws, st);
-    else
-      launch_gru(sh, h->w, ws.h[0], ws.h[1], nullptr, 0, ws.slots, ws.bad, B, ws, st);
-  }
-  int cur = 1;
+  // Prefix: h(1) = GRU(E[verified], 0) and c(1) = W_hh h(1).  It runs for
+  // every P: its gates are where an invalid verified token is flagged.
   const int steps = P - 1;  // correction steps of this run
-  for (int k = 1; k <= steps; ++k) {
-    {
-      PhaseTimer t(h, kFc1, st);
-      launch_fc1(sh, h->w, ws.h[cur], s, k - 1, ws, B, st);
+  const int path = step_path(sh, B, h->step_path);
+  StepArgs sa{};
+  sa.F1 = h->w.fc1;
+  sa.W_hh = h->w.w_hh;
+  sa.G = ws.G;
+  sa.bad = ws.bad;
+  sa.s = s;
+  sa.u = ws.u;
+  sa.u_hi = ws.u_hi;
+  sa.u_lo = ws.u_lo;
+  sa.partial = ws.partial;
+  sa.B = B;
+  sa.V = sh.V;
+  sa.g = sh.g;
+  sa.r = sh.r;
+  auto step_launches = [&](int phase_gates, int phase_product) {
+    if (path != kStepFused || sa.nrows == 0) {
+      PhaseTimer t(h, phase_gates, st);
+      launch_gru_gates(sa, st);
     }
+    if (sa.nrows > 0) {
+      PhaseTimer t(h, phase_product, st);
+      launch_step_product(sh, sa, path, st);
+    }
+  };
+  sa.h_prev = nullptr;
+  sa.c_prev = nullptr;
+  sa.h_new = ws.h[0];
+  sa.c_new = ws.c[0];
+  sa.tok_i32 = ver;
+  sa.tok_stride = 1;
+  sa.tok_key = nullptr;
+  sa.row0 = sh.r;  // W_hh rows only
+  sa.nrows = steps > 0 ? 3 * sh.g : 0;
+  step_launches(kGru, kGru);
+  int cur = 0;
+  for (int k = 1; k <= steps; ++k) {
+    // h(k+1) = GRU(E[p_k], h(k)); u = SiLU(fc1 h(k+1) + s[k-1]); c(k+1) = W_hh h(k+1)
+    sa.h_prev = ws.h[cur];
+    sa.c_prev = ws.c[cur];
+    sa.h_new = ws.h[cur ^ 1];
+    sa.c_new = ws.c[cur ^ 1];
+    if (forced) {
+      sa.tok_i32 = forced + (k - 1);
+      sa.tok_stride = DOMINO_T;
+      sa.tok_key = nullptr;
+    } else {
+      sa.tok_i32 = nullptr;
+      sa.tok_key = ws.slots + (size_t)(k - 1) * B;
+    }
+    sa.step = k - 1;
+    sa.row0 = 0;
+    sa.nrows = k < steps ? sh.r + 3 * sh.g : sh.r;  // no W_hh after the last step
+    step_launches(kGru, kFc1);
+    cur ^= 1;
     {
       PhaseTimer t(h, kCorrect, st);
       if (pool)
         launch_correct_pool(sh, h->w, ws, k, B, K, st);
       else
         launch_correct_full(sh, h->w, ws, k, B, st);
-    }
-    if (k < steps) {
-      PhaseTimer t(h, kGru, st);
-      if (forced)
-        launch_gru(sh, h->w, ws.h[cur], ws.h[cur ^ 1], forced + k, DOMINO_T, nullptr, ws.bad, B, ws,
-                   st);
-      else
-        launch_gru(sh, h->w, ws.h[cur], ws.h[cur ^ 1], nullptr, 0, ws.slots + (size_t)k * B, ws.bad,
-                   B, ws, st);
-      cur ^= 1;
     }
   }
   launch_writeout(ws, B, P, out_tokens, out_top1, st);
@@ -588,6 +632,21 @@ extern "C" domino_status_t domino_rollout_set_pool_strategy(domino_rollout_t* h,
     for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);  // captured the old strategy
     h->graphs.clear();
     h->ws.pool_strategy = strategy;
+  }
+  return DOMINO_OK;
+}
+
+extern "C" domino_status_t domino_rollout_set_step_path(domino_rollout_t* h, int32_t path) {
+  if (!h) return DOMINO_ERR_INVALID_ARG;
+  if (path < kStepAuto || path > kStepMfma)
+    return h->fail(DOMINO_ERR_INVALID_ARG, "set_step_path: path must be 0, 1, 2 or 3");
+  if (path != h->step_path) {
+    DeviceGuard dg(h->device);
+    if (hipDeviceSynchronize() != hipSuccess)
+      return h->fail(DOMINO_ERR_HIP, "set_step_path: synchronize failed");
+    for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);  // captured the old path
+    h->graphs.clear();
+    h->step_path = path;
   }
   return DOMINO_OK;
 }

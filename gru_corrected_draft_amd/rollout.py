@@ -30,8 +30,11 @@ EXPORTED = ("domino_rollout_create", "domino_rollout_run", "domino_rollout_run_g
             "domino_rollout_run_prefix", "domino_rollout_run_forced",
             "domino_rollout_read_workspace", "domino_rollout_destroy",
             "domino_rollout_last_error", "domino_rollout_set_timing",
-            "domino_rollout_kernel_times", "domino_rollout_set_pool_strategy")
-PHASES = {"lmhead": 0, "correct": 1, "gru": 2, "fc1": 3, "pool": 4, "argmax0": 5, "offsets": 6}
+            "domino_rollout_kernel_times", "domino_rollout_set_pool_strategy",
+            "domino_rollout_set_step_path")
+# gru: the GRU gates (prefix launch, separate gate kernel); step: projector
+# layer 1 and W_hh of the new state (with the gates where fused)
+PHASES = {"lmhead": 0, "correct": 1, "gru": 2, "step": 3, "pool": 4, "argmax0": 5, "offsets": 6}
 
 
 class Config(ctypes.Structure):
@@ -92,6 +95,8 @@ def load_library():
     lib.domino_rollout_set_timing.restype = ctypes.c_int
     lib.domino_rollout_set_pool_strategy.argtypes = [vp, i32]
     lib.domino_rollout_set_pool_strategy.restype = ctypes.c_int
+    lib.domino_rollout_set_step_path.argtypes = [vp, i32]
+    lib.domino_rollout_set_step_path.restype = ctypes.c_int
     lib.domino_rollout_kernel_times.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_int64)]
     lib.domino_rollout_kernel_times.restype = ctypes.c_int
@@ -222,6 +227,10 @@ class DominoRollout:
     def set_pool_strategy(self, strategy):
         """0 automatic, 1 per-request gather, 2 group unions where supported."""
         self._check(self.lib.domino_rollout_set_pool_strategy(self.handle, int(strategy)))
+
+    def set_step_path(self, path):
+        """0 automatic, 1 fused gates + rows, 2 gate kernel + rows, 3 gate kernel + matrix cores."""
+        self._check(self.lib.domino_rollout_set_step_path(self.handle, int(path)))
 
     def set_timing(self, enable):
         self._check(self.lib.domino_rollout_set_timing(self.handle, 1 if enable else 0))

@@ -102,7 +102,12 @@ typedef struct domino_rollout domino_rollout_t;
 
 /* Validates the configuration, checks that the current HIP device is gfx950,
  * records the borrowed weights and allocates the workspace (base logits
- * [15, max_batch, V] fp32, pool buffers, GRU / projector state).  On success
+ * [15, max_batch, V] fp32, pool buffers, GRU / projector state).  It also
+ * forms, once, the GRU input projection of every vocabulary id,
+ * G[v, :] = gru_w_ih · embed[v, :] ([V, 3g] fp32, 1.9 GB at V = 151936,
+ * g = 1024), so that a GRU update reads one row of G instead of multiplying
+ * gru_w_ih by an embedding row; this is why embed and gru_w_ih must not change
+ * while the handle lives.  create() synchronises the device.  On success
  * *out owns the handle; on failure *out is NULL and the status says why
  * (domino_rollout_last_error(NULL) holds the message). */
 domino_status_t domino_rollout_create(const domino_config_t* cfg, const domino_weights_t* w,
@@ -185,11 +190,25 @@ domino_status_t domino_rollout_read_workspace(const domino_rollout_t* h, int32_t
  * waits for the pending events, adds the kernel durations to per-phase
  * totals and returns the total milliseconds and the number of phase
  * instances of one phase: 0 = LM-head GEMM, 1 = correction + argmax (full
- * vocabulary or pool), 2 = GRU cell (with its split-sum kernel where used),
- * 3 = fc1 + SiLU (likewise), 4 = pool build (all its kernels), 5 =
- * first-proposal argmax, 6 = step offsets formed in the library.  which = -1
- * clears the totals.  Timing changes no result. */
+ * vocabulary or pool), 2 = GRU gates (the prefix launch, and the separate
+ * gate kernel of step paths 2 and 3), 3 = step product: projector layer 1 +
+ * SiLU and W_hh of the new state (with the gates in path 1, and its split-sum
+ * kernel where used), 4 = pool build (all its kernels), 5 = first-proposal
+ * argmax, 6 = step offsets formed in the library.  which = -1 clears the
+ * totals.  Timing changes no result. */
 domino_status_t domino_rollout_set_timing(domino_rollout_t* h, int32_t enable);
+
+/* How each correction step forms the GRU update and projector layer 1
+ * (identical arithmetic, different kernels): 0 = automatic by batch (the
+ * default), 1 = one launch whose workgroups each evaluate the GRU gates of
+ * every request before multiplying their rows of [fc1; gru_w_hh] (bf16, at
+ * most 8 requests), 2 = a gate kernel, then the same row product (bf16, at
+ * most 16 requests), 3 = a gate kernel, then a matrix-core product.  Paths 1
+ * and 2 fall back to 3 where they do not apply.  The paths sum in different
+ * orders, so results may differ in the last bits of fp32.  Changing the path
+ * waits for the device and drops the handle's cached graphs.  INVALID_ARG
+ * for any other value. */
+domino_status_t domino_rollout_set_step_path(domino_rollout_t* h, int32_t path);
 
 /* How pool corrections (0 < K < V) read the fc2 rows when the batch has at
  * most 64 requests and the weights are bf16: 0 = automatic (the default:

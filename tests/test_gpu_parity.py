@@ -106,10 +106,11 @@ WIDE = synth.custom_shape(2053, 256, 512, 512, 512, "bf16", 79, name="small-bf16
 
 @pytest.mark.parametrize("B,K", [(17, 0), (40, 100), (64, 0), (64, 300)])
 def test_gemv_split_over_workgroups(B, K):
-    """Above 16 requests the GRU and fc1 products of a 16-unit tile are split
-    over four workgroups along the reduction (512 = 16 chunks of 32) and the
-    last one to arrive adds the partials; the arrival counters reset
-    themselves, so a second run on the same handle must repeat the first."""
+    """Above 12 requests the step product runs on the matrix cores; with
+    g = 512 its 16-row tiles are split over two workgroups along g (four for
+    the last step's projector-only product) and a second kernel adds the
+    partials in split order, so a second run on the same handle must repeat
+    the first bit for bit."""
     G.log(f"[gpu-test] split GEMVs B={B} K={K}")
     tok, top, h = G.gpu_run(WIDE, B, 800 + B, 0, K, max_batch=64, max_k=2048, scales_key=STRONG)
     ref = G.oracle_run(WIDE, B, 800 + B, 0, K, scales_key=STRONG)
@@ -118,6 +119,51 @@ def test_gemv_split_over_workgroups(B, K):
     assert c > 0
     tok2, top2, _ = G.gpu_run(WIDE, B, 800 + B, 0, K, max_batch=64, max_k=2048, scales_key=STRONG)
     assert np.array_equal(tok, tok2) and np.array_equal(top.view(np.uint32), top2.view(np.uint32))
+
+
+# g = e = 96: rows of 24 four-element lane slices, W_hh of 288 rows, and a GRU
+# input table formed by the direct kernel (e is not a multiple of 64)
+ODD = synth.custom_shape(1999, 256, 96, 96, 128, "bf16", 80, name="small-bf16-odd-gru")
+# g = e = 1280: five 256-wide slices per lane in the row kernels, 80 KB of LDS state at 16 requests
+WIDE5 = synth.custom_shape(1031, 256, 1280, 1280, 256, "bf16", 81, name="small-bf16-gru1280")
+STEP_SHAPES = {"small": SMALL, "odd": ODD, "wide5": WIDE5}
+
+
+@pytest.mark.parametrize("shape_name", ["small", "odd", "wide5"])
+@pytest.mark.parametrize("B", [1, 3, 16, 17])
+def test_step_paths(shape_name, B):
+    """Each arrangement of the GRU update + projector step (1: gates inside
+    the row kernel, 2: gate kernel + row kernel, 3: gate kernel + matrix
+    cores; 1 and 2 fall back to 3 above 16 requests) meets the oracle, in
+    eager runs and graph replays, and the three give the same tokens."""
+    shape = STEP_SHAPES[shape_name]
+    K = 0 if B % 2 else 60
+    ref = G.oracle_run(shape, B, 1000 + B, 0, K, scales_key=STRONG)
+    h = G.handle(shape, 17, 64, STRONG)
+    results = []
+    for path in (1, 2, 3, 0):
+        G.log(f"[gpu-test] step path {path} {shape_name} B={B} K={K}")
+        h.set_step_path(path)
+        for graph in (False, True):
+            tok, top, _ = G.gpu_run(shape, B, 1000 + B, 0, K, max_batch=17, max_k=64,
+                                    scales_key=STRONG, graph=graph)
+            compare(tok, top, ref, TOL["bf16"])
+            compare(tok, top, ref, TOL["bf16"], margin_min=TIGHT_MARGIN)
+            results.append(tok)
+    h.set_step_path(0)
+    ok = ref["margin"] >= TIGHT_MARGIN
+    for t in results[1:]:
+        # identical wherever every earlier step of the request is decisive
+        first_bad = np.where(ok.all(axis=1), 15, np.argmin(ok, axis=1))
+        for b in range(B):
+            assert np.array_equal(t[b, :first_bad[b]], results[0][b, :first_bad[b]])
+
+
+def test_step_path_rejects_unknown_values():
+    h = G.handle(SMALL, 64, 2048, STRONG)
+    for bad in (-1, 4):
+        with pytest.raises(R.DominoError):
+            h.set_step_path(bad)
 
 
 @pytest.mark.parametrize("K", [0, 64])
