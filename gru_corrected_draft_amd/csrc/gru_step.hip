@@ -31,6 +31,15 @@
 //  3. gru_gate_kernel, then step_mfma_kernel: matrix-core products over
 //     16-row tiles of the stacked matrix (hi/lo bf16 split of h), optionally
 //     split along g over workgroups with a fixed-order combine.
+//
+// Fragment order (bf16 models, path 3).  A 16x16x32 product reads, in lane l,
+// 8 consecutive k of row l % 16 (weights) or of request l % 16 (state),
+// starting at 8 (l / 16): sixteen 64-byte pieces of sixteen rows per load.
+// Both operands are therefore stored in the order the lanes read them: for
+// each 16-row tile (or 16-request block) and 32-wide chunk c of g, 64 lanes x
+// 8 bf16 = 1 KB contiguous, so a load covers eight whole 128-byte lines.  The
+// weights are packed once at create(); the gate kernel writes the new state
+// both as fp32 [B, g] and as this hi/lo pair (two 1 KB planes per chunk).
 #include "common.h"
 #include "frag.h"
 #include "launch.h"
@@ -104,7 +113,38 @@ __global__ __launch_bounds__(256) void gru_gate_kernel(StepArgs a) {
   if (t >= a.B * ncol) return;
   const int b = t / ncol, col = t - b * ncol;
   const int tok = step_token(a, b, col == 0);
-  *reinterpret_cast<float4*>(a.h_new + (size_t)b * a.g + 4 * col) = gates4(a, b, tok, 4 * col);
+  const float4 v = gates4(a, b, tok, 4 * col);
+  *reinterpret_cast<float4*>(a.h_new + (size_t)b * a.g + 4 * col) = v;
+  if (a.hp) {
+    // units j..j+3 sit in chunk j / 32, lane (j % 32) / 8 * 16 + b % 16, elements j % 8 ..
+    const int j = 4 * col, c = j >> 5, l = ((j & 31) >> 3) * 16 + (b & 15), e = j & 7;
+    const size_t o = ((((size_t)(b >> 4) * (a.g >> 5) + c) * 2) * 64 + l) * 8 + e;
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      hi[i] = f32_to_bf16(x[i]);
+      lo[i] = f32_to_bf16(x[i] - bf16_to_f32(hi[i]));
+    }
+    *reinterpret_cast<uint2*>(a.hp + o) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+    *reinterpret_cast<uint2*>(a.hp + o + 512) =
+        make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+  }
+}
+
+// stacked [fc1; W_hh] rows into fragment order, one thread per (tile, chunk, lane)
+__global__ __launch_bounds__(256) void pack_step_weights_kernel(const bf16_t* __restrict__ F1,
+                                                                const bf16_t* __restrict__ W_hh,
+                                                                bf16_t* __restrict__ Wp, int r,
+                                                                int g, int n) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= n) return;
+  const int nch = g >> 5;
+  const int l = t & 63, tc = t >> 6;
+  const int T = tc / nch, c = tc - T * nch;
+  const int R = T * 16 + (l & 15), k = c * 32 + (l >> 4) * 8;
+  const bf16_t* src = R < r ? F1 + (size_t)R * g + k : W_hh + (size_t)(R - r) * g + k;
+  *reinterpret_cast<uint4*>(Wp + (size_t)t * 8) = *reinterpret_cast<const uint4*>(src);
 }
 
 // ------------------------------------------------------------ row kernel
@@ -266,16 +306,21 @@ __global__ __launch_bounds__(512) void step_mfma_kernel(StepArgs a) {
   const int row = lane & 15, q = lane >> 4;
   const int R0 = a.row0 + blockIdx.x * 16;
   const int g = a.g, r = a.r, nch = g / 32;
-  const W_t<BF>* pw = (R0 < r ? (const W_t<BF>*)a.F1 + (size_t)(R0 + row) * g
-                              : (const W_t<BF>*)a.W_hh + (size_t)(R0 - r + row) * g) +
-                      q * 8;
+  // bf16: packed operands, chunk c of tile T at ((T nch + c) 64 + lane) 8; fp32: row-major
+  const W_t<BF>* pw = BF ? (const W_t<BF>*)a.Wp + ((size_t)(R0 >> 4) * nch * 64 + lane) * 8
+                         : (R0 < r ? (const W_t<BF>*)a.F1 + (size_t)(R0 + row) * g
+                                   : (const W_t<BF>*)a.W_hh + (size_t)(R0 - r + row) * g) +
+                               q * 8;
+  const int wstep = BF ? 64 * 8 : 32;  // elements from one chunk to the next
   const float* hrow[NB];
+  const bf16_t* hpk[NB];
   bool bok[NB];
 #pragma unroll
   for (int cb = 0; cb < NB; ++cb) {
     const int b = cb * 16 + row;
     bok[cb] = b < a.B;
     hrow[cb] = a.h_new + (size_t)min(b, a.B - 1) * g + q * 8;
+    hpk[cb] = BF ? a.hp + ((size_t)cb * nch * 2 * 64 + lane) * 8 : nullptr;
   }
   v4f acc[NB];
 #pragma unroll
@@ -288,10 +333,20 @@ __global__ __launch_bounds__(512) void step_mfma_kernel(StepArgs a) {
     for (int i = 0; i < CPW; ++i) {
       const int c = c0 + i * stride;
       const bool live = c < nch;
-      const int k = (live ? c : c0) * 32;
-      A[i].load(pw + k);
+      const int cc = live ? c : c0;
+      A[i].load(pw + (size_t)cc * wstep);
 #pragma unroll
-      for (int cb = 0; cb < NB; ++cb) load_h(X[i][cb], hrow[cb] + k, bok[cb] && live);
+      for (int cb = 0; cb < NB; ++cb) {
+        if constexpr (BF) {
+          const bf16_t* p = hpk[cb] + (size_t)cc * 2 * 512;
+          const v8s hi = load_frag_bf16(p), lo = load_frag_bf16(p + 512);
+          const bool ok = bok[cb] && live;
+          X[i][cb].hi = ok ? hi : zero_frag();
+          X[i][cb].lo = ok ? lo : zero_frag();
+        } else {
+          load_h(X[i][cb], hrow[cb] + cc * 32, bok[cb] && live);
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
@@ -421,6 +476,14 @@ int step_path(const Shape& s, int B, int forced) {
   if (B <= kStepFusedAutoMaxBatch) return kStepFused;
   if (B <= kStepRowsAutoMaxBatch) return kStepRows;
   return kStepMfma;
+}
+
+size_t step_packed_weight_elems(int g, int r) { return (size_t)(r + 3 * g) * g; }
+
+void launch_pack_step_weights(const Shape& s, const DeviceWeights& w, uint16_t* Wp, hipStream_t st) {
+  const int n = (s.r + 3 * s.g) / 16 * (s.g / 32) * 64;
+  hipLaunchKernelGGL(pack_step_weights_kernel, dim3((n + 255) / 256), dim3(256), 0, st,
+                     (const bf16_t*)w.fc1, (const bf16_t*)w.w_hh, (bf16_t*)Wp, s.r, s.g, n);
 }
 
 void launch_gru_gates(const StepArgs& a, hipStream_t st) {

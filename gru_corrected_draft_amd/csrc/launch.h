@@ -48,6 +48,8 @@ struct Workspace {
   float* pool_base;    // [14, Bmax, Kmax]
   float* h[2];         // [Bmax, g] ping-pong GRU state
   float* c[2];         // [Bmax, 3g] W_hh h of the matching state
+  uint16_t* Wp;        // stacked [fc1; W_hh] in fragment order (bf16 models)
+  uint16_t* hp;        // new state in fragment order, hi/lo bf16 (bf16 models)
   float* G;            // [V, 3g] GRU input projection of every id (built at create)
   float* u;            // [Bmax, r]
   uint16_t* u_hi;      // [Bmax, r]
@@ -132,6 +134,10 @@ struct StepArgs {
   uint16_t* u_lo;
   int row0, nrows;         // stacked rows [row0, row0 + nrows); multiples of 16
   float* partial;          // split partial tiles of the matrix-core path
+  // bf16 matrix-core path: operands in fragment order (see gru_step.hip)
+  const uint16_t* Wp;      // [(r + 3g) / 16][g / 32][64 lanes][8] stacked weights
+  uint16_t* hp;            // [ceil(B / 16)][g / 32][hi, lo][64 lanes][8] new state, written
+                           // by the gate kernel when not nullptr
   int B, V, g, r;
 };
 // arrangements of a step (see gru_step.hip)
@@ -156,6 +162,9 @@ int step_path(const Shape& s, int B, int forced);
 size_t step_partial_floats(int g, int r);
 void step_prepare();
 void launch_gru_gates(const StepArgs& a, hipStream_t st);
+// [fc1; W_hh] (bf16) in fragment order for the matrix-core step product
+size_t step_packed_weight_elems(int g, int r);
+void launch_pack_step_weights(const Shape& s, const DeviceWeights& w, uint16_t* Wp, hipStream_t st);
 void launch_step_product(const Shape& s, const StepArgs& a, int path, hipStream_t st);
 // G[v, :] = W_ih E[v], [V, 3g] fp32 (kernels.hip)
 void launch_gru_table(const Shape& s, const DeviceWeights& w, float* G, hipStream_t st);

@@ -215,6 +215,15 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   ws.c[0] = (float*)alloc(Bm * 3 * g * 4);
   ws.c[1] = (float*)alloc(Bm * 3 * g * 4);
   ws.G = (float*)alloc(V * 3 * g * 4);
+  if (h->shape.bf16) {
+    ws.Wp = (uint16_t*)alloc(step_packed_weight_elems((int)g, (int)r) * 2);
+    ws.hp = (uint16_t*)alloc((Bm + 15) / 16 * 16 * g * 4);
+    if (!ws.Wp || !ws.hp) {
+      set_global_err("create: workspace allocation failed");
+      domino_rollout_destroy(h);
+      return DOMINO_ERR_OUT_OF_MEMORY;
+    }
+  }
   ws.u = (float*)alloc(Bm * r * 4);
   ws.u_hi = (uint16_t*)alloc(Bm * r * 2);
   ws.u_lo = (uint16_t*)alloc(Bm * r * 2);
@@ -259,6 +268,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
     if (hipMemset(h->allocations[i], 0, 256) != hipSuccess) break;
   }
   if ((unions && hipMemset(ws.umask, 0, 2 * V * 4) != hipSuccess) ||
+      (ws.hp && hipMemset(ws.hp, 0, (Bm + 15) / 16 * 16 * g * 4) != hipSuccess) ||
       hipMemset(ws.pool_ids, 0, Bm * Km * 4) != hipSuccess ||
       hipMemset(ws.base, 0, DOMINO_T * Bm * V * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     set_global_err("create: workspace initialisation failed");
@@ -271,9 +281,11 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
     lmhead_fused_prepare();
     step_prepare();
   });
-  // GRU input projection of every id, G[v, :] = W_ih E[v]; E and W_ih are
-  // borrowed and must not change for the handle's life
+  // GRU input projection of every id, G[v, :] = W_ih E[v], and the stacked
+  // step weights in fragment order; the weights are borrowed and must not
+  // change for the handle's life
   launch_gru_table(h->shape, h->w, ws.G, nullptr);
+  if (h->shape.bf16) launch_pack_step_weights(h->shape, h->w, ws.Wp, nullptr);
   if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     set_global_err("create: building the GRU input-projection table failed");
     domino_rollout_destroy(h);
@@ -421,6 +433,8 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
   sa.u_hi = ws.u_hi;
   sa.u_lo = ws.u_lo;
   sa.partial = ws.partial;
+  sa.Wp = ws.Wp;
+  sa.hp = path == kStepMfma ? ws.hp : nullptr;  // only the matrix-core product reads it
   sa.B = B;
   sa.V = sh.V;
   sa.g = sh.g;

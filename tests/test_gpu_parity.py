@@ -247,14 +247,16 @@ def test_batch_permutation_bit_exact(B):
 
 def test_batch_independence():
     """Each request run alone gives the same proposals as inside a batch: bit
-    for bit while both batch sizes take the same kernels (4 requests and 1
-    run the one-wave-per-unit GRU), and within float32 rounding of the GRU
-    sums when the batch crosses to the matrix-core GRU (8 requests)."""
+    for bit while both batch sizes take the same step kernels (the fused step
+    at 1 and 2 requests, or the matrix-core step forced at 1 and 4), and
+    within float32 rounding of the GRU sums when the batch crosses from the
+    fused step to the matrix-core one (8 requests)."""
     h = G.handle(SMALL, 64, 2048, STRONG)
-    for B, exact in ((4, True), (8, False)):
+    for path, B, exact in ((0, 2, True), (3, 4, True), (0, 8, False)):
+        h.set_step_path(path)
         inp = synth.make_inputs(SMALL, B, 904, 0)
         for K in (0, 100):
-            G.log(f"[gpu-test] batch independence B={B} K={K}")
+            G.log(f"[gpu-test] batch independence path={path} B={B} K={K}")
             t_all, l_all = _run_rows(h, inp, list(range(B)), K)
             for b in range(B):
                 t1, l1 = _run_rows(h, inp, [b], K)
@@ -263,6 +265,7 @@ def test_batch_independence():
                     assert np.array_equal(l1[0].view(np.uint32), l_all[b].view(np.uint32)), b
                 else:
                     np.testing.assert_allclose(l1[0], l_all[b], rtol=1e-5, atol=1e-5)
+    h.set_step_path(0)
 
 
 def test_out_of_range_verified_token_poisons_only_its_request():
