@@ -795,6 +795,7 @@ void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace
   if (s.bf16 && rowstream_supported(s.r, B)) {
     StreamArgs a{(const uint16_t*)w.fc2, s.V, s.r, ws.u_hi, ws.u_lo, B, 0, 0, nullptr,
                  (const uint16_t*)w.fc2_b, base_k, slot_k, kReverseOddSteps ? (k & 1) : 0};
+    a.Wpk = B >= kPackedStreamMinBatch ? ws.fc2p : nullptr;
     launch_rowstream_argmax(a, st);
   } else if (s.bf16) {
     CorrArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, base_k, ws.u, ws.u_hi, ws.u_lo,

@@ -50,6 +50,8 @@ struct Workspace {
   float* c[2];         // [Bmax, 3g] W_hh h of the matching state
   uint16_t* Wp;        // stacked [fc1; W_hh] in fragment order (bf16 models)
   uint16_t* hp;        // new state in fragment order, hi/lo bf16 (bf16 models)
+  uint16_t* fc2p;      // fc2 in tile order for the full-vocabulary stream (bf16, r % 128 == 0,
+                       // max_batch >= kPackedStreamMinBatch)
   float* G;            // [V, 3g] GRU input projection of every id (built at create)
   float* u;            // [Bmax, r]
   uint16_t* u_hi;      // [Bmax, r]
@@ -71,6 +73,15 @@ struct Workspace {
   int mstride;         // member slots per group, kUnionGroup * Kmax
   int pool_strategy;   // 0 automatic, 1 per-request gather, 2 group unions where supported
 };
+
+// The full-vocabulary correction reads fc2 in tile order from this batch on.
+// Measured at the 8B shapes (us per launch, tile order / row-major): B = 1
+// 51.5 / 49.2, 8 53.6 / 51.5, 16 55.7 / 55.1, 24 61.7 / 62.8, 32 64.5 / 65.5,
+// 48 71.2 / 86.6, 64 69.4 / 89.2.  Up to 16 requests every fc2 line crosses
+// from L2 to the CUs once and row-major streams slightly faster; with two
+// 32-request groups it crosses twice, and the fragment-shaped loads of the
+// row-major layout limit that traffic.
+constexpr int kPackedStreamMinBatch = 17;
 
 // requests per union group (one 32-bit member mask per union row)
 constexpr int kUnionGroup = 32;
@@ -100,8 +111,14 @@ struct StreamArgs {
   const float* mb_k;       // [groups, mstride] for this step
   int ustride, mstride;
   int umaxu;               // units per wave staged in LDS (set by the launcher)
+  // W repacked in tile order (launch_pack_tiles), or nullptr; the persistent
+  // full-vocabulary argmax stream reads it instead of W
+  const uint16_t* Wpk;
 };
 bool rowstream_supported(int K, int ncols);
+// W [N, K] (K a multiple of 128) in tile order, N rounded up to 16 rows
+size_t packed_tiles_elems(int N, int K);
+void launch_pack_tiles(const uint16_t* W, int N, int K, uint16_t* out, hipStream_t st);
 void rowstream_prepare();
 void launch_rowstream_store(StreamArgs a, hipStream_t st);
 void launch_rowstream_argmax(StreamArgs a, hipStream_t st);

@@ -215,10 +215,13 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   ws.c[0] = (float*)alloc(Bm * 3 * g * 4);
   ws.c[1] = (float*)alloc(Bm * 3 * g * 4);
   ws.G = (float*)alloc(V * 3 * g * 4);
+  const bool pack_fc2 =
+      h->shape.bf16 && rowstream_supported((int)r, 1) && cfg->max_batch >= kPackedStreamMinBatch;
   if (h->shape.bf16) {
     ws.Wp = (uint16_t*)alloc(step_packed_weight_elems((int)g, (int)r) * 2);
     ws.hp = (uint16_t*)alloc((Bm + 15) / 16 * 16 * g * 4);
-    if (!ws.Wp || !ws.hp) {
+    if (pack_fc2) ws.fc2p = (uint16_t*)alloc(packed_tiles_elems((int)V, (int)r) * 2);
+    if (!ws.Wp || !ws.hp || (pack_fc2 && !ws.fc2p)) {
       set_global_err("create: workspace allocation failed");
       domino_rollout_destroy(h);
       return DOMINO_ERR_OUT_OF_MEMORY;
@@ -281,11 +284,12 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
     lmhead_fused_prepare();
     step_prepare();
   });
-  // GRU input projection of every id, G[v, :] = W_ih E[v], and the stacked
-  // step weights in fragment order; the weights are borrowed and must not
-  // change for the handle's life
+  // GRU input projection of every id, G[v, :] = W_ih E[v], the stacked step
+  // weights in fragment order and fc2 in tile order; the weights are borrowed
+  // and must not change for the handle's life
   launch_gru_table(h->shape, h->w, ws.G, nullptr);
   if (h->shape.bf16) launch_pack_step_weights(h->shape, h->w, ws.Wp, nullptr);
+  if (ws.fc2p) launch_pack_tiles((const uint16_t*)h->w.fc2, (int)V, (int)r, ws.fc2p, nullptr);
   if (hipGetLastError() != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     set_global_err("create: building the GRU input-projection table failed");
     domino_rollout_destroy(h);

@@ -239,7 +239,10 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
 // that request's pool, with the base value from the members' compact array.  WV waves per block share the panel (8
 // when the panel allows one block per CU, so two waves per SIMD overlap
 // their products with their loads).
-template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI, int WV>
+// PK: the weights come from a.Wpk, W repacked in tile order (see
+// pack_tiles_kernel): one load instruction of a wave then reads 1 KB of whole
+// 128-byte lines instead of sixteen 64-byte pieces of sixteen rows.
+template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI, int WV, bool PK = false>
 __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
   extern __shared__ __align__(16) bf16_t sact[];
   const int lane = threadIdx.x & 63, wave = wave_index();
@@ -304,8 +307,14 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
   int pj = 0, pci = 0;
   int prow0 = 0, prow1 = 0;
   static_assert(RT <= 2, "row cursor holds two tiles");
+  static_assert(!PK || EPI != kEpiUnion, "unions gather rows by id");
+  const int ntiles = (N + 15) / 16;
   auto set_rows = [&](int j) {
-    if (EPI == kEpiUnion) {
+    if (PK) {  // tile indices, clamped like the rows
+      const int u = unit_of(j);
+      prow0 = min(max(u * RT, 0), ntiles - 1);
+      prow1 = min(max(u * RT + 1, 0), ntiles - 1);
+    } else if (EPI == kEpiUnion) {
       const int jj = min(j, my_n - 1);
       prow0 = jj >= 0 ? (int)srec[jj * kUnionUnitRows + row].x : 0;
       prow1 = jj >= 0 ? (int)srec[jj * kUnionUnitRows + 16 + row].x : 0;
@@ -318,12 +327,22 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
   set_rows(0);
   v8s A[D][RT][4];
   auto load_next = [&](v8s (&dst)[RT][4]) {
-    const int k = kchunk(pci) * kSC + q * 8;
+    if (PK) {
 #pragma unroll
-    for (int t = 0; t < RT; ++t) {
-      const bf16_t* p = a.W + (size_t)(t == 0 ? prow0 : prow1) * K + k;
+      for (int t = 0; t < RT; ++t) {
+        const bf16_t* p =
+            a.Wpk + (((size_t)(t == 0 ? prow0 : prow1) * nsc + kchunk(pci)) * 4 * 64 + lane) * 8;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) dst[t][c] = load_frag_bf16(p + c * 32);
+        for (int c = 0; c < 4; ++c) dst[t][c] = load_frag_bf16(p + c * 512);
+      }
+    } else {
+      const int k = kchunk(pci) * kSC + q * 8;
+#pragma unroll
+      for (int t = 0; t < RT; ++t) {
+        const bf16_t* p = a.W + (size_t)(t == 0 ? prow0 : prow1) * K + k;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) dst[t][c] = load_frag_bf16(p + c * 32);
+      }
     }
     if (++pci == nsc) {
       pci = 0;
@@ -514,7 +533,7 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
   }
 }
 
-template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI, int WV>
+template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI, int WV, bool PK = false>
 void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
   static int per_cu = -1, cus = 0;  // resident blocks per CU at this panel size
   static size_t per_cu_lds = 0;
@@ -524,7 +543,7 @@ void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
     (void)hipGetDevice(&dev);
     (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI, WV>, WV * 64, lds) != hipSuccess)
+            &n, rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI, WV, PK>, WV * 64, lds) != hipSuccess)
       n = 1;
     per_cu = n < 1 ? 1 : n;
   }
@@ -532,7 +551,7 @@ void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
   const int unit = 8 * a.groups;
   const int want = (cus > 0 ? cus : 256) * per_cu;
   const int grid = ((want + unit - 1) / unit) * unit;
-  DLAUNCH((rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI, WV>), dim3(grid), dim3(WV * 64), lds,
+  DLAUNCH((rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI, WV, PK>), dim3(grid), dim3(WV * 64), lds,
           st, a);
 }
 
@@ -542,7 +561,7 @@ size_t persist_lds(int K, int cols, bool split) {
 }
 
 // gcols: activation columns per group (at most NB * 16)
-template <int NB, int RT, int D, bool SPLIT, int EPI, int WV>
+template <int NB, int RT, int D, bool SPLIT, int EPI, int WV, bool PK = false>
 void launch_persist(StreamArgs a, int gcols, hipStream_t st) {
   a.gcols = gcols;
   a.groups = (a.ncols + gcols - 1) / gcols;
@@ -553,9 +572,9 @@ void launch_persist(StreamArgs a, int gcols, hipStream_t st) {
                             (reinterpret_cast<uintptr_t>(a.base_k) & 15) == 0)
                          : (reinterpret_cast<uintptr_t>(a.out) & 15) == 0);
   if (vec)
-    launch_persist_t<NB, RT, D, true, SPLIT, EPI, WV>(a, lds, st);
+    launch_persist_t<NB, RT, D, true, SPLIT, EPI, WV, PK>(a, lds, st);
   else
-    launch_persist_t<NB, RT, D, false, SPLIT, EPI, WV>(a, lds, st);
+    launch_persist_t<NB, RT, D, false, SPLIT, EPI, WV, PK>(a, lds, st);
 }
 
 template <int NB, int RT, bool SPLIT, int EPI, int D>
@@ -615,13 +634,20 @@ constexpr int kArgmaxD = 2;
 constexpr int kArgmaxWV1 = 4;  // waves per block, groups of up to 16 requests
 constexpr int kArgmaxWV2 = 8;  // waves per block, 32-request groups (one block per CU)
 void dispatch_argmax(StreamArgs a, hipStream_t st) {
+  const bool pk = a.Wpk != nullptr;
   if (a.ncols <= 16 && persist_fits<kArgmaxD>(a.K, a.ncols, true)) {
-    launch_persist<1, kArgmaxRT, kArgmaxD, true, kEpiArgmax, kArgmaxWV1>(a, a.ncols, st);
+    if (pk)
+      launch_persist<1, kArgmaxRT, kArgmaxD, true, kEpiArgmax, kArgmaxWV1, true>(a, a.ncols, st);
+    else
+      launch_persist<1, kArgmaxRT, kArgmaxD, true, kEpiArgmax, kArgmaxWV1>(a, a.ncols, st);
   } else if (a.ncols <= 16) {
     a.KS = pick_slice(a.K, a.ncols, 2, 32 * 1024);
     launch_t<1, 2, true, kEpiArgmax, 2>(a, st);
   } else if (persist_fits<kArgmaxD>(a.K, 32, true)) {
-    launch_persist<2, kArgmaxRT, kArgmaxD, true, kEpiArgmax, kArgmaxWV2>(a, 32, st);
+    if (pk)
+      launch_persist<2, kArgmaxRT, kArgmaxD, true, kEpiArgmax, kArgmaxWV2, true>(a, 32, st);
+    else
+      launch_persist<2, kArgmaxRT, kArgmaxD, true, kEpiArgmax, kArgmaxWV2>(a, 32, st);
   } else {
     a.KS = pick_slice(a.K, min(a.ncols, 64), 2, 32 * 1024);
     launch_t<4, 2, true, kEpiArgmax, 2>(a, st);
@@ -661,7 +687,35 @@ void dispatch_union(StreamArgs a, int ubound, hipStream_t st) {
       a, union_lds(a.K, a.ncols, ubound), st);
 }
 
+// W [N, K] in tile order: for 16-row tile T, super-chunk s (128 k), slice c
+// (32 k) and lane l, the 8 elements lane l of a 16x16x32 product reads (row
+// 16 T + l % 16, k = 128 s + 32 c + 8 (l / 16)) sit at (((T nsc + s) 4 + c)
+// 64 + l) 8.  Rows past N repeat row N - 1 (their results are masked).  One
+// thread per 16-byte piece.
+__global__ __launch_bounds__(256) void pack_tiles_kernel(const bf16_t* __restrict__ W, int N,
+                                                         int K, bf16_t* __restrict__ out,
+                                                         size_t pieces) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= pieces) return;
+  const int nsc = K / kSC;
+  const int l = (int)(t & 63), c = (int)((t >> 6) & 3);
+  const size_t ts = t >> 8;
+  const int sc = (int)(ts % nsc);
+  const size_t T = ts / nsc;
+  const size_t R = min(T * 16 + (size_t)(l & 15), (size_t)N - 1);
+  const bf16_t* src = W + R * K + sc * kSC + c * 32 + (l >> 4) * 8;
+  *reinterpret_cast<uint4*>(out + t * 8) = *reinterpret_cast<const uint4*>(src);
+}
+
 }  // namespace
+
+size_t packed_tiles_elems(int N, int K) { return (size_t)(N + 15) / 16 * 16 * K; }
+
+void launch_pack_tiles(const uint16_t* W, int N, int K, uint16_t* out, hipStream_t st) {
+  const size_t pieces = packed_tiles_elems(N, K) / 8;
+  hipLaunchKernelGGL(pack_tiles_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
+                     (const bf16_t*)W, N, K, (bf16_t*)out, pieces);
+}
 
 bool rowstream_supported(int K, int ncols) { return K % kSC == 0 && ncols >= 1 && ncols <= 128; }
 
@@ -690,15 +744,19 @@ void rowstream_prepare() {
   SET(7, 1, false, kEpiStore, 2); SET(8, 1, false, kEpiStore, 2);
   SET(1, 2, true, kEpiArgmax, 2); SET(4, 2, true, kEpiArgmax, 2);
 #undef SET
-#define SETP(NB, RT, D, VEC, SP, EP, WV)                                                         \
-  (void)hipFuncSetAttribute((const void*)rowpersist_kernel<NB, RT, D, VEC, SP, EP, WV>,          \
+#define SETP(NB, RT, D, VEC, SP, EP, WV, ...)                                                   \
+  (void)hipFuncSetAttribute((const void*)rowpersist_kernel<NB, RT, D, VEC, SP, EP, WV, ##__VA_ARGS__>, \
                             hipFuncAttributeMaxDynamicSharedMemorySize, kPersistBudget)
   SETP(1, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax, kArgmaxWV1);
   SETP(1, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax, kArgmaxWV1);
   SETP(2, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax, kArgmaxWV2);
   SETP(2, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax, kArgmaxWV2);
+  SETP(1, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax, kArgmaxWV1, true);
+  SETP(1, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax, kArgmaxWV1, true);
+  SETP(2, kArgmaxRT, kArgmaxD, true, true, kEpiArgmax, kArgmaxWV2, true);
+  SETP(2, kArgmaxRT, kArgmaxD, false, true, kEpiArgmax, kArgmaxWV2, true);
   (void)hipFuncSetAttribute(
-      (const void*)rowpersist_kernel<2, kArgmaxRT, kArgmaxD, false, true, kEpiUnion, kArgmaxWV2>,
+      (const void*)rowpersist_kernel<2, kArgmaxRT, kArgmaxD, false, true, kEpiUnion, kArgmaxWV2, false>,
       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kUnionLdsLimit);
 #undef SETP
 }

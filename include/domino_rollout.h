@@ -106,8 +106,11 @@ typedef struct domino_rollout domino_rollout_t;
  * forms, once, the GRU input projection of every vocabulary id,
  * G[v, :] = gru_w_ih · embed[v, :] ([V, 3g] fp32, 1.9 GB at V = 151936,
  * g = 1024), so that a GRU update reads one row of G instead of multiplying
- * gru_w_ih by an embedding row; this is why embed and gru_w_ih must not change
- * while the handle lives.  create() synchronises the device.  On success
+ * gru_w_ih by an embedding row, and keeps repacked copies of [fc1_w; gru_w_hh]
+ * (8.4 MB at g = r = 1024) and, when max_batch > 16, of fc2_w (311 MB at
+ * V = 151936, r = 1024) in the order the matrix cores read them.  This is why
+ * these weights must not change while the handle lives.  create()
+ * synchronises the device.  On success
  * *out owns the handle; on failure *out is NULL and the status says why
  * (domino_rollout_last_error(NULL) holds the message). */
 domino_status_t domino_rollout_create(const domino_config_t* cfg, const domino_weights_t* w,
