@@ -931,8 +931,94 @@ __global__ __launch_bounds__(256) void correct_pool_split_kernel(PoolArgs<true> 
   if (lane == 0) publish_max(&a.slot_k[b], best);
 }
 
+// bf16 pool correction with whole-line loads, for small batches: one wave
+// per 16 candidates of one request.  Lane l reads elements 512 p + 8 l .. +7
+// of every candidate's fc2 row (one 16-byte load per 512-wide piece p), so a
+// load instruction covers 1 KB of one row, eight whole 128-byte lines, where
+// a matrix-core fragment would touch sixteen rows at 64 bytes each.  The dots
+// are fp32 FMAs of the bf16 weights against u in fp32 (the work is tiny:
+// 2 r flops per candidate); a transposed butterfly finishes all 16 dots of a
+// wave with 17 shuffles, leaving candidate (l >> 2) & 15 in lanes 4i..4i+3.
+// The epilogue operands (the candidate's id, base logit and bias) are loaded
+// before the weights arrive.
+template <int NP>
+__global__ __launch_bounds__(256) void correct_pool_lines_kernel(PoolArgs<true> a) {
+  const int lane = threadIdx.x & 63;
+  const int K = a.K, r = a.r;
+  const int tiles = (K + 15) / 16;
+  const int unit = blockIdx.x * 4 + wave_index();
+  const int b = unit / tiles;
+  if (b >= a.B) return;  // no barrier in this kernel
+  const int tile = unit - b * tiles;
+  const int32_t* ids = a.pool_ids + (size_t)b * K;
+  // the id of candidate lane % 16 (row addresses), and of this lane's result row
+  const int myid = min(max(ids[min(tile * 16 + (lane & 15), K - 1)], 0), a.V - 1);
+  const int rr = (lane >> 2) & 15, ridx = tile * 16 + rr;
+  const int rid = min(max(ids[min(ridx, K - 1)], 0), a.V - 1);
+  const float rbase = a.pool_base_k[(size_t)b * K + min(ridx, K - 1)];
+  const float rbias = bf16_to_f32(a.b2[rid]);
+  float uf[NP][8];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int k = 512 * p + 8 * lane;
+    const bool ok = k < r;
+    const F8 v = load8_f32(a.u + (size_t)b * r + (ok ? k : 0));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) uf[p][e] = ok ? v.v[e] : 0.f;
+  }
+  uint4 w[16][NP];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const bf16_t* row = a.F2 + (size_t)__shfl(myid, i, 64) * r;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int k = 512 * p + 8 * lane;
+      w[i][p] = *reinterpret_cast<const uint4*>(row + (k < r ? k : 0));  // masked by uf = 0
+    }
+  }
+  float d[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float acc = 0.f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t x[4] = {w[i][p].x, w[i][p].y, w[i][p].z, w[i][p].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(__uint_as_float(x[e] << 16), uf[p][2 * e], acc);
+        acc = fmaf(__uint_as_float(x[e] & 0xFFFF0000u), uf[p][2 * e + 1], acc);
+      }
+    }
+    d[i] = acc;
+  }
+  // transposed butterfly: after the step over lane bit m, a lane keeps the
+  // half of its values whose row index has that bit equal to its own
+  const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8, h2 = lane & 4;
+  float e8[8], e4[4], e2[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    e8[j] = (h5 ? d[8 + j] : d[j]) + __shfl_xor(h5 ? d[j] : d[8 + j], 32, 64);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    e4[j] = (h4 ? e8[4 + j] : e8[j]) + __shfl_xor(h4 ? e8[j] : e8[4 + j], 16, 64);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    e2[j] = (h3 ? e4[2 + j] : e4[j]) + __shfl_xor(h3 ? e4[j] : e4[2 + j], 8, 64);
+  float dot = (h2 ? e2[1] : e2[0]) + __shfl_xor(h2 ? e2[0] : e2[1], 4, 64);
+  dot += __shfl_xor(dot, 2, 64);
+  dot += __shfl_xor(dot, 1, 64);
+  const float y = rbase + (dot + rbias);
+  uint64_t best = (ridx < K) ? pack_key(y, (uint32_t)rid) : 0ull;
+  best = wave_max_u64(best);
+  if (lane == 0) publish_max(&a.slot_k[b], best);
+}
+
 constexpr int kPoolRT = 2;
 constexpr int kPoolSplitMaxBatch = 16;
+// The whole-line gather serves up to this many requests.  Measured at the 8B
+// shapes, K = 2048 (us per correction, whole lines / fragments): B = 1 5.6 /
+// 6.1, 2 8.3 / 8.1, 4 11.8 / 13.6, 8 16.8 / 21.0, 12 21.2 / 26.0, 16 43.9 / 33.3.
+constexpr int kPoolLinesMaxBatch = 12;
 
 // Above the small-batch split kernel, bf16 pools can be corrected by
 // streaming each request group's union of pool rows once through the
@@ -979,7 +1065,16 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
     return;
   }
   // small batches are latency bound: spread each request's pool over many workgroups
-  if (s.bf16 && B <= kPoolSplitMaxBatch && s.r % 32 == 0 && s.r <= 32 * 4 * 12) {
+  if (s.bf16 && B <= kPoolLinesMaxBatch && s.r <= 512 * 3) {
+    PoolArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,
+                     ws.u_lo, slot_k, B, K, s.r, s.V, upr};
+    const dim3 g4((unsigned)((B * tiles + 3) / 4));
+    switch ((s.r + 511) / 512) {
+      case 1: DLAUNCH((correct_pool_lines_kernel<1>), g4, dim3(256), 0, st, a); break;
+      case 2: DLAUNCH((correct_pool_lines_kernel<2>), g4, dim3(256), 0, st, a); break;
+      default: DLAUNCH((correct_pool_lines_kernel<3>), g4, dim3(256), 0, st, a); break;
+    }
+  } else if (s.bf16 && B <= kPoolSplitMaxBatch && s.r % 32 == 0 && s.r <= 32 * 4 * 12) {
     PoolArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,
                      ws.u_lo, slot_k, B, K, s.r, s.V, upr};
     const dim3 g2((unsigned)(B * tiles));

@@ -159,6 +159,28 @@ def test_step_paths(shape_name, B):
             assert np.array_equal(t[b, :first_bad[b]], results[0][b, :first_bad[b]])
 
 
+# projector width 1280: three 512-wide pieces per row in the whole-line pool gather, the last half masked
+R1280 = synth.custom_shape(1031, 256, 128, 128, 1280, "bf16", 82, name="small-bf16-r1280")
+
+
+@pytest.mark.parametrize("shape_name,B,K", [("small", 1, 50), ("small", 12, 300), ("r1280", 1, 64),
+                                            ("r1280", 7, 300), ("r1280", 12, 1000)])
+def test_pool_gather_widths(shape_name, B, K):
+    """The per-request pool gather for up to 12 requests (whole-line loads,
+    fp32 dots) at projector widths below one piece (128: lanes 16..63 idle)
+    and of two and a half pieces (1280), against the oracle."""
+    shape = {"small": SMALL, "r1280": R1280}[shape_name]
+    G.log(f"[gpu-test] pool gather {shape_name} B={B} K={K}")
+    tok, top, h = G.gpu_run(shape, B, 1100 + B, 0, K, max_batch=12, max_k=1000, scales_key=STRONG)
+    ref = G.oracle_run(shape, B, 1100 + B, 0, K, scales_key=STRONG)
+    c, _ = compare(tok, top, ref, TOL["bf16"])
+    compare(tok, top, ref, TOL["bf16"], margin_min=TIGHT_MARGIN)
+    assert c > 0
+    ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
+    for b in range(B):
+        assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
+
+
 def test_step_path_rejects_unknown_values():
     h = G.handle(SMALL, 64, 2048, STRONG)
     for bad in (-1, 4):
