@@ -293,8 +293,8 @@ __global__ void reset_kernel(uint64_t* slots, int nslots, uint32_t* hist, int nh
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < nhist; j += stride) hist[j] = 0;
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < nslots; j += stride) slots[j] = 0;
   for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < B; j += stride) {
-    state[2 * j] = 0;
-    state[2 * j + 1] = (uint32_t)K;
+    state[8 * j] = 0;  // radix state 0: empty prefix, rank K
+    state[8 * j + 1] = (uint32_t)K;
     bad[j] = 0;
   }
 }
@@ -381,15 +381,67 @@ __global__ __launch_bounds__(256) void pool_score_hist_kernel(const float* __res
     if (h[i]) atomicAdd(&hh[i], h[i]);
 }
 
+// The radix state of request b after s selections sits at state[8 b + 2 s]
+// (key prefix so far) and state[8 b + 2 s + 1] (rank of the K-th key among
+// the keys with that prefix); s = 0 is (0, K), set by the reset kernel.
+
+// Block-wide (256 threads): the bin of pass PASS (histogram hh) that holds
+// the need-th largest key with the current prefix; returns the extended
+// prefix and the rank left inside that bin.  Exactly one bin qualifies, so
+// one thread writes res; every thread returns the result.
+template <int PASS>
+__device__ __forceinline__ uint2 select_bin(const uint32_t* __restrict__ hh, uint32_t prefix,
+                                            uint32_t need, int* lds, uint32_t* res) {
+  constexpr int NBINS = PASS < 2 ? 2048 : 1024;
+  constexpr int PER = NBINS / 256;
+  constexpr int BITS = PASS < 2 ? 11 : 10;
+  // thread 0 holds the highest PER bins, thread 255 the lowest
+  const int lo_bin = NBINS - (threadIdx.x + 1) * PER;
+  uint32_t c[PER];
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    c[j] = hh[lo_bin + j];
+    tot += (int)c[j];
+  }
+  uint32_t above = (uint32_t)block_excl_scan_256(tot, lds, nullptr);
+#pragma unroll
+  for (int j = PER - 1; j >= 0; --j) {
+    if (above < need && above + c[j] >= need) {
+      res[0] = (prefix << BITS) | (uint32_t)(lo_bin + j);
+      res[1] = need - above;
+    }
+    above += c[j];
+  }
+  __syncthreads();
+  return make_uint2(res[0], res[1]);
+}
+
+// Histogram pass PASS of the keys of request blockIdx.y in one chunk of ids.
+// Passes 1 and 2 first repeat the previous pass's selection in every
+// workgroup (from its finished histogram) instead of in a launch of its own;
+// the chunk-0 workgroup records the new state for the next kernel.
 template <int PASS>
 __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restrict__ keys, int V,
-                                                        const uint32_t* __restrict__ state,
+                                                        uint32_t* __restrict__ state,
                                                         uint32_t* __restrict__ hist) {
   constexpr int NBINS = PASS < 2 ? 2048 : 1024;
   __shared__ uint32_t h[NBINS];
+  __shared__ int lds[4];
+  __shared__ uint32_t res[2];
   const int b = blockIdx.y;
-  const uint32_t prefix = state[2 * b];
   for (int i = threadIdx.x; i < NBINS; i += 256) h[i] = 0;
+  uint32_t prefix = 0;
+  if (PASS > 0) {
+    uint32_t* sb = state + 8 * b + 2 * (PASS - 1);
+    const uint2 ns = select_bin<PASS - 1>(hist + ((size_t)b * 3 + PASS - 1) * 2048, sb[0], sb[1],
+                                          lds, res);
+    prefix = ns.x;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      sb[2] = ns.x;
+      sb[3] = ns.y;
+    }
+  }
   __syncthreads();
   const int v0 = blockIdx.x * kPoolChunk;
 #pragma unroll
@@ -412,45 +464,22 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
     if (h[i]) atomicAdd(&hh[i], h[i]);
 }
 
-// One workgroup per request: find the bin holding the remaining-th largest
-// key, extend the prefix by the bin and subtract the keys in higher bins.
-template <int PASS>
-__global__ __launch_bounds__(256) void pool_select_kernel(const uint32_t* __restrict__ hist,
-                                                          uint32_t* __restrict__ state) {
-  constexpr int NBINS = PASS < 2 ? 2048 : 1024;
-  constexpr int PER = NBINS / 256;
-  constexpr int BITS = PASS < 2 ? 11 : 10;
-  __shared__ int lds[4];
-  const int b = blockIdx.x;
-  const uint32_t prefix = state[2 * b];
-  const uint32_t need = state[2 * b + 1];
-  const uint32_t* hh = hist + ((size_t)b * 3 + PASS) * 2048;
-  // thread 0 holds the highest PER bins, thread 255 the lowest
-  const int lo_bin = NBINS - (threadIdx.x + 1) * PER;
-  uint32_t c[PER];
-  int tot = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    c[j] = hh[lo_bin + j];
-    tot += (int)c[j];
-  }
-  uint32_t above = (uint32_t)block_excl_scan_256(tot, lds, nullptr);
-#pragma unroll
-  for (int j = PER - 1; j >= 0; --j) {
-    if (above < need && above + c[j] >= need) {
-      state[2 * b] = (prefix << BITS) | (uint32_t)(lo_bin + j);
-      state[2 * b + 1] = need - above;
-    }
-    above += c[j];
-  }
-}
-
+// Keys above and equal to the threshold per chunk, after the last selection
+// (repeated in every workgroup, recorded by chunk 0's as state 3).
 __global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restrict__ keys, int V,
-                                                         const uint32_t* __restrict__ state,
+                                                         uint32_t* __restrict__ state,
+                                                         const uint32_t* __restrict__ hist,
                                                          uint32_t* __restrict__ counts, int nch) {
   __shared__ int lds[4];
+  __shared__ uint32_t res[2];
   const int b = blockIdx.y;
-  const uint32_t T = state[2 * b];
+  uint32_t* sb = state + 8 * b + 4;
+  const uint2 ns = select_bin<2>(hist + ((size_t)b * 3 + 2) * 2048, sb[0], sb[1], lds, res);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    sb[2] = ns.x;
+    sb[3] = ns.y;
+  }
+  const uint32_t T = ns.x;
   const int v0 = blockIdx.x * kPoolChunk;
   int gt = 0, eq = 0;
 #pragma unroll
@@ -478,8 +507,8 @@ __global__ __launch_bounds__(256) void pool_compact_kernel(
     uint32_t* __restrict__ umask) {
   __shared__ int lds[4];
   const int b = blockIdx.y, chunk = blockIdx.x;
-  const uint32_t T = state[2 * b];
-  const int need = (int)state[2 * b + 1];
+  const uint32_t T = state[8 * b + 6];
+  const int need = (int)state[8 * b + 7];
   int gt_b = 0, eq_b = 0;
   for (int c = threadIdx.x; c < chunk; c += 256) {
     gt_b += (int)counts[((size_t)b * nch + c) * 2];
@@ -633,6 +662,17 @@ __global__ __launch_bounds__(256) void union_members_kernel(
   for (int t = 0; t < DOMINO_S; ++t) mb[((size_t)t * 2 + g) * mstride + slot] = vals[t];
 }
 
+// The whole-line pool gather (correct_pool_lines_kernel) serves bf16 models
+// up to this many requests, when the pool is not read as group unions.
+// Measured at the 8B shapes, K = 2048 (us per correction, whole lines /
+// fragments): B = 1 5.6 / 6.1, 2 8.3 / 8.1, 4 11.8 / 13.6, 8 16.8 / 21.0,
+// 12 21.2 / 26.0, 16 43.9 / 33.3.  It reads each candidate's base logit from
+// the step's base row itself, so the build skips the base-value gather.
+constexpr int kPoolLinesMaxBatch = 12;
+static bool pool_lines(const Shape& s, int B) {
+  return s.bf16 && B <= kPoolLinesMaxBatch && s.r <= 512 * 3;
+}
+
 void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
                        bool keys_ready, hipStream_t st) {
   const int nch = (s.V + kPoolChunk - 1) / kPoolChunk;
@@ -641,12 +681,9 @@ void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, i
     DLAUNCH(pool_hist_kernel<0>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
   else
     DLAUNCH(pool_score_hist_kernel, grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
-  DLAUNCH(pool_select_kernel<0>, dim3(B), blk, 0, st, ws.hist, ws.state);
   DLAUNCH(pool_hist_kernel<1>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
-  DLAUNCH(pool_select_kernel<1>, dim3(B), blk, 0, st, ws.hist, ws.state);
   DLAUNCH(pool_hist_kernel<2>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
-  DLAUNCH(pool_select_kernel<2>, dim3(B), blk, 0, st, ws.hist, ws.state);
-  DLAUNCH(pool_count_kernel, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.counts, nch);
+  DLAUNCH(pool_count_kernel, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, ws.counts, nch);
   const bool uni = pool_union(s, ws, B, K);
   DLAUNCH(pool_compact_kernel, grid, blk, 0, st, ws.keys, s.V, K, ws.state, ws.counts, nch,
           ws.pool_ids, uni ? ws.umask : nullptr);
@@ -657,7 +694,7 @@ void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, i
             ws.ucounts, nch, ws.urec, ws.uidx, ws.un, ws.umax);
     DLAUNCH(union_members_kernel, dim3((B * K + 255) / 256), blk, 0, st, ws.pool_ids, ws.base, B,
             K, s.V, ws.uidx, ws.urec, ws.umax, ws.mb, ws.mstride);
-  } else {
+  } else if (!pool_lines(s, B)) {  // the whole-line gather reads base rows itself
     const size_t n = (size_t)B * K * DOMINO_S;
     DLAUNCH(pool_gather_kernel, dim3((unsigned)((n + 255) / 256)), blk, 0, st, ws.pool_ids,
             ws.base, s.V, B, K, ws.pool_base);
@@ -822,6 +859,7 @@ struct PoolArgs {
   const uint16_t* u_lo;
   uint64_t* slot_k;
   int B, K, r, V, units_per_req;
+  const float* base_k;       // [B, V] base row of step k (whole-line gather)
 };
 
 template <bool BF, int RT>
@@ -939,8 +977,8 @@ __global__ __launch_bounds__(256) void correct_pool_split_kernel(PoolArgs<true> 
 // are fp32 FMAs of the bf16 weights against u in fp32 (the work is tiny:
 // 2 r flops per candidate); a transposed butterfly finishes all 16 dots of a
 // wave with 17 shuffles, leaving candidate (l >> 2) & 15 in lanes 4i..4i+3.
-// The epilogue operands (the candidate's id, base logit and bias) are loaded
-// before the weights arrive.
+// The epilogue operands (the candidate's id, then its base logit, read from
+// the step's base row, and its bias) are loaded before the weights arrive.
 template <int NP>
 __global__ __launch_bounds__(256) void correct_pool_lines_kernel(PoolArgs<true> a) {
   const int lane = threadIdx.x & 63;
@@ -955,7 +993,7 @@ __global__ __launch_bounds__(256) void correct_pool_lines_kernel(PoolArgs<true> 
   const int myid = min(max(ids[min(tile * 16 + (lane & 15), K - 1)], 0), a.V - 1);
   const int rr = (lane >> 2) & 15, ridx = tile * 16 + rr;
   const int rid = min(max(ids[min(ridx, K - 1)], 0), a.V - 1);
-  const float rbase = a.pool_base_k[(size_t)b * K + min(ridx, K - 1)];
+  const float rbase = a.base_k[(size_t)b * a.V + rid];
   const float rbias = bf16_to_f32(a.b2[rid]);
   float uf[NP][8];
 #pragma unroll
@@ -1015,10 +1053,7 @@ __global__ __launch_bounds__(256) void correct_pool_lines_kernel(PoolArgs<true> 
 
 constexpr int kPoolRT = 2;
 constexpr int kPoolSplitMaxBatch = 16;
-// The whole-line gather serves up to this many requests.  Measured at the 8B
-// shapes, K = 2048 (us per correction, whole lines / fragments): B = 1 5.6 /
-// 6.1, 2 8.3 / 8.1, 4 11.8 / 13.6, 8 16.8 / 21.0, 12 21.2 / 26.0, 16 43.9 / 33.3.
-constexpr int kPoolLinesMaxBatch = 12;
+
 
 // Above the small-batch split kernel, bf16 pools can be corrected by
 // streaming each request group's union of pool rows once through the
@@ -1065,9 +1100,10 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
     return;
   }
   // small batches are latency bound: spread each request's pool over many workgroups
-  if (s.bf16 && B <= kPoolLinesMaxBatch && s.r <= 512 * 3) {
+  if (pool_lines(s, B)) {
     PoolArgs<true> a{(const bf16_t*)w.fc2, (const bf16_t*)w.fc2_b, pb, ws.pool_ids, ws.u, ws.u_hi,
                      ws.u_lo, slot_k, B, K, s.r, s.V, upr};
+    a.base_k = ws.base + (size_t)k * B * s.V;
     const dim3 g4((unsigned)((B * tiles + 3) / 4));
     switch ((s.r + 511) / 512) {
       case 1: DLAUNCH((correct_pool_lines_kernel<1>), g4, dim3(256), 0, st, a); break;

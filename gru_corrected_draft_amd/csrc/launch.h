@@ -42,7 +42,7 @@ struct Workspace {
   float* base;         // [15, Bmax, V] step-major base logits
   uint32_t* keys;      // [Bmax, V] orderable pool scores
   uint32_t* hist;      // [Bmax, 3, 2048] radix histograms
-  uint32_t* state;     // [Bmax, 2] (prefix, remaining count)
+  uint32_t* state;     // [Bmax, 4, 2] radix state (prefix, remaining count) after 0..3 selections
   uint32_t* counts;    // [Bmax, nchunks, 2] (greater, equal) per chunk
   int32_t* pool_ids;   // [Bmax, Kmax]
   float* pool_base;    // [14, Bmax, Kmax]

@@ -206,7 +206,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   ws.base = (float*)alloc(DOMINO_T * Bm * V * 4);
   ws.keys = (uint32_t*)alloc(Bm * V * 4);
   ws.hist = (uint32_t*)alloc(Bm * 3 * 2048 * 4);
-  ws.state = (uint32_t*)alloc(Bm * 2 * 4);
+  ws.state = (uint32_t*)alloc(Bm * 8 * 4);
   ws.counts = (uint32_t*)alloc(Bm * nch * 2 * 4);
   ws.pool_ids = (int32_t*)alloc(Bm * Km * 4);
   ws.pool_base = (float*)alloc(DOMINO_S * Bm * Km * 4);
