@@ -40,7 +40,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic(shape, B, K, union_sizes=None):
+def algorithmic(shape, B, K, union_sizes=None, proposals=15):
     """Algorithmic bytes / flops per launch of each kernel class (the unit
     figures of the design notes times the units one launch processes).
     union_sizes: rows of each request group's pool union when the pool
@@ -60,9 +60,17 @@ def algorithmic(shape, B, K, union_sizes=None):
         correct_bytes = V * r * wb + V * wb + B * V * 4 + B * r * 4
     lm_bytes = V * H * wb + B * 15 * H * wb + 15 * B * V * 4
     lm_flops = 2.0 * 15 * B * H * V
-    gru_bytes = 3 * g * (e + g) * wb + B * (e * wb + 2 * g * 4)
+    # GRU update + projector layer 1 of one correction step: the stacked
+    # [fc1; W_hh] rows once, the gate inputs (row G[token], c = W_hh h, h),
+    # the new h and c, u with its bf16 planes and s; the last step has no
+    # W_hh rows and no c.  Average per step launch over the P - 1 steps.
+    gates_in = B * (3 * g * 4 + 3 * g * 4 + g * 4)
+    full = (r + 3 * g) * g * wb + gates_in + B * (g * 4 + 3 * g * 4 + r * (4 + 2 + 2) + r * 4)
+    last = r * g * wb + gates_in + B * (g * 4 + r * (4 + 2 + 2) + r * 4)
+    nsteps = max(proposals - 1, 1)
+    step_bytes = ((nsteps - 1) * full + last) / nsteps
     return {"correct_bytes": correct_bytes, "lm_bytes": lm_bytes, "lm_flops": lm_flops,
-            "gru_bytes": gru_bytes}
+            "step_bytes": step_bytes}
 
 
 def kernel_source_digest():
@@ -229,7 +237,7 @@ def main():
             union_sizes = h.read_workspace(3).cpu().tolist()
         except R.DominoError:
             union_sizes = None
-    alg = algorithmic(shape, B, K, union_sizes)
+    alg = algorithmic(shape, B, K, union_sizes, P)
     digest = kernel_source_digest()
     corr_ms = avg["correct"]
     lm_ms = avg["lmhead"]
@@ -259,6 +267,13 @@ def main():
     roof["launch_ms"] = round(dominant_ms, 5)
     phases = {k: {"ms_per_launch": round(v, 5), "launches_per_block": kt[k][1] // args.steps}
               for k, v in avg.items() if v}
+    # achieved algorithmic bandwidth of the HBM-bound phases (the step product
+    # is latency bound: ~8 MB per launch against a few-microsecond launch)
+    for k, nbytes in (("correct", alg["correct_bytes"]), ("step", alg["step_bytes"])):
+        if k in phases:
+            gbs = nbytes / (avg[k] * 1e-3) / 1e9
+            phases[k]["alg_gb_s"] = round(gbs, 1)
+            phases[k]["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
 
     line = {
         "metric": f"Domino rollout ms/block ({P} proposals)",
