@@ -88,10 +88,11 @@ def test_small_bf16_ragged_rollout(B, K):
 DEEP = synth.custom_shape(3001, 1024, 256, 256, 256, "bf16", 78, name="small-bf16-deep")
 
 
-@pytest.mark.parametrize("B,K", [(8, 0), (3, 50), (8, 200)])
+@pytest.mark.parametrize("B,K", [(8, 0), (3, 50), (8, 200), (1, 0), (1, 50), (1, 3001)])
 def test_lmhead_with_many_activation_slices(B, K):
     """H = 1024 at B = 8 streams the LM-head against eight 128-wide slices of
-    the 120-column activation panel (an odd super-chunk count per slice)."""
+    the 120-column activation panel (an odd super-chunk count per slice); at
+    B = 1 the single-request stream, first-proposal kernel and scoring pass."""
     G.log(f"[gpu-test] deep hidden B={B} K={K}")
     tok, top, h = G.gpu_run(DEEP, B, 700 + B, 0, K, max_batch=64, max_k=2048)
     ref = G.oracle_run(DEEP, B, 700 + B, 0, K)
@@ -99,6 +100,10 @@ def test_lmhead_with_many_activation_slices(B, K):
     base = h.read_workspace(0).cpu().numpy().reshape(15, B, -1)
     want = ref_base(DEEP, B, 700 + B, 0)
     assert np.max(np.abs(base - want)) < 1e-4
+    if 0 < K < DEEP.vocab:
+        ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
+        for b in range(B):
+            assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
 
 
 WIDE = synth.custom_shape(2053, 256, 512, 512, 512, "bf16", 79, name="small-bf16-wide")
