@@ -88,11 +88,14 @@ def test_small_bf16_ragged_rollout(B, K):
 DEEP = synth.custom_shape(3001, 1024, 256, 256, 256, "bf16", 78, name="small-bf16-deep")
 
 
-@pytest.mark.parametrize("B,K", [(8, 0), (3, 50), (8, 200), (1, 0), (1, 50), (1, 3001)])
+@pytest.mark.parametrize("B,K", [(8, 0), (3, 50), (8, 200), (1, 0), (1, 50), (1, 3001), (40, 0),
+                                 (40, 200), (64, 100)])
 def test_lmhead_with_many_activation_slices(B, K):
     """H = 1024 at B = 8 streams the LM-head against eight 128-wide slices of
     the 120-column activation panel (an odd super-chunk count per slice); at
-    B = 1 the single-request stream, first-proposal kernel and scoring pass."""
+    B = 1 the single-request stream, first-proposal kernel and scoring pass;
+    above 24 requests the line-copy GEMM (16 stages of 64, a ragged last
+    vocabulary tile, a partial last request group at B = 40)."""
     G.log(f"[gpu-test] deep hidden B={B} K={K}")
     tok, top, h = G.gpu_run(DEEP, B, 700 + B, 0, K, max_batch=64, max_k=2048)
     ref = G.oracle_run(DEEP, B, 700 + B, 0, K)
