@@ -356,6 +356,10 @@ __device__ __forceinline__ int block_sum_256(int v, int* lds) {
   return t;
 }
 
+// The pool kernels take chunks of F * kPoolChunk ids per workgroup: larger
+// chunks for larger batches, where the per-workgroup cost (clearing and
+// flushing the bins, repeating the selection) would otherwise dominate.
+template <int F>
 __global__ __launch_bounds__(256) void pool_score_hist_kernel(const float* __restrict__ base, int V,
                                                               int B, uint32_t* __restrict__ keys,
                                                               uint32_t* __restrict__ hist) {
@@ -363,9 +367,9 @@ __global__ __launch_bounds__(256) void pool_score_hist_kernel(const float* __res
   const int b = blockIdx.y;
   for (int i = threadIdx.x; i < 2048; i += 256) h[i] = 0;
   __syncthreads();
-  const int v0 = blockIdx.x * kPoolChunk;
+  const int v0 = blockIdx.x * F * kPoolChunk;
 #pragma unroll
-  for (int j = 0; j < kPoolChunk / 256; ++j) {
+  for (int j = 0; j < F * kPoolChunk / 256; ++j) {
     const int v = v0 + j * 256 + threadIdx.x;
     if (v < V) {
       float sc = base[(size_t)b * V + v];
@@ -421,7 +425,7 @@ __device__ __forceinline__ uint2 select_bin(const uint32_t* __restrict__ hh, uin
 // Passes 1 and 2 first repeat the previous pass's selection in every
 // workgroup (from its finished histogram) instead of in a launch of its own;
 // the chunk-0 workgroup records the new state for the next kernel.
-template <int PASS>
+template <int PASS, int F>
 __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restrict__ keys, int V,
                                                         uint32_t* __restrict__ state,
                                                         uint32_t* __restrict__ hist) {
@@ -443,9 +447,9 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
     }
   }
   __syncthreads();
-  const int v0 = blockIdx.x * kPoolChunk;
+  const int v0 = blockIdx.x * F * kPoolChunk;
 #pragma unroll
-  for (int j = 0; j < kPoolChunk / 256; ++j) {
+  for (int j = 0; j < F * kPoolChunk / 256; ++j) {
     const int v = v0 + j * 256 + threadIdx.x;
     if (v < V) {
       const uint32_t key = keys[(size_t)b * V + v];
@@ -466,6 +470,7 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
 
 // Keys above and equal to the threshold per chunk, after the last selection
 // (repeated in every workgroup, recorded by chunk 0's as state 3).
+template <int F>
 __global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restrict__ keys, int V,
                                                          uint32_t* __restrict__ state,
                                                          const uint32_t* __restrict__ hist,
@@ -480,10 +485,10 @@ __global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restr
     sb[3] = ns.y;
   }
   const uint32_t T = ns.x;
-  const int v0 = blockIdx.x * kPoolChunk;
+  const int v0 = blockIdx.x * F * kPoolChunk;
   int gt = 0, eq = 0;
 #pragma unroll
-  for (int j = 0; j < kPoolChunk / 256; ++j) {
+  for (int j = 0; j < F * kPoolChunk / 256; ++j) {
     const int v = v0 + j * 256 + threadIdx.x;
     if (v < V) {
       const uint32_t key = keys[(size_t)b * V + v];
@@ -500,7 +505,10 @@ __global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restr
 }
 
 // umask (or nullptr): the selected ids also set their request's bit in the
-// member mask of its group (union stream)
+// member mask of its group (union stream).  A workgroup walks its chunk in
+// sub-chunks of kPoolChunk ids, four consecutive ids per thread, so the scan
+// order is the id order.
+template <int F>
 __global__ __launch_bounds__(256) void pool_compact_kernel(
     const uint32_t* __restrict__ keys, int V, int K, const uint32_t* __restrict__ state,
     const uint32_t* __restrict__ counts, int nch, int32_t* __restrict__ pool_ids,
@@ -509,47 +517,55 @@ __global__ __launch_bounds__(256) void pool_compact_kernel(
   const int b = blockIdx.y, chunk = blockIdx.x;
   const uint32_t T = state[8 * b + 6];
   const int need = (int)state[8 * b + 7];
-  int gt_b = 0, eq_b = 0;
+  int gt_b = 0, eq_b = 0;  // keys above / equal to the threshold before this sub-chunk
   for (int c = threadIdx.x; c < chunk; c += 256) {
     gt_b += (int)counts[((size_t)b * nch + c) * 2];
     eq_b += (int)counts[((size_t)b * nch + c) * 2 + 1];
   }
   gt_b = block_sum_256(gt_b, lds);
   eq_b = block_sum_256(eq_b, lds);
-  // four consecutive ids per thread keep the scan order equal to id order
-  const int v0 = chunk * kPoolChunk + threadIdx.x * 4;
-  bool isgt[4], iseq[4];
-  int my_eq = 0;
+#pragma unroll 1
+  for (int f = 0; f < F; ++f) {
+    const int v0 = (chunk * F + f) * kPoolChunk + threadIdx.x * 4;
+    bool isgt[4], iseq[4];
+    int my_eq = 0, my_gt = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int v = v0 + j;
-    uint32_t key = 0;
-    const bool ok = v < V;
-    if (ok) key = keys[(size_t)b * V + v];
-    isgt[j] = ok && key > T;
-    iseq[j] = ok && key == T;
-    my_eq += iseq[j];
-  }
-  const int eq_before = eq_b + block_excl_scan_256(my_eq, lds, nullptr);
-  bool sel[4];
-  int my_sel = 0, e = eq_before;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    sel[j] = isgt[j] || (iseq[j] && e < need);
-    e += iseq[j];
-    my_sel += sel[j];
-  }
-  int pos = gt_b + min(eq_b, need) + block_excl_scan_256(my_sel, lds, nullptr);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (!sel[j]) continue;
-    const int v = v0 + j;
-    if (pos < K) {
-      pool_ids[(size_t)b * K + pos] = v;
-      if (umask)
-        atomicOr(&umask[(size_t)(b / kUnionGroup) * V + v], 1u << (b % kUnionGroup));
+    for (int j = 0; j < 4; ++j) {
+      const int v = v0 + j;
+      uint32_t key = 0;
+      const bool ok = v < V;
+      if (ok) key = keys[(size_t)b * V + v];
+      isgt[j] = ok && key > T;
+      iseq[j] = ok && key == T;
+      my_eq += iseq[j];
+      my_gt += isgt[j];
     }
-    ++pos;
+    int eq_sub = 0;
+    const int eq_before = eq_b + block_excl_scan_256(my_eq, lds, &eq_sub);
+    bool sel[4];
+    int my_sel = 0, e = eq_before;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sel[j] = isgt[j] || (iseq[j] && e < need);
+      e += iseq[j];
+      my_sel += sel[j];
+    }
+    int pos = gt_b + min(eq_b, need) + block_excl_scan_256(my_sel, lds, nullptr);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!sel[j]) continue;
+      const int v = v0 + j;
+      if (pos < K) {
+        pool_ids[(size_t)b * K + pos] = v;
+        if (umask)
+          atomicOr(&umask[(size_t)(b / kUnionGroup) * V + v], 1u << (b % kUnionGroup));
+      }
+      ++pos;
+    }
+    if (F > 1) {
+      gt_b += block_sum_256(my_gt, lds);
+      eq_b += eq_sub;
+    }
   }
 }
 
@@ -673,20 +689,34 @@ static bool pool_lines(const Shape& s, int B) {
   return s.bf16 && B <= kPoolLinesMaxBatch && s.r <= 512 * 3;
 }
 
-void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
-                       bool keys_ready, hipStream_t st) {
-  const int nch = (s.V + kPoolChunk - 1) / kPoolChunk;
+template <int F>
+static void pool_select_passes(const Shape& s, const Workspace& ws, int B, int K, bool keys_ready,
+                               bool uni, hipStream_t st) {
+  const int nch = (s.V + F * kPoolChunk - 1) / (F * kPoolChunk);
   const dim3 grid(nch, B), blk(256);
   if (keys_ready)
-    DLAUNCH(pool_hist_kernel<0>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+    DLAUNCH((pool_hist_kernel<0, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
   else
-    DLAUNCH(pool_score_hist_kernel, grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
-  DLAUNCH(pool_hist_kernel<1>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
-  DLAUNCH(pool_hist_kernel<2>, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
-  DLAUNCH(pool_count_kernel, grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, ws.counts, nch);
-  const bool uni = pool_union(s, ws, B, K);
-  DLAUNCH(pool_compact_kernel, grid, blk, 0, st, ws.keys, s.V, K, ws.state, ws.counts, nch,
+    DLAUNCH((pool_score_hist_kernel<F>), grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
+  DLAUNCH((pool_hist_kernel<1, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+  DLAUNCH((pool_hist_kernel<2, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+  DLAUNCH((pool_count_kernel<F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, ws.counts,
+          nch);
+  DLAUNCH((pool_compact_kernel<F>), grid, blk, 0, st, ws.keys, s.V, K, ws.state, ws.counts, nch,
           ws.pool_ids, uni ? ws.umask : nullptr);
+}
+
+void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
+                       bool keys_ready, hipStream_t st) {
+  const int nch = (s.V + kPoolChunk - 1) / kPoolChunk;  // union kernels: kPoolChunk ids per chunk
+  const dim3 blk(256);
+  const bool uni = pool_union(s, ws, B, K);
+  if (B >= kPoolChunk4MinBatch)
+    pool_select_passes<4>(s, ws, B, K, keys_ready, uni, st);
+  else if (B >= kPoolChunk2MinBatch)
+    pool_select_passes<2>(s, ws, B, K, keys_ready, uni, st);
+  else
+    pool_select_passes<1>(s, ws, B, K, keys_ready, uni, st);
   if (uni) {
     const dim3 ug(nch, (B + kUnionGroup - 1) / kUnionGroup);
     DLAUNCH(union_count_kernel, ug, blk, 0, st, ws.umask, s.V, ws.ucounts, nch);

@@ -87,6 +87,10 @@ constexpr int kPackedStreamMinBatch = 17;
 constexpr int kUnionGroup = 32;
 
 constexpr int kPoolChunk = 1024;
+// pool selection passes take 4 x or 2 x kPoolChunk ids per workgroup from
+// these batch sizes on
+constexpr int kPoolChunk4MinBatch = 32;
+constexpr int kPoolChunk2MinBatch = 16;
 
 // streaming row kernel (stream.hip)
 struct StreamArgs {
