@@ -367,14 +367,21 @@ __global__ __launch_bounds__(256) void pool_score_hist_kernel(const float* __res
   const int b = blockIdx.y;
   for (int i = threadIdx.x; i < 2048; i += 256) h[i] = 0;
   __syncthreads();
+  // every load is issued at a clamped address before any is used (a load
+  // guarded by a divergent branch makes the compiler wait after each one)
   const int v0 = blockIdx.x * F * kPoolChunk;
 #pragma unroll
   for (int j = 0; j < F * kPoolChunk / 256; ++j) {
     const int v = v0 + j * 256 + threadIdx.x;
+    const int vc = min(v, V - 1);
+    float x[DOMINO_T];
+#pragma unroll
+    for (int t = 0; t < DOMINO_T; ++t) x[t] = base[((size_t)t * B + b) * V + vc];
+    float sc = x[0];
+#pragma unroll
+    for (int t = 1; t < DOMINO_T; ++t) sc = fmaxf(sc, x[t]);
+    const uint32_t key = orderable(sc);
     if (v < V) {
-      float sc = base[(size_t)b * V + v];
-      for (int t = 1; t < DOMINO_T; ++t) sc = fmaxf(sc, base[((size_t)t * B + b) * V + v]);
-      const uint32_t key = orderable(sc);
       keys[(size_t)b * V + v] = key;
       atomicAdd(&h[key >> 21], 1u);
     }
@@ -434,6 +441,13 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
   __shared__ int lds[4];
   __shared__ uint32_t res[2];
   const int b = blockIdx.y;
+  // all key loads first, at clamped addresses (see pool_score_hist_kernel),
+  // so they are in flight during the selection
+  constexpr int NL = F * kPoolChunk / 256;
+  const int v0 = blockIdx.x * F * kPoolChunk;
+  uint32_t kv[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) kv[j] = keys[(size_t)b * V + min(v0 + j * 256 + (int)threadIdx.x, V - 1)];
   for (int i = threadIdx.x; i < NBINS; i += 256) h[i] = 0;
   uint32_t prefix = 0;
   if (PASS > 0) {
@@ -447,19 +461,16 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
     }
   }
   __syncthreads();
-  const int v0 = blockIdx.x * F * kPoolChunk;
 #pragma unroll
-  for (int j = 0; j < F * kPoolChunk / 256; ++j) {
-    const int v = v0 + j * 256 + threadIdx.x;
-    if (v < V) {
-      const uint32_t key = keys[(size_t)b * V + v];
-      if (PASS == 0) {
-        atomicAdd(&h[key >> 21], 1u);
-      } else if (PASS == 1) {
-        if ((key >> 21) == prefix) atomicAdd(&h[(key >> 10) & 2047u], 1u);
-      } else {
-        if ((key >> 10) == prefix) atomicAdd(&h[key & 1023u], 1u);
-      }
+  for (int j = 0; j < NL; ++j) {
+    const bool ok = v0 + j * 256 + (int)threadIdx.x < V;
+    const uint32_t key = kv[j];
+    if (PASS == 0) {
+      if (ok) atomicAdd(&h[key >> 21], 1u);
+    } else if (PASS == 1) {
+      if (ok && (key >> 21) == prefix) atomicAdd(&h[(key >> 10) & 2047u], 1u);
+    } else {
+      if (ok && (key >> 10) == prefix) atomicAdd(&h[key & 1023u], 1u);
     }
   }
   __syncthreads();
@@ -478,6 +489,11 @@ __global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restr
   __shared__ int lds[4];
   __shared__ uint32_t res[2];
   const int b = blockIdx.y;
+  constexpr int NL = F * kPoolChunk / 256;
+  const int v0 = blockIdx.x * F * kPoolChunk;
+  uint32_t kv[NL];  // issued before the selection, which they do not depend on
+#pragma unroll
+  for (int j = 0; j < NL; ++j) kv[j] = keys[(size_t)b * V + min(v0 + j * 256 + (int)threadIdx.x, V - 1)];
   uint32_t* sb = state + 8 * b + 4;
   const uint2 ns = select_bin<2>(hist + ((size_t)b * 3 + 2) * 2048, sb[0], sb[1], lds, res);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -485,16 +501,12 @@ __global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restr
     sb[3] = ns.y;
   }
   const uint32_t T = ns.x;
-  const int v0 = blockIdx.x * F * kPoolChunk;
   int gt = 0, eq = 0;
 #pragma unroll
-  for (int j = 0; j < F * kPoolChunk / 256; ++j) {
-    const int v = v0 + j * 256 + threadIdx.x;
-    if (v < V) {
-      const uint32_t key = keys[(size_t)b * V + v];
-      gt += key > T;
-      eq += key == T;
-    }
+  for (int j = 0; j < NL; ++j) {
+    const bool ok = v0 + j * 256 + (int)threadIdx.x < V;
+    gt += ok && kv[j] > T;
+    eq += ok && kv[j] == T;
   }
   gt = block_sum_256(gt, lds);
   eq = block_sum_256(eq, lds);
@@ -529,14 +541,14 @@ __global__ __launch_bounds__(256) void pool_compact_kernel(
     const int v0 = (chunk * F + f) * kPoolChunk + threadIdx.x * 4;
     bool isgt[4], iseq[4];
     int my_eq = 0, my_gt = 0;
+    uint32_t kv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kv[j] = keys[(size_t)b * V + min(v0 + j, V - 1)];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int v = v0 + j;
-      uint32_t key = 0;
-      const bool ok = v < V;
-      if (ok) key = keys[(size_t)b * V + v];
-      isgt[j] = ok && key > T;
-      iseq[j] = ok && key == T;
+      const bool ok = v0 + j < V;
+      isgt[j] = ok && kv[j] > T;
+      iseq[j] = ok && kv[j] == T;
       my_eq += iseq[j];
       my_gt += isgt[j];
     }
@@ -603,7 +615,8 @@ __global__ __launch_bounds__(256) void union_count_kernel(const uint32_t* __rest
 #pragma unroll
   for (int j = 0; j < kPoolChunk / 256; ++j) {
     const int v = v0 + j * 256 + threadIdx.x;
-    const uint32_t m = v < V ? umask[(size_t)g * V + v] : 0u;
+    const uint32_t mv = umask[(size_t)g * V + min(v, V - 1)];  // clamped: issued unconditionally
+    const uint32_t m = v < V ? mv : 0u;
     rows += m != 0u;
     mem += __popc(m);
   }
