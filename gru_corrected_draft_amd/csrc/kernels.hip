@@ -672,7 +672,8 @@ __global__ __launch_bounds__(256) void union_compact_kernel(
 }
 
 // base logits of steps 1..14 at every member, in the group's slot order,
-// read straight from the base logits (all 14 loads issued before the stores)
+// read straight from the base logits (all 14 loads issued with the row
+// index, before the record that depends on it)
 __global__ __launch_bounds__(256) void union_members_kernel(
     const int32_t* __restrict__ pool_ids, const float* __restrict__ base, int B, int K, int V,
     const int32_t* __restrict__ uidx, const uint4* __restrict__ urec, int umax,
@@ -682,10 +683,13 @@ __global__ __launch_bounds__(256) void union_members_kernel(
   const int b = idx / K;
   const int g = b / kUnionGroup, bl = b % kUnionGroup;
   const int v = pool_ids[idx];
+  // the row index and the 14 base values in one round trip, then the record
+  const int ui = uidx[(size_t)g * V + v];
   float vals[DOMINO_S];
 #pragma unroll
   for (int t = 0; t < DOMINO_S; ++t) vals[t] = base[((size_t)(t + 1) * B + b) * V + v];
-  const uint4 rc = urec[(size_t)g * umax + uidx[(size_t)g * V + v]];
+  __builtin_amdgcn_sched_barrier(0);
+  const uint4 rc = urec[(size_t)g * umax + ui];
   const uint32_t slot = rc.z + __popc(rc.w & ((1u << bl) - 1u));
 #pragma unroll
   for (int t = 0; t < DOMINO_S; ++t) mb[((size_t)t * 2 + g) * mstride + slot] = vals[t];
