@@ -203,6 +203,11 @@ __global__ __launch_bounds__(256) void step_rows_kernel(StepArgs a) {
   const int R0 = Rg + wave * kRowsPerWave;
   const bf16_t* wrow = R0 < r ? (const bf16_t*)a.F1 + (size_t)R0 * g
                               : (const bf16_t*)a.W_hh + (size_t)(R0 - r) * g;
+  // Issue order: the weights, then the tokens (uniform scalar loads, which
+  // drain on their own counter, so they do not wait for the weights), the
+  // projector offsets and the gate inputs.  Vector loads drain in order: a
+  // vector load waited on before the gates would hold them until every
+  // weight had landed, so the offsets go to LDS only just before the barrier.
   uint2 w[kRowsPerWave][IG];
 #pragma unroll
   for (int q = 0; q < kRowsPerWave; ++q)
@@ -212,17 +217,22 @@ __global__ __launch_bounds__(256) void step_rows_kernel(StepArgs a) {
       // a lane past the row's end reads the row's first elements and is zeroed below
       w[q][it] = *reinterpret_cast<const uint2*>(wrow + (size_t)q * g + (k < g ? k : 0));
     }
-  if (Rg < r && threadIdx.x < NBR * kRowsPerGroup) {
+  __builtin_amdgcn_sched_barrier(0);
+  int toks[NBR];
+  if (GATES) {
+#pragma unroll
+    for (int b = 0; b < NBR; ++b)
+      toks[b] = step_token(a, min(b, B - 1), blockIdx.x == 0 && threadIdx.x == 0 && b < B);
+  }
+  float sv = 0.f;
+  const bool s_lane = Rg < r && threadIdx.x < NBR * kRowsPerGroup;
+  if (s_lane) {
     const int b = threadIdx.x / kRowsPerGroup, rr = threadIdx.x % kRowsPerGroup;
-    ssh[b][rr] = a.s[((size_t)min(b, B - 1) * DOMINO_S + a.step) * r + Rg + rr];
+    sv = a.s[((size_t)min(b, B - 1) * DOMINO_S + a.step) * r + Rg + rr];
   }
 
   const int ncol = g / 4;
   if (GATES) {
-    int toks[NBR];
-#pragma unroll
-    for (int b = 0; b < NBR; ++b)
-      toks[b] = step_token(a, min(b, B - 1), blockIdx.x == 0 && threadIdx.x == 0 && b < B);
     for (int col = threadIdx.x; col < ncol; col += 256) {
       float4 v[NBR];
 #pragma unroll
@@ -241,6 +251,7 @@ __global__ __launch_bounds__(256) void step_rows_kernel(StepArgs a) {
     for (int i = threadIdx.x; i < B * ncol; i += 256)
       reinterpret_cast<float4*>(hs)[i] = ld4(a.h_new + (size_t)i * 4);
   }
+  if (s_lane) ssh[threadIdx.x / kRowsPerGroup][threadIdx.x % kRowsPerGroup] = sv;
   __syncthreads();
 
   float wf[kRowsPerWave][IG][4];
