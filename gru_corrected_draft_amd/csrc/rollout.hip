@@ -49,7 +49,7 @@ struct GraphEntry {
 };
 
 constexpr int kPhases = 7;
-enum Phase { kLmHead = 0, kCorrect = 1, kGru = 2, kFc1 = 3, kPool = 4, kArgmax0 = 5, kOffsets = 6 };
+enum Phase { kLmHead = 0, kCorrect = 1, kGru = 2, kStep = 3, kPool = 4, kArgmax0 = 5, kOffsets = 6 };
 
 }  // namespace
 
@@ -481,7 +481,7 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
     sa.step = k - 1;
     sa.row0 = 0;
     sa.nrows = k < steps ? sh.r + 3 * sh.g : sh.r;  // no W_hh after the last step
-    step_launches(kGru, kFc1);
+    step_launches(kGru, kStep);
     cur ^= 1;
     {
       PhaseTimer t(h, kCorrect, st);
