@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--pool-strategy", type=int, default=0, choices=(0, 1, 2),
                     help="pool correction at 17-64 requests: 0 automatic, 1 per-request "
                          "gather, 2 group unions")
+    ap.add_argument("--flushed", action="store_true",
+                    help="also time replays one by one after streaming 512 MB (cold memory-side cache)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -217,6 +219,41 @@ def main():
     wall_ms = (time.perf_counter() - t_wall) * 1e3
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
+    assert torch.equal(out_t, ref_tokens), "graph replays disagree"
+
+    # spread: rounds of back-to-back replays (median, p10, p90 of the
+    # per-block time of each round), outside the timed region
+    rounds = []
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            h.run(hid, s, ver, K, out_tokens=out_t, out_top1=out_l, graph=True, proposals=prop)
+        e1.record()
+        torch.cuda.synchronize()
+        rounds.append(e0.elapsed_time(e1) / 20)
+    spread = {"rounds": 5, "replays_per_round": 20,
+              "median_ms": round(float(np.median(rounds)), 4),
+              "p10_ms": round(float(np.percentile(rounds, 10)), 4),
+              "p90_ms": round(float(np.percentile(rounds, 90)), 4)}
+    flushed = None
+    if args.flushed:
+        # each replay timed alone after streaming 512 MB, so the memory-side
+        # cache holds none of the weights the block reads
+        junk = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        per = []
+        for _ in range(20):
+            junk.add_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            h.run(hid, s, ver, K, out_tokens=out_t, out_top1=out_l, graph=True, proposals=prop)
+            e1.record()
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1))
+        del junk
+        flushed = {"replays": 20, "median_ms": round(float(np.median(per)), 4),
+                   "p10_ms": round(float(np.percentile(per, 10)), 4),
+                   "p90_ms": round(float(np.percentile(per, 90)), 4)}
     assert torch.equal(out_t, ref_tokens), "graph replays disagree"
 
     # per-kernel durations: HIP events stamped by each kernel's dispatch, eager runs, same stream
@@ -301,6 +338,8 @@ def main():
         "roofline": roof,
         "phases": phases,
         "wall_ms_per_step": round(wall_ms / args.steps, 4),
+        "spread": spread,
+        **({"flushed": flushed} if flushed else {}),
         "kernel_source_digest": digest,
     }
     if not args.no_cpu_baseline:

@@ -636,6 +636,28 @@ def test_full_size_rollout(name, K):
     assert checked > 0
 
 
+@pytest.mark.parametrize("name,K", [("8b_b64", 0), ("8b_b64", 2048), ("27b_b64", 2048)])
+def test_full_size_teacher_forced(name, K):
+    """Every step's winning logit at full size, whatever the chain: the GPU
+    consumes the oracle's own proposals (teacher forcing), so each step is an
+    independent argmax of the same inputs on both sides; tokens must agree
+    wherever the oracle's top-2 margin is at least 2e-3."""
+    wl = synth.WORKLOADS[name]
+    shape = synth.MODELS[wl.model]
+    free = G.oracle_run(wl.model, wl.batch, wl.input_seed, 0, K)
+    forced = np.asarray(free["tokens"], np.int32)
+    G.log(f"[gpu-test] {name} K={K} teacher forced")
+    tok, top, _ = G.gpu_run(wl.model, wl.batch, wl.input_seed, 0, K, max_batch=64, max_k=2048,
+                            forced=forced)
+    ref = G.oracle_run(wl.model, wl.batch, wl.input_seed, 0, K,
+                       forced_key=tuple(forced.reshape(-1).tolist()))
+    err = compare_forced(top, ref, TOL[shape.dtype])
+    ok = ref["margin"] >= TIGHT_MARGIN
+    assert np.array_equal(tok[ok], ref["tokens"][ok])
+    G.log(f"[gpu-test] {name} K={K} forced: {int(ok.sum())} of {ok.size} steps decisive, "
+          f"max top-1 error {err:.3g}")
+
+
 def _check_full_size_intermediates(h, wl, shape, trial, K, tok, ref):
     B, V = wl.batch, shape.vocab
     base = h.read_workspace(0).cpu().numpy().reshape(15, B, V)
