@@ -82,18 +82,23 @@ def kernel_source_digest():
     return h.hexdigest()[:16]
 
 
-def read_traffic(kernel, workload, digest):
-    """HBM bytes per launch recorded from rocprofv3 counters, if they were
-    taken on the current kernel sources (else None)."""
+def read_counter(kernel, workload, digest, field="hbm_bytes_per_launch"):
+    """A figure recorded from rocprofv3 counters (HBM bytes per launch, or
+    the matrix-core busy fraction), if they were taken on the current kernel
+    sources (else None)."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_d = re.search(r"kernel_source_digest:\s*([0-9a-f]+)", text)
-    m_t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_t = re.search(field + r":\s*([0-9.eE+]+)", text)
     if not m_d or not m_t or m_d.group(1) != digest:
         return None
     return float(m_t.group(1))
+
+
+def read_traffic(kernel, workload, digest):
+    return read_counter(kernel, workload, digest)
 
 
 def cpu_baseline(w, shape, B, K, input_seed, budget_s, proposals=None, in_library_s=False):
@@ -292,6 +297,9 @@ def main():
             roof = {"bound": "hbm", "kernel": "lmhead_gemm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
         roof["traffic"] = read_traffic("lmhead", f"{args.workload}_k{K}", digest)
+        if lm_bound_mfma:  # rocprofv3 MfmaUtil of the same kernel, when recorded
+            roof["mfma_util_counter"] = read_counter("lmhead", f"{args.workload}_k{K}", digest,
+                                                     "mfma_util")
         dominant_ms = lm_ms
     else:
         achieved = alg["correct_bytes"] / (corr_ms * 1e-3) / 1e9
