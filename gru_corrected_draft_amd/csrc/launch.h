@@ -50,6 +50,7 @@ struct Workspace {
   float* c[2];         // [Bmax, 3g] W_hh h of the matching state
   uint16_t* Wp;        // stacked [fc1; W_hh] in fragment order (bf16 models)
   uint16_t* hp;        // new state in fragment order, hi/lo bf16 (bf16 models)
+  uint16_t* xp;        // the block's hiddens in fragment order for the LM-head above 24 requests
   uint16_t* fc2p;      // fc2 in tile order for the full-vocabulary stream (bf16, r % 128 == 0,
                        // max_batch >= kPackedStreamMinBatch)
   float* G;            // [V, 3g] GRU input projection of every id (built at create)
@@ -198,6 +199,7 @@ struct FusedArgs {
   uint32_t* keys;      // [B, V] orderable max over the block, or nullptr
   uint64_t* slots;     // argmax words of position 0 [B]
   int V, H, B;
+  uint16_t* XP;        // workspace for the hiddens in fragment order (lmhead_xfrag_elems), or nullptr
 };
 // A single request streams lm_head once through the row kernel (8B, per
 // block: 1.117 against 1.152 ms fused); from two requests on, the fused
@@ -207,6 +209,12 @@ constexpr int kFusedMinBatch = 2;
 void lmhead_fused_prepare();
 bool lmhead_fused_supported(int H);
 void launch_lmhead_fused(const FusedArgs& a, hipStream_t st);
+// Above 24 requests (H a multiple of 128, request groups of 32 nearly full)
+// the LM-head reads the hiddens from a fragment-ordered copy of
+// lmhead_xfrag_elems(B, H) bf16 elements; possible: for some B <= max_batch.
+bool lmhead_xfrag_used(int B, int H);
+bool lmhead_xfrag_possible(int max_batch, int H);
+size_t lmhead_xfrag_elems(int B, int H);
 
 void launch_reset(const Workspace& ws, int B, int K, hipStream_t st);
 void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int B, hipStream_t st);

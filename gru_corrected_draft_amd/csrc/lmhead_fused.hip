@@ -524,6 +524,228 @@ __global__ __launch_bounds__(256) void lmhead_m32_kernel(FusedArgs a) {
   }
 }
 
+// LM-head above 24 requests: the activations as register operands.
+//
+// A workgroup computes 128 vocabulary rows x 32 requests (512 activation
+// rows, 16 per request: the 15 positions and a padding row that repeats
+// position 14).  Each of its eight waves (two per SIMD) owns 4 requests and
+// all 128 rows: 2 x 4 tiles of 32x32x16 products (128 accumulators).  Only
+// lm_head goes through LDS (whole-line loads into 64-wide k stages with the
+// m32 kernel's chunk swizzle, three stages); each wave reads its activation
+// fragments straight from a copy of the block's hiddens laid out in fragment
+// order (xfrag_pack_kernel, once per call, so every load instruction reads
+// 1 KB of whole lines), through a 4-deep register ring of 32-wide k steps,
+// and the lm_head fragments of each 16-wide slice one slice ahead of its
+// products.  lm_head is staged through registers rather than by direct
+// global->LDS copies: the compiler cannot tell those copies from the
+// fragment loads and would wait for every load in flight before each LDS
+// read.
+//
+// Measured (LM-head ms): 8B B = 64 1.143 (line kernel 1.143), B = 32 0.638
+// (0.644), 27B-class B = 64 1.436 (1.553).  One wave per SIMD with 4 x 4
+// tiles (256 accumulators) ran at 1.30 ms at 8B B = 64.  Counters at 8B
+// B = 64: the matrix cores are busy 56% of the active cycles (line kernel
+// 42%), but the part runs this kernel at ~1.9 GHz against ~2.35 GHz for the
+// line kernel (active cycles per microsecond), so the two take the same time.
+typedef int v4i __attribute__((ext_vector_type(4)));
+// fourth word of a raw buffer resource on gfx9-class parts (32-bit data format)
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kXfRq = 32;                      // requests per workgroup
+constexpr int kXfV = 128;                      // vocabulary rows per workgroup
+constexpr int kXfK = 64;                       // k per LDS stage
+constexpr int kXfRing = 3;                     // LDS stages
+constexpr int kXfA = 4;                        // register ring of 32-wide k steps
+constexpr int kXfTA = 2;                       // activation tiles per wave (8 waves)
+constexpr int kXfStage = kXfV * kXfK * 2;      // 16 KB
+constexpr size_t kXfLds = (size_t)kXfRing * kXfStage;
+
+// XP: activation tile a (32 rows; group a / 16 holds requests 32 (a / 16) ..,
+// row R = 32 (a % 16) + l % 32 is request 32 (a / 16) + R / 16 at position
+// min(R % 16, 14)), 16-wide k slice s, lane l, element e at
+// ((a nk16 + s) 64 + l) 8 + e with k = 16 s + 8 (l / 32) + e.  Requests past
+// B repeat request B - 1 (their results are not stored).
+__host__ __device__ inline size_t lmhead_xfrag_bytes(int B, int H) {
+  return (size_t)((B + kXfRq - 1) / kXfRq) * 16 * 32 * H * 2;
+}
+
+__global__ __launch_bounds__(256) void xfrag_pack_kernel(const bf16_t* __restrict__ X, int B,
+                                                         int H, bf16_t* __restrict__ XP,
+                                                         size_t pieces) {
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= pieces) return;
+  const int nk16 = H / 16;
+  const int l = (int)(t & 63);
+  const size_t ts = t >> 6;
+  const int s = (int)(ts % nk16);
+  const int at = (int)(ts / nk16);
+  const int R = (at % 16) * 32 + (l & 31);
+  const int req = min((at / 16) * kXfRq + R / 16, B - 1), pos = min(R % 16, DOMINO_T - 1);
+  const int k = 16 * s + 8 * (l >> 5);
+  *reinterpret_cast<uint4*>(XP + t * 8) =
+      *reinterpret_cast<const uint4*>(X + ((size_t)req * DOMINO_T + pos) * H + k);
+}
+
+// TA activation tiles (2 TA requests) per wave: 4 (four waves, one per SIMD) or 2 (eight
+// waves, two per SIMD, 128 accumulators each)
+template <int TA>
+__global__ __launch_bounds__(64 * 16 / TA) void lmhead_xf_kernel(FusedArgs a) {
+  constexpr int kW = 16 / TA;  // waves
+  constexpr int kC = 16 / kW;  // lm_head copy blocks per wave and stage
+  const int V = a.V, H = a.H, B = a.B;
+  const int nvt = (V + kXfV - 1) / kXfV, ngrp = (B + kXfRq - 1) / kXfRq;
+  const int j0 = blockIdx.x, xcd = j0 & 7, local = j0 >> 3;
+  const int vt = (local / ngrp) * 8 + xcd, grp = local % ngrp;
+  if (vt >= nvt) return;  // uniform per workgroup, before any barrier
+  const int v0 = vt * kXfV, b0 = grp * kXfRq;
+  extern __shared__ __align__(1024) unsigned char ring[];
+  const int lane = threadIdx.x & 63, wave = wave_index();
+  const int nk16 = H / 16, nst = H / kXfK, nstep = H / 32;
+
+  // lm_head copies: 16 blocks of 8 rows x 128 B per stage, blocks wave + kW i;
+  // lane (rr, pp) fetches logical chunk pp ^ ((r >> 1) & 7) of row rr
+  const int rr = lane >> 3, pp = lane & 7;
+  uint32_t woff[kC];
+#pragma unroll
+  for (int i = 0; i < kC; ++i) {
+    const int blk = wave + kW * i;
+    const int r = (blk & 3) * 8 + rr;
+    const int v = min(v0 + blk * 8 + rr, V - 1);
+    woff[i] = ((uint32_t)v * (uint32_t)H + (uint32_t)(pp ^ ((r >> 1) & 7)) * 8u) * 2u;
+  }
+  // Both operands are read through buffer resources: a wave-uniform byte
+  // offset in a scalar register plus one per-lane offset, so the loads need
+  // no 64-bit address registers.
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.W, (short)0, (int)((uint64_t)V * H * 2), kBufferWord3);
+  v4i VR[kC];  // this wave's part of one lm_head stage on its way to LDS
+  auto load_v = [&](int t) {  // stage t (past the end: the last one again)
+    const int kb = min(t, nst - 1) * (kXfK * 2);
+#pragma unroll
+    for (int i = 0; i < kC; ++i) VR[i] = __builtin_amdgcn_raw_buffer_load_b128(wres, (int)woff[i], kb, 0);
+  };
+  auto store_v = [&](int t) {  // into slot t % ring
+    unsigned char* ws = ring + (t % kXfRing) * kXfStage + lane * 16;
+#pragma unroll
+    for (int i = 0; i < kC; ++i) *reinterpret_cast<v4i*>(ws + (wave + kW * i) * 1024) = VR[i];
+  };
+  // this wave's activation tiles: TA of its group's 16, each 2 H bytes per
+  // row of 32 (1 KB per 16-wide k slice)
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)a.XP, (short)0, (int)(lmhead_xfrag_bytes(B, H)), kBufferWord3);
+  const int xbase = (grp * 16 + wave * TA) * nk16 * 1024, tstride = nk16 * 1024;
+  v8s X[kXfA][TA][2];
+  auto issue_x = [&](v8s (&dst)[TA][2], int j) {  // 32-wide k step j (clamped)
+    const int jc = min(j, nstep - 1);
+#pragma unroll
+    for (int ta = 0; ta < TA; ++ta)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        dst[ta][h] = __builtin_bit_cast(
+            v8s, __builtin_amdgcn_raw_buffer_load_b128(xres, lane * 16,
+                                                       xbase + ta * tstride + (2 * jc + h) * 1024, 0));
+  };
+
+  v16f acc[TA][4];
+#pragma unroll
+  for (int ta = 0; ta < TA; ++ta)
+#pragma unroll
+    for (int tv = 0; tv < 4; ++tv)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[ta][tv][i] = 0.f;
+
+  const int frow = lane & 31, fhi = lane >> 5, fsw = (frow >> 1) & 7;
+  // lm_head fragments of 16-wide slice q (step q / 2, stage q / 4)
+  auto read_v = [&](v8s (&fv)[4], int q) {
+    const unsigned char* vs = ring + ((q >> 2) % kXfRing) * kXfStage + frow * 128;
+    const int cofs = ((2 * (q & 3) + fhi) ^ fsw) * 16;
+#pragma unroll
+    for (int tv = 0; tv < 4; ++tv) fv[tv] = *reinterpret_cast<const v8s*>(vs + tv * 4096 + cofs);
+  };
+  // Step j (32-wide k): load the activations of step j + 3; at even j also
+  // write lm_head stage j / 2 + 1 (loaded two steps earlier) to LDS and load
+  // stage j / 2 + 2; at odd j a barrier makes stage (j + 1) / 2 visible.  A
+  // stage is read from the second half of step 2t - 1 (the fragments of each
+  // 16-wide slice are read one slice ahead of its products) to step 2t + 1;
+  // its slot (three of them) is rewritten at step 2t + 4, after the barrier
+  // at step 2t + 3.  The prologue covers steps -3..-1.
+  load_v(0);
+  store_v(0);
+  issue_x(X[0], 0);
+  issue_x(X[1], 1);
+  load_v(1);  // in the place the loop issues it, so the loop's waits hold from the start
+  issue_x(X[2], 2);
+  __syncthreads();
+  v8s fcur[4];
+  read_v(fcur, 0);
+  for (int j0s = 0; j0s < nstep; j0s += kXfA) {
+#pragma unroll
+    for (int d = 0; d < kXfA; ++d) {
+      const int j = j0s + d;
+      if (d & 1) __syncthreads();
+      // the scheduling barriers keep the loads in issue order, so the wait
+      // for one group never covers a group issued after it
+      __builtin_amdgcn_sched_barrier(0);
+      issue_x(X[(d + 3) % kXfA], j + 3);
+      __builtin_amdgcn_sched_barrier(0);
+      if ((d & 1) == 0) {
+        store_v(j / 2 + 1);
+        load_v(j / 2 + 2);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v8s fnext[4];
+        read_v(fnext, 2 * j + h + 1);
+#pragma unroll
+        for (int ta = 0; ta < TA; ++ta)
+#pragma unroll
+          for (int tv = 0; tv < 4; ++tv) acc[ta][tv] = mfma32(X[d][ta][h], fcur[tv], acc[ta][tv]);
+#pragma unroll
+        for (int tv = 0; tv < 4; ++tv) fcur[tv] = fnext[tv];
+      }
+    }
+  }
+
+  // epilogue: base logits (step-major), pool score keys, first-proposal argmax
+  const int vl = lane & 31, hh = lane >> 5;
+  const int bw = b0 + wave * 2 * TA;  // this wave's first request
+  uint64_t best[2 * TA];
+#pragma unroll
+  for (int r = 0; r < 2 * TA; ++r) best[r] = 0;
+#pragma unroll
+  for (int ta = 0; ta < TA; ++ta)
+#pragma unroll
+    for (int tv = 0; tv < 4; ++tv) {
+      const int v = v0 + tv * 32 + vl;
+      const bool vok = v < V;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int req = bw + 2 * ta + jj;
+        const bool ok = vok && req < B;
+        float m = -INFINITY;
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const int i = jj * 8 + ii;
+          const int pos = 8 * ((i >> 2) & 1) + 4 * hh + (i & 3);
+          const float y = acc[ta][tv][i];
+          if (pos < DOMINO_T) {
+            m = fmaxf(m, y);
+            if (ok) a.base[((size_t)pos * B + req) * V + v] = y;
+          }
+        }
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (a.keys && hh == 0 && ok) a.keys[(size_t)req * V + v] = orderable(m);
+        const uint64_t k0 = pack_key(acc[ta][tv][jj * 8], (uint32_t)v);  // position 0 on hh == 0
+        best[2 * ta + jj] = (hh == 0 && vok) ? umax64(best[2 * ta + jj], k0) : best[2 * ta + jj];
+      }
+    }
+#pragma unroll
+  for (int r = 0; r < 2 * TA; ++r) {
+    const uint64_t m = wave_max_u64(best[r]);
+    if (lane == 0 && bw + r < B) publish_max(&a.slots[bw + r], m);
+  }
+}
+
 // vocabulary tiles per wave by batch: the 128-row workgroup tile doubles the
 // workgroup count where lm_head streaming, not the products, bounds the time
 constexpr int kM32SmallBatch = 8;
@@ -543,6 +765,24 @@ void lmhead_fused_prepare() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   (void)hipFuncSetAttribute((const void*)lmhead_lines_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLinesLds);
+  (void)hipFuncSetAttribute((const void*)lmhead_xf_kernel<kXfTA>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kXfLds);
+}
+
+size_t lmhead_xfrag_elems(int B, int H) { return lmhead_xfrag_bytes(B, H) / 2; }
+
+// Requests are processed in groups of 32, so a partial last group wastes
+// products: taken when the waste is at most an eighth (B = 28-32, 56-64) and
+// otherwise left to the line kernel (B = 48: 1.12 against 0.95 ms).
+bool lmhead_xfrag_used(int B, int H) {
+  const int padded = (B + kXfRq - 1) / kXfRq * kXfRq;
+  return B > kM32MaxBatch && H % 128 == 0 && 8 * (padded - B) <= padded;
+}
+
+bool lmhead_xfrag_possible(int max_batch, int H) {
+  for (int b = kM32MaxBatch + 1; b <= max_batch; ++b)
+    if (lmhead_xfrag_used(b, H)) return true;
+  return false;
 }
 
 bool lmhead_fused_supported(int H) { return H % 32 == 0; }
@@ -562,6 +802,15 @@ void launch_lmhead_fused(const FusedArgs& a, hipStream_t st) {
       DLAUNCH(lmhead_m32_kernel<2>, dim3(8 * ((nvt + 7) / 8) * ngrp), dim3(256), M32<2>::kLds, st,
               a);
     }
+    return;
+  }
+  if (a.XP && lmhead_xfrag_used(a.B, a.H) && offsets32) {
+    const size_t pieces = lmhead_xfrag_elems(a.B, a.H) / 8;
+    DLAUNCH(xfrag_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
+            (const bf16_t*)a.X, a.B, a.H, (bf16_t*)a.XP, pieces);
+    const int nvt = (a.V + kXfV - 1) / kXfV, ngrp = (a.B + kXfRq - 1) / kXfRq;
+    DLAUNCH(lmhead_xf_kernel<kXfTA>, dim3(8 * ((nvt + 7) / 8) * ngrp), dim3(64 * 16 / kXfTA), kXfLds,
+            st, a);
     return;
   }
   const int nvt = (a.V + kBN - 1) / kBN, ngrp = (a.B + kBJ - 1) / kBJ;

@@ -221,7 +221,9 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
     ws.Wp = (uint16_t*)alloc(step_packed_weight_elems((int)g, (int)r) * 2);
     ws.hp = (uint16_t*)alloc((Bm + 15) / 16 * 16 * g * 4);
     if (pack_fc2) ws.fc2p = (uint16_t*)alloc(packed_tiles_elems((int)V, (int)r) * 2);
-    if (!ws.Wp || !ws.hp || (pack_fc2 && !ws.fc2p)) {
+    const bool xfrag = lmhead_xfrag_possible((int)Bm, cfg->hidden);
+    if (xfrag) ws.xp = (uint16_t*)alloc(lmhead_xfrag_elems((int)Bm, cfg->hidden) * 2);
+    if (!ws.Wp || !ws.hp || (pack_fc2 && !ws.fc2p) || (xfrag && !ws.xp)) {
       set_global_err("create: workspace allocation failed");
       domino_rollout_destroy(h);
       return DOMINO_ERR_OUT_OF_MEMORY;
@@ -409,7 +411,7 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
     // base logits, pool-score keys and the first proposal in one pass
     PhaseTimer t(h, kLmHead, st);
     FusedArgs fa{(const uint16_t*)h->w.lm_head, (const uint16_t*)hidden, ws.base,
-                 pool ? ws.keys : nullptr, ws.slots, sh.V, sh.H, B};
+                 pool ? ws.keys : nullptr, ws.slots, sh.V, sh.H, B, ws.xp};
     launch_lmhead_fused(fa, st);
   } else {
     {

@@ -89,13 +89,16 @@ DEEP = synth.custom_shape(3001, 1024, 256, 256, 256, "bf16", 78, name="small-bf1
 
 
 @pytest.mark.parametrize("B,K", [(8, 0), (3, 50), (8, 200), (1, 0), (1, 50), (1, 3001), (40, 0),
-                                 (40, 200), (64, 100)])
+                                 (40, 200), (64, 100), (28, 0), (60, 300)])
 def test_lmhead_with_many_activation_slices(B, K):
     """H = 1024 at B = 8 streams the LM-head against eight 128-wide slices of
     the 120-column activation panel (an odd super-chunk count per slice); at
     B = 1 the single-request stream, first-proposal kernel and scoring pass;
-    above 24 requests the line-copy GEMM (16 stages of 64, a ragged last
-    vocabulary tile, a partial last request group at B = 40)."""
+    above 24 requests the line-copy GEMM at B = 40 (16 stages of 64, a ragged
+    last vocabulary tile, a partial last request group) and the
+    register-operand GEMM at B = 28, 60 and 64 (fragment-ordered hiddens,
+    32-request groups, the last one partial at 28 and 60, a ragged last
+    128-row vocabulary tile)."""
     G.log(f"[gpu-test] deep hidden B={B} K={K}")
     tok, top, h = G.gpu_run(DEEP, B, 700 + B, 0, K, max_batch=64, max_k=2048)
     ref = G.oracle_run(DEEP, B, 700 + B, 0, K)
