@@ -517,14 +517,14 @@ __global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restr
 }
 
 // umask (or nullptr): the selected ids also set their request's bit in the
-// member mask of its group (union stream).  A workgroup walks its chunk in
+// member mask of its group of ug requests (union stream).  A workgroup walks its chunk in
 // sub-chunks of kPoolChunk ids, four consecutive ids per thread, so the scan
 // order is the id order.
 template <int F>
 __global__ __launch_bounds__(256) void pool_compact_kernel(
     const uint32_t* __restrict__ keys, int V, int K, const uint32_t* __restrict__ state,
     const uint32_t* __restrict__ counts, int nch, int32_t* __restrict__ pool_ids,
-    uint32_t* __restrict__ umask) {
+    uint32_t* __restrict__ umask, int ug) {
   __shared__ int lds[4];
   const int b = blockIdx.y, chunk = blockIdx.x;
   const uint32_t T = state[8 * b + 6];
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(256) void pool_compact_kernel(
       if (pos < K) {
         pool_ids[(size_t)b * K + pos] = v;
         if (umask)
-          atomicOr(&umask[(size_t)(b / kUnionGroup) * V + v], 1u << (b % kUnionGroup));
+          atomicOr(&umask[(size_t)(b / ug) * V + v], 1u << (b % ug));
       }
       ++pos;
     }
@@ -582,7 +582,7 @@ __global__ __launch_bounds__(256) void pool_compact_kernel(
 }
 
 // ------------------------------------------------------ pool row unions
-// For each group of kUnionGroup requests, the union of their pools in id
+// For each group of ug requests, the union of their pools in id
 // order: one row per id that some request of the group selected, with the
 // bits of the requests that did.  A row's members take consecutive slots of
 // the group's member arrays (row order, then request order), so the base
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(256) void union_compact_kernel(
   for (int j = 0; j < 4; ++j) {
     if (m[j] == 0u) continue;
     const int v = v0 + j;
-    if (rpos < umax) {  // always: a group's union has at most kUnionGroup * K <= umax rows
+    if (rpos < umax) {  // always: a group's union has at most ug * K <= umax rows
       urec[(size_t)g * umax + rpos] =
           make_uint4((uint32_t)v, __float_as_uint(bf16_to_f32(b2[v])), (uint32_t)mpos, m[j]);
       uidx[(size_t)g * V + v] = rpos;
@@ -677,11 +677,11 @@ __global__ __launch_bounds__(256) void union_compact_kernel(
 __global__ __launch_bounds__(256) void union_members_kernel(
     const int32_t* __restrict__ pool_ids, const float* __restrict__ base, int B, int K, int V,
     const int32_t* __restrict__ uidx, const uint4* __restrict__ urec, int umax,
-    float* __restrict__ mb, int mstride) {
+    float* __restrict__ mb, int mstride, int ug, int ugmax) {
   const int idx = blockIdx.x * 256 + threadIdx.x;
   if (idx >= B * K) return;
   const int b = idx / K;
-  const int g = b / kUnionGroup, bl = b % kUnionGroup;
+  const int g = b / ug, bl = b % ug;
   const int v = pool_ids[idx];
   // the row index and the 14 base values in one round trip, then the record
   const int ui = uidx[(size_t)g * V + v];
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(256) void union_members_kernel(
   const uint4 rc = urec[(size_t)g * umax + ui];
   const uint32_t slot = rc.z + __popc(rc.w & ((1u << bl) - 1u));
 #pragma unroll
-  for (int t = 0; t < DOMINO_S; ++t) mb[((size_t)t * 2 + g) * mstride + slot] = vals[t];
+  for (int t = 0; t < DOMINO_S; ++t) mb[((size_t)t * ugmax + g) * mstride + slot] = vals[t];
 }
 
 // The whole-line pool gather (correct_pool_lines_kernel) serves bf16 models
@@ -720,7 +720,7 @@ static void pool_select_passes(const Shape& s, const Workspace& ws, int B, int K
   DLAUNCH((pool_count_kernel<F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, ws.counts,
           nch);
   DLAUNCH((pool_compact_kernel<F>), grid, blk, 0, st, ws.keys, s.V, K, ws.state, ws.counts, nch,
-          ws.pool_ids, uni ? ws.umask : nullptr);
+          ws.pool_ids, uni ? ws.umask : nullptr, ws.ugroup);
 }
 
 void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
@@ -735,12 +735,12 @@ void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, i
   else
     pool_select_passes<1>(s, ws, B, K, keys_ready, uni, st);
   if (uni) {
-    const dim3 ug(nch, (B + kUnionGroup - 1) / kUnionGroup);
+    const dim3 ug(nch, (B + ws.ugroup - 1) / ws.ugroup);
     DLAUNCH(union_count_kernel, ug, blk, 0, st, ws.umask, s.V, ws.ucounts, nch);
     DLAUNCH(union_compact_kernel, ug, blk, 0, st, ws.umask, (const bf16_t*)fc2_b, s.V,
             ws.ucounts, nch, ws.urec, ws.uidx, ws.un, ws.umax);
     DLAUNCH(union_members_kernel, dim3((B * K + 255) / 256), blk, 0, st, ws.pool_ids, ws.base, B,
-            K, s.V, ws.uidx, ws.urec, ws.umax, ws.mb, ws.mstride);
+            K, s.V, ws.uidx, ws.urec, ws.umax, ws.mb, ws.mstride, ws.ugroup, ws.ugmax);
   } else if (!pool_lines(s, B)) {  // the whole-line gather reads base rows itself
     const size_t n = (size_t)B * K * DOMINO_S;
     DLAUNCH(pool_gather_kernel, dim3((unsigned)((n + 255) / 256)), blk, 0, st, ws.pool_ids,
@@ -1113,13 +1113,13 @@ constexpr int kPoolSplitMaxBatch = 16;
 // latency-bound small-batch gather (B = 16, K = 2048: unions 1.13 against
 // 1.27 ms per block; B = 8: even).
 constexpr long long kUnionMinGatherBytes = 96ll << 20;
-static int union_bound(const Shape& s, int K) {
-  return (int)std::min<long long>(s.V, (long long)kUnionGroup * K);
+static int union_bound(const Shape& s, const Workspace& ws, int K) {
+  return (int)std::min<long long>(s.V, (long long)ws.ugroup * K);
 }
 
 bool pool_union(const Shape& s, const Workspace& ws, int B, int K) {
-  if (!(s.bf16 && ws.umask != nullptr && B <= 2 * kUnionGroup &&
-        rowstream_union_supported(s.r, B, union_bound(s, K))) ||
+  if (!(s.bf16 && ws.umask != nullptr && ws.ugroup > 0 && B <= ws.ugroup * ws.ugmax &&
+        rowstream_union_supported(s.r, B, union_bound(s, ws, K), ws.ugroup)) ||
       ws.pool_strategy == 1)
     return false;
   const long long gather = (long long)B * K * s.r * 2;
@@ -1140,10 +1140,10 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
                  nullptr, nullptr, slot_k, kReverseOddSteps ? (k & 1) : 0};
     a.urec = ws.urec;
     a.un = ws.un;
-    a.mb_k = ws.mb + (size_t)(k - 1) * 2 * ws.mstride;
+    a.mb_k = ws.mb + (size_t)(k - 1) * ws.ugmax * ws.mstride;
     a.ustride = ws.umax;
     a.mstride = ws.mstride;
-    launch_rowstream_union(a, union_bound(s, K), st);
+    launch_rowstream_union(a, union_bound(s, ws, K), ws.ugroup, st);
     return;
   }
   // small batches are latency bound: spread each request's pool over many workgroups

@@ -62,16 +62,18 @@ struct Workspace {
   float* partial;      // split partial tiles of the step product
   float* s_tmp;        // k-split partials of the step-offset product
   float* s;            // [Bmax, 14, r] per-step projector offsets formed in the library
-  // pool rows streamed once per group of kUnionGroup requests (bf16, large batches)
-  uint32_t* umask;     // [2, V] member bits of each id per group; zero between runs
-  uint32_t* ucounts;   // [2, nchunks, 2] (union rows, members) per id chunk
-  uint4* urec;         // [2, Umax] union rows in id order: {id, b2 as float bits,
+  // pool rows streamed once per group of ugroup requests (bf16, large batches)
+  uint32_t* umask;     // [ugmax, V] member bits of each id per group; zero between runs
+  uint32_t* ucounts;   // [ugmax, nchunks, 2] (union rows, members) per id chunk
+  uint4* urec;         // [ugmax, Umax] union rows in id order: {id, b2 as float bits,
                        // first member slot, member bits}
-  int32_t* uidx;       // [2, V] union row of an id (valid for the group's members)
-  int32_t* un;         // [2] union sizes
-  float* mb;           // [14, 2, mstride] base logits of the members, union order
-  int umax;            // Umax: rows per group list, min(V, kUnionGroup * Kmax)
-  int mstride;         // member slots per group, kUnionGroup * Kmax
+  int32_t* uidx;       // [ugmax, V] union row of an id (valid for the group's members)
+  int32_t* un;         // [ugmax] union sizes
+  float* mb;           // [14, ugmax, mstride] base logits of the members, union order
+  int umax;            // Umax: rows per group list, min(V, ugroup * Kmax)
+  int mstride;         // member slots per group, ugroup * Kmax
+  int ugroup;          // requests per union group (at most kUnionGroup; 0: no unions)
+  int ugmax;           // groups at max_batch
   int pool_strategy;   // 0 automatic, 1 per-request gather, 2 group unions where supported
 };
 
@@ -84,7 +86,8 @@ struct Workspace {
 // row-major layout limit that traffic.
 constexpr int kPackedStreamMinBatch = 17;
 
-// requests per union group (one 32-bit member mask per union row)
+// most requests per union group (one 32-bit member mask per union row); a
+// projector too wide for a 32-request panel takes 24 or 16
 constexpr int kUnionGroup = 32;
 
 constexpr int kPoolChunk = 1024;
@@ -129,8 +132,11 @@ void launch_rowstream_store(StreamArgs a, hipStream_t st);
 void launch_rowstream_argmax(StreamArgs a, hipStream_t st);
 // whether the union stream runs for K-wide rows, ncols requests and row
 // lists of at most ubound rows (its 32-request panel and staged records fit)
-bool rowstream_union_supported(int K, int ncols, int ubound);
-void launch_rowstream_union(StreamArgs a, int ubound, hipStream_t st);
+bool rowstream_union_supported(int K, int ncols, int ubound, int group);
+// largest union group (32, 24 or 16 requests) whose stream fits K-wide rows,
+// up to max_batch requests and lists of min(V, group * max_k) rows; 0: none
+int rowstream_union_group(int K, int V, int max_batch, int max_k);
+void launch_rowstream_union(StreamArgs a, int ubound, int group, hipStream_t st);
 
 // GRU update and projector layer 1 of one correction step (gru_step.hip).
 // Stacked rows [fc1 (r rows); W_hh (3g rows)] are multiplied by the new state

@@ -240,16 +240,21 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
                              sizeof(float));
     ws.s = (float*)alloc((size_t)DOMINO_S * Bm * r * sizeof(float));
   }
-  const bool unions = h->shape.bf16;  // pool unions (pool_union())
+  // pool unions (pool_union()): groups of up to 32 requests, fewer when the
+  // projector is too wide for a 32-request panel
+  ws.ugroup = h->shape.bf16 ? rowstream_union_group((int)r, (int)V, (int)Bm, (int)Km) : 0;
+  const bool unions = ws.ugroup > 0;
   if (unions) {
-    ws.umax = (int)std::min<size_t>(V, (size_t)kUnionGroup * Km);
-    ws.mstride = kUnionGroup * (int)Km;
-    ws.umask = (uint32_t*)alloc(2 * V * 4);
-    ws.ucounts = (uint32_t*)alloc(2 * nch * 2 * 4);
-    ws.urec = (uint4*)alloc(2 * (size_t)ws.umax * sizeof(uint4));
-    ws.uidx = (int32_t*)alloc(2 * V * 4);
-    ws.un = (int32_t*)alloc(2 * 4);
-    ws.mb = (float*)alloc((size_t)DOMINO_S * 2 * ws.mstride * 4);
+    const size_t G = (Bm + ws.ugroup - 1) / ws.ugroup;
+    ws.ugmax = (int)G;
+    ws.umax = (int)std::min<size_t>(V, (size_t)ws.ugroup * Km);
+    ws.mstride = ws.ugroup * (int)Km;
+    ws.umask = (uint32_t*)alloc(G * V * 4);
+    ws.ucounts = (uint32_t*)alloc(G * nch * 2 * 4);
+    ws.urec = (uint4*)alloc(G * (size_t)ws.umax * sizeof(uint4));
+    ws.uidx = (int32_t*)alloc(G * V * 4);
+    ws.un = (int32_t*)alloc(G * 4);
+    ws.mb = (float*)alloc((size_t)DOMINO_S * G * ws.mstride * 4);
     if (!ws.umask || !ws.ucounts || !ws.urec || !ws.uidx || !ws.un || !ws.mb) {
       set_global_err("create: workspace allocation failed");
       domino_rollout_destroy(h);
@@ -272,7 +277,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   for (size_t i = 0; i < h->allocations.size(); ++i) {
     if (hipMemset(h->allocations[i], 0, 256) != hipSuccess) break;
   }
-  if ((unions && hipMemset(ws.umask, 0, 2 * V * 4) != hipSuccess) ||
+  if ((unions && hipMemset(ws.umask, 0, (size_t)ws.ugmax * V * 4) != hipSuccess) ||
       (ws.hp && hipMemset(ws.hp, 0, (Bm + 15) / 16 * 16 * g * 4) != hipSuccess) ||
       hipMemset(ws.pool_ids, 0, Bm * Km * 4) != hipSuccess ||
       hipMemset(ws.base, 0, DOMINO_T * Bm * V * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
@@ -627,7 +632,7 @@ extern "C" domino_status_t domino_rollout_read_workspace(const domino_rollout_t*
     n = (size_t)h->last_B * DOMINO_S * h->cfg.proj_dim * 4;
   } else if (which == 3 && h->last_union) {
     src = h->ws.un;
-    n = (size_t)((h->last_B + kUnionGroup - 1) / kUnionGroup) * 4;
+    n = (size_t)((h->last_B + h->ws.ugroup - 1) / h->ws.ugroup) * 4;
   } else {
     return DOMINO_ERR_INVALID_ARG;
   }

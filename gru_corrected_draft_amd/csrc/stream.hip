@@ -16,6 +16,8 @@
 // request (correction, "[Spec] Add Domino projector support to DFlash
 // speculative decoding (V2)", section "Implementation": fused
 // SiLU(z+s)·fc2ᵀ + bias + base_logits followed by the argmax).
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -654,8 +656,8 @@ void dispatch_argmax(StreamArgs a, hipStream_t st) {
   }
 }
 
-// Union stream: groups of 32 requests, each over its own row list of at
-// most `ubound` rows.  Each wave stages the records of its units in LDS
+// Union stream: groups of `group` requests (at most 32), each over its own
+// row list of at most `ubound` rows.  Each wave stages the records of its units in LDS
 // behind the panel; the count per wave is bounded with the smallest grid the
 // launch can choose (one block per CU).
 constexpr size_t kUnionLdsLimit = 156 * 1024;
@@ -674,17 +676,17 @@ int union_units_per_wave(int groups, int ubound) {
   const int waves = parts * kArgmaxWV2;
   return max(1, (units + waves - 1) / waves);
 }
-size_t union_lds(int K, int ncols, int ubound) {
-  const int groups = (ncols + kUnionGroup - 1) / kUnionGroup;
-  return persist_lds(K, min(ncols, kUnionGroup), true) +
+size_t union_lds(int K, int ncols, int ubound, int group) {
+  const int groups = (ncols + group - 1) / group;
+  return persist_lds(K, min(ncols, group), true) +
          (size_t)kArgmaxWV2 * union_units_per_wave(groups, ubound) * kUnionUnitRows * sizeof(uint4);
 }
-void dispatch_union(StreamArgs a, int ubound, hipStream_t st) {
-  a.gcols = kUnionGroup;
-  a.groups = (a.ncols + kUnionGroup - 1) / kUnionGroup;
+void dispatch_union(StreamArgs a, int ubound, int group, hipStream_t st) {
+  a.gcols = group;
+  a.groups = (a.ncols + group - 1) / group;
   a.umaxu = union_units_per_wave(a.groups, ubound);
   launch_persist_t<2, kArgmaxRT, kArgmaxD, false, true, kEpiUnion, kArgmaxWV2>(
-      a, union_lds(a.K, a.ncols, ubound), st);
+      a, union_lds(a.K, a.ncols, ubound, group), st);
 }
 
 // W [N, K] in tile order: for 16-row tile T, super-chunk s (128 k), slice c
@@ -719,13 +721,26 @@ void launch_pack_tiles(const uint16_t* W, int N, int K, uint16_t* out, hipStream
 
 bool rowstream_supported(int K, int ncols) { return K % kSC == 0 && ncols >= 1 && ncols <= 128; }
 
-bool rowstream_union_supported(int K, int ncols, int ubound) {
-  return K % kSC == 0 && (K / kSC) % kArgmaxD == 0 && ncols >= 1 && ncols <= 2 * kUnionGroup &&
-         union_lds(K, ncols, ubound) <= kUnionLdsLimit;
+bool rowstream_union_supported(int K, int ncols, int ubound, int group) {
+  return K % kSC == 0 && (K / kSC) % kArgmaxD == 0 && group >= 1 && group <= kUnionGroup &&
+         ncols >= 1 && ncols <= 64 && union_lds(K, ncols, ubound, group) <= kUnionLdsLimit;
 }
 
-void launch_rowstream_union(StreamArgs a, int ubound, hipStream_t st) {
-  dispatch_union(a, ubound, st);
+int rowstream_union_group(int K, int V, int max_batch, int max_k) {
+  // the staged records grow with the groups' row lists, the panel with the
+  // group: the largest group for which every batch up to max_batch fits
+  for (int group : {32, 24, 16}) {
+    const int ubound = (int)std::min<long long>(V, (long long)group * max_k);
+    bool ok = true;
+    for (int n = 1; n <= std::min(max_batch, 64) && ok; ++n)
+      ok = rowstream_union_supported(K, n, ubound, group);
+    if (ok) return group;
+  }
+  return 0;
+}
+
+void launch_rowstream_union(StreamArgs a, int ubound, int group, hipStream_t st) {
+  dispatch_union(a, ubound, group, st);
 }
 
 void launch_rowstream_store(StreamArgs a, hipStream_t st) { dispatch_store(a, st); }

@@ -212,7 +212,8 @@ class DominoRollout:
         """Copy of a workspace buffer of the last run: 0 = base logits
         [15, B, V] fp32 (step-major), 1 = pool ids [B, K] int32, 2 = the step
         offsets [B, 14, r] fp32 the library formed (runs with step_s=None),
-        3 = the pool union size of each group of 32 requests, int32."""
+        3 = the pool union size of each group of 32 requests (24 or 16 when
+        the projector is too wide for a 32-request panel), int32."""
         import torch
         n = ctypes.c_size_t()
         self._check(self.lib.domino_rollout_read_workspace(self.handle, which, None, 0,

@@ -177,9 +177,10 @@ domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const void* base_
  * least dst_bytes), stream-ordered on `stream`.  which: 0 = base logits fp32
  * [15, batch, V] (step-major), 1 = pool ids int32 [batch, K] sorted
  * ascending (pool runs only), 2 = step_s fp32 [batch, 14, r] as the library
- * computed it (runs with step_s = NULL only), 3 = int32 [ceil(batch / 32)]
- * sizes of the pool unions of each group of 32 requests (pool runs that
- * streamed the unions: bf16 weights, 17 <= batch <= 64).  *bytes receives
+ * computed it (runs with step_s = NULL only), 3 = int32 [ceil(batch / G)]
+ * sizes of the pool unions of each group of G requests (pool runs that
+ * streamed the unions: bf16 weights, batch <= 64; G = 32, or 24 or 16 when a
+ * 32-request panel of u does not fit in LDS, e.g. 24 at r = 1280).  *bytes receives
  * the buffer's size for the last run; with dst == NULL nothing is copied.
  * INVALID_ARG if which is unknown or not available for the last run, no run
  * has happened, or dst_bytes is too small. */
@@ -217,9 +218,9 @@ domino_status_t domino_rollout_set_step_path(domino_rollout_t* h, int32_t path);
  * most 64 requests and the weights are bf16: 0 = automatic (the default:
  * group unions once the per-request gather would read 96 MB or more per step,
  * 48 MB at 16 requests or fewer), 1 = every request gathers its own K rows,
- * 2 = each group of 32 requests streams the union of its pools once (where
- * the projector width allows it: r a multiple of 256 whose 32-request panel
- * fits in LDS; otherwise the gather).  Both score the same candidates; their dot products are summed in
+ * 2 = each group of 32 requests (24 or 16 for projectors too wide for a
+ * 32-request panel in LDS) streams the union of its pools once (where the
+ * projector width allows it: r a multiple of 256; otherwise the gather).  Both score the same candidates; their dot products are summed in
  * different orders, so top-1 values may differ in the last bits.  Changing
  * the strategy waits for the device and drops the handle's cached graphs.
  * INVALID_ARG for any other value.  ("feat: support tensor-parallel Domino

@@ -378,13 +378,44 @@ def test_pool_union_stream(B, K):
     assert c > 0
     for b in range(B):
         assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
-    # each group streamed exactly the union of its requests' pools
-    assert un.shape == ((B + 31) // 32,)
-    for g in range((B + 31) // 32):
+    _check_unions(un, ref, B, 32)
+    assert np.array_equal(tok, tok2) and np.array_equal(top.view(np.uint32), top2.view(np.uint32))
+
+
+def _check_unions(un, ref, B, group):
+    """Each group of `group` requests streamed exactly the union of its
+    requests' pools."""
+    assert un.shape == ((B + group - 1) // group,)
+    for g in range(un.shape[0]):
         want = set()
-        for b in range(32 * g, min(B, 32 * g + 32)):
+        for b in range(group * g, min(B, group * g + group)):
             want.update(ref["pools"][b].tolist())
         assert int(un[g]) == len(want), f"union of group {g}"
+
+
+# r = 1280: a 32-request panel of u (hi and lo planes) does not fit in LDS,
+# so the union groups hold 24 requests (three groups at B = 64)
+PROJ1280 = synth.custom_shape(2053, 256, 128, 128, 1280, "bf16", 82, name="small-bf16-proj1280")
+
+
+@pytest.mark.parametrize("B,K", [(17, 300), (24, 100), (25, 100), (48, 2048), (64, 300)])
+def test_pool_union_groups_of_24(B, K):
+    """A projector too wide for 32-request panels streams unions of 24-request
+    groups: group edges at 24 / 25 (one request alone in the second group),
+    two full groups at 48, three at 64 (the last of 16); the tokens meet the
+    oracle, the union sizes match the oracle's pools and a second run
+    repeats the first bit for bit."""
+    G.log(f"[gpu-test] pool union, 24-request groups B={B} K={K}")
+    with _pool_strategy(G.handle(PROJ1280, 64, 2048, STRONG), 2):
+        tok, top, h = G.gpu_run(PROJ1280, B, 650 + B, 0, K, max_batch=64, max_k=2048,
+                                scales_key=STRONG)
+        un = h.read_workspace(3).cpu().numpy()
+        tok2, top2, _ = G.gpu_run(PROJ1280, B, 650 + B, 0, K, max_batch=64, max_k=2048,
+                                  scales_key=STRONG)
+    ref = G.oracle_run(PROJ1280, B, 650 + B, 0, K, scales_key=STRONG)
+    c, _ = compare(tok, top, ref, TOL["bf16"])
+    assert c > 0
+    _check_unions(un, ref, B, 24)
     assert np.array_equal(tok, tok2) and np.array_equal(top.view(np.uint32), top2.view(np.uint32))
 
 
