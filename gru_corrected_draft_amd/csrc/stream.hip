@@ -29,7 +29,19 @@ constexpr int kUnionUnitRows = 32;  // rows per unit of the union stream (two 16
 constexpr int kSC = 128;  // k per super-chunk (4 MFMA k-slices of 32)
 constexpr bool kStraightWalk = true;
 
-template <int NB, int RT, bool SPLIT, int EPI, int D>
+// Row spreading (SP, the one-request LM-head).  A 16-row tile T normally
+// holds weight rows 16 T .. 16 T + 15; spread, its row r is weight row r S + T
+// (S = ceil(N / 16) tiles), so the sixteen rows a wave streams side by side
+// are S rows apart instead of adjacent.  A load-only probe on MI355X read
+// adjacent 8 KB rows at ~5.3 TB/s and spread ones at ~6.0; in this kernel the
+// LM-head at one request went from 251 to 248 us.  (The correction stream,
+// 2 KB rows, was slower spread: 49.4 -> 54.1 us, its epilogue then reading
+// bias and base values one by one.)
+__device__ __forceinline__ int tile_row(bool sp, int T, int r, int S) {
+  return sp ? r * S + T : T * 16 + r;
+}
+
+template <int NB, int RT, bool SPLIT, int EPI, int D, bool SP = false>
 __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
   extern __shared__ __align__(16) bf16_t sact[];
   const int lane = threadIdx.x & 63, wave = wave_index();
@@ -47,11 +59,13 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
   const int ncl = min(NB * 16, a.ncols - c0);  // columns of this block (>= 1)
   const int tile0 = (rowblock * 4 + wave) * RT;
   const bool active = tile0 * 16 < N;
+  const int S = (N + 15) / 16;
+  static_assert(!SP || EPI == kEpiStore, "spread rows: store epilogue only");
 
   const bf16_t* pa[RT];
 #pragma unroll
   for (int t = 0; t < RT; ++t)
-    pa[t] = a.W + (size_t)min((tile0 + t) * 16 + row, N - 1) * K + q * 8;
+    pa[t] = a.W + (size_t)min(tile_row(SP, tile0 + t, row, S), N - 1) * K + q * 8;
 
   v4f acc[RT][NB];
 #pragma unroll
@@ -166,7 +180,13 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
 #pragma unroll
       for (int t = 0; t < RT; ++t) {
         const int v = (tile0 + t) * 16 + 4 * q;
-        if ((N & 3) == 0 && v + 3 < N) {
+        if (SP) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int vs = tile_row(true, tile0 + t, 4 * q + i, S);
+            if (vs < N) orow[vs] = acc[t][cb][i];
+          }
+        } else if ((N & 3) == 0 && v + 3 < N) {
           *reinterpret_cast<float4*>(orow + v) =
               make_float4(acc[t][cb][0], acc[t][cb][1], acc[t][cb][2], acc[t][cb][3]);
         } else {
@@ -579,7 +599,7 @@ void launch_persist(StreamArgs a, int gcols, hipStream_t st) {
     launch_persist_t<NB, RT, D, false, SPLIT, EPI, WV, PK>(a, lds, st);
 }
 
-template <int NB, int RT, bool SPLIT, int EPI, int D>
+template <int NB, int RT, bool SPLIT, int EPI, int D, bool SP = false>
 void launch_t(StreamArgs a, hipStream_t st) {
   const int tiles = (a.N + 15) / 16;
   const int waves = (tiles + RT - 1) / RT;
@@ -587,7 +607,7 @@ void launch_t(StreamArgs a, hipStream_t st) {
   const int cols = min(a.ncols, NB * 16);
   a.groups = (a.ncols + NB * 16 - 1) / (NB * 16);
   const size_t lds = (size_t)(SPLIT ? 2 : 1) * cols * (a.KS + 8) * sizeof(bf16_t);
-  DLAUNCH((rowstream_kernel<NB, RT, SPLIT, EPI, D>),
+  DLAUNCH((rowstream_kernel<NB, RT, SPLIT, EPI, D, SP>),
                      dim3(8 * a.groups * ((rowblocks + 7) / 8)), dim3(256), lds, st, a);
 }
 
@@ -616,8 +636,8 @@ void dispatch_store(StreamArgs a, hipStream_t st) {
   const int nb = (a.ncols + 15) / 16;
   a.KS = pick_slice(a.K, a.ncols, 1, kStoreBudget);
   switch (nb) {
-    // one column block: a single row tile per wave streams faster
-    case 1: launch_t<1, 1, false, kEpiStore, kStoreD>(a, st); break;
+    // one column block: a single row tile per wave streams faster, its rows spread
+    case 1: launch_t<1, 1, false, kEpiStore, kStoreD, true>(a, st); break;
     case 2: launch_t<2, 2, false, kEpiStore, 2>(a, st); break;
     case 3: launch_t<3, 2, false, kEpiStore, 2>(a, st); break;
     case 4: launch_t<4, 2, false, kEpiStore, 2>(a, st); break;
@@ -753,7 +773,9 @@ void rowstream_prepare() {
 #define SET(NB, RT, SP, EP, D)                                                                   \
   (void)hipFuncSetAttribute((const void*)rowstream_kernel<NB, RT, SP, EP, D>,                    \
                             hipFuncAttributeMaxDynamicSharedMemorySize, lim)
-  SET(1, 1, false, kEpiStore, kStoreD); SET(2, 2, false, kEpiStore, 2);
+  (void)hipFuncSetAttribute((const void*)rowstream_kernel<1, 1, false, kEpiStore, kStoreD, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lim);
+  SET(2, 2, false, kEpiStore, 2);
   SET(3, 2, false, kEpiStore, 2); SET(4, 2, false, kEpiStore, 2);
   SET(5, 1, false, kEpiStore, 2); SET(6, 1, false, kEpiStore, 2);
   SET(7, 1, false, kEpiStore, 2); SET(8, 1, false, kEpiStore, 2);
