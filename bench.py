@@ -319,6 +319,16 @@ def main():
             gbs = nbytes / (avg[k] * 1e-3) / 1e9
             phases[k]["alg_gb_s"] = round(gbs, 1)
             phases[k]["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+    # one correction step as a whole: its correction launch plus the GRU
+    # update and projector launches that feed the next step (the prefix
+    # launch included), algorithmic bytes of both over their summed time
+    per_step = None
+    if P > 1 and "correct" in phases:
+        t_ms = sum(avg[k] * kt[k][1] / args.steps for k in ("correct", "step", "gru") if avg.get(k))
+        t_ms /= P - 1
+        nbytes = alg["correct_bytes"] + alg["step_bytes"]
+        per_step = {"ms": round(t_ms, 5), "alg_gb_s": round(nbytes / (t_ms * 1e-3) / 1e9, 1),
+                    "hbm_frac": round(nbytes / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     line = {
         "metric": f"Domino rollout ms/block ({P} proposals)",
@@ -345,6 +355,7 @@ def main():
                    "mode": "hip graph replay"},
         "roofline": roof,
         "phases": phases,
+        "per_step": per_step,
         "wall_ms_per_step": round(wall_ms / args.steps, 4),
         "spread": spread,
         **({"flushed": flushed} if flushed else {}),
