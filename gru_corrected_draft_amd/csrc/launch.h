@@ -215,9 +215,9 @@ constexpr int kFusedMinBatch = 2;
 void lmhead_fused_prepare();
 bool lmhead_fused_supported(int H);
 void launch_lmhead_fused(const FusedArgs& a, hipStream_t st);
-// Above 24 requests (H a multiple of 128, request groups of 32 nearly full)
-// the LM-head reads the hiddens from a fragment-ordered copy of
-// lmhead_xfrag_elems(B, H) bf16 elements; possible: for some B <= max_batch.
+// From 17 to 32 requests and at 56-64 (H a multiple of 128) the LM-head reads
+// the hiddens from a fragment-ordered copy of lmhead_xfrag_elems(B, H) bf16
+// elements; possible: for some B <= max_batch.
 bool lmhead_xfrag_used(int B, int H);
 bool lmhead_xfrag_possible(int max_batch, int H);
 size_t lmhead_xfrag_elems(int B, int H);

@@ -524,7 +524,7 @@ __global__ __launch_bounds__(256) void lmhead_m32_kernel(FusedArgs a) {
   }
 }
 
-// LM-head above 24 requests: the activations as register operands.
+// LM-head from 17 requests on: the activations as register operands.
 //
 // A workgroup computes 128 vocabulary rows x 32 requests (512 activation
 // rows, 16 per request: the 15 positions and a padding row that repeats
@@ -542,7 +542,8 @@ __global__ __launch_bounds__(256) void lmhead_m32_kernel(FusedArgs a) {
 // read.
 //
 // Measured (LM-head ms): 8B B = 64 1.143 (line kernel 1.143), B = 32 0.638
-// (0.644), 27B-class B = 64 1.436 (1.553).  One wave per SIMD with 4 x 4
+// (0.644), 27B-class B = 64 1.436 (1.553); the dispatch range is set at
+// lmhead_xfrag_used().  One wave per SIMD with 4 x 4
 // tiles (256 accumulators) ran at 1.30 ms at 8B B = 64.  Counters at 8B
 // B = 64: the matrix cores are busy 56% of the active cycles (line kernel
 // 42%), but the part runs this kernel at ~1.9 GHz against ~2.35 GHz for the
@@ -771,16 +772,20 @@ void lmhead_fused_prepare() {
 
 size_t lmhead_xfrag_elems(int B, int H) { return lmhead_xfrag_bytes(B, H) / 2; }
 
-// Requests are processed in groups of 32, so a partial last group wastes
-// products: taken when the waste is at most an eighth (B = 28-32, 56-64) and
-// otherwise left to the line kernel (B = 48: 1.12 against 0.95 ms).
+// Requests are processed in groups of 32.  One group wins from 17 requests
+// on, even part full (8B LM-head ms, this kernel / the m32 or line kernel:
+// B = 17 0.569 / 0.607, 20 0.588 / 0.607, 24 0.589 / 0.614, 26 0.607 /
+// 0.654, 28 0.605 / -, 32 0.638 / 0.644); with two groups the partial one's
+// wasted products cost more than they save unless the waste is at most an
+// eighth (B = 56-64; B = 40 1.124 / 0.877, 48 1.12 / 0.94).
+constexpr int kXfMinBatch = 17;
 bool lmhead_xfrag_used(int B, int H) {
   const int padded = (B + kXfRq - 1) / kXfRq * kXfRq;
-  return B > kM32MaxBatch && H % 128 == 0 && 8 * (padded - B) <= padded;
+  return B >= kXfMinBatch && H % 128 == 0 && (B <= kXfRq || 8 * (padded - B) <= padded);
 }
 
 bool lmhead_xfrag_possible(int max_batch, int H) {
-  for (int b = kM32MaxBatch + 1; b <= max_batch; ++b)
+  for (int b = kXfMinBatch; b <= max_batch; ++b)
     if (lmhead_xfrag_used(b, H)) return true;
   return false;
 }
@@ -791,6 +796,15 @@ void launch_lmhead_fused(const FusedArgs& a, hipStream_t st) {
   // 32-bit byte offsets of the line copies
   const bool offsets32 = (uint64_t)a.V * a.H * 2 < (1ull << 32) &&
                          (uint64_t)a.B * DOMINO_T * a.H * 2 < (1ull << 32);
+  if (a.XP && lmhead_xfrag_used(a.B, a.H) && offsets32) {
+    const size_t pieces = lmhead_xfrag_elems(a.B, a.H) / 8;
+    DLAUNCH(xfrag_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
+            (const bf16_t*)a.X, a.B, a.H, (bf16_t*)a.XP, pieces);
+    const int nvt = (a.V + kXfV - 1) / kXfV, ngrp = (a.B + kXfRq - 1) / kXfRq;
+    DLAUNCH(lmhead_xf_kernel<kXfTA>, dim3(8 * ((nvt + 7) / 8) * ngrp), dim3(64 * 16 / kXfTA), kXfLds,
+            st, a);
+    return;
+  }
   if (a.B <= kM32MaxBatch && a.H % kMK == 0 && offsets32) {
     const int ngrp = (a.B + kMR - 1) / kMR;
     if (a.B <= kM32SmallBatch) {
@@ -802,15 +816,6 @@ void launch_lmhead_fused(const FusedArgs& a, hipStream_t st) {
       DLAUNCH(lmhead_m32_kernel<2>, dim3(8 * ((nvt + 7) / 8) * ngrp), dim3(256), M32<2>::kLds, st,
               a);
     }
-    return;
-  }
-  if (a.XP && lmhead_xfrag_used(a.B, a.H) && offsets32) {
-    const size_t pieces = lmhead_xfrag_elems(a.B, a.H) / 8;
-    DLAUNCH(xfrag_pack_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, st,
-            (const bf16_t*)a.X, a.B, a.H, (bf16_t*)a.XP, pieces);
-    const int nvt = (a.V + kXfV - 1) / kXfV, ngrp = (a.B + kXfRq - 1) / kXfRq;
-    DLAUNCH(lmhead_xf_kernel<kXfTA>, dim3(8 * ((nvt + 7) / 8) * ngrp), dim3(64 * 16 / kXfTA), kXfLds,
-            st, a);
     return;
   }
   const int nvt = (a.V + kBN - 1) / kBN, ngrp = (a.B + kBJ - 1) / kBJ;

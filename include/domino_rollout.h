@@ -110,7 +110,7 @@ typedef struct domino_rollout domino_rollout_t;
  * (8.4 MB at g = r = 1024) and, when max_batch > 16, of fc2_w (311 MB at
  * V = 151936, r = 1024) in the order the matrix cores read them.  This is why
  * these weights must not change while the handle lives.  With bf16 weights,
- * max_batch >= 28 and H a multiple of 128, the workspace also holds the
+ * max_batch >= 17 and H a multiple of 128, the workspace also holds the
  * block's hiddens in fragment order for the LM-head (8.4 MB at 64 requests,
  * H = 4096, rewritten by every run).  create()
  * synchronises the device.  On success
