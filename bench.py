@@ -165,8 +165,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the rollout is built and timed on a single MI355X; "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        print("bench.py times one GPU: the rollout runs on a single MI355X, and --gpus above 1 "
+              "is not supported.", file=sys.stderr)
         sys.exit(2)
 
     import torch
