@@ -181,7 +181,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
     return DOMINO_ERR_HIP;
   }
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
-    set_global_err(std::string("create: device is ") + prop.gcnArchName + ", this build needs gfx950");
+    set_global_err(std::string("create: device is ") + prop.gcnArchName + ", the library runs on gfx950 only");
     return DOMINO_ERR_UNSUPPORTED;
   }
 

@@ -52,7 +52,7 @@ typedef enum {
   DOMINO_OK = 0,
   DOMINO_ERR_INVALID_ARG = -1,     /* bad scalar or NULL pointer; nothing launched */
   DOMINO_ERR_INVALID_CONFIG = -2,  /* create(): inconsistent configuration        */
-  DOMINO_ERR_UNSUPPORTED = -3,     /* device is not gfx950, or a shape this build
+  DOMINO_ERR_UNSUPPORTED = -3,     /* device is not gfx950, or a shape the library
                                       does not handle (see domino_config_t)       */
   DOMINO_ERR_OUT_OF_MEMORY = -4,   /* workspace allocation failed in create()      */
   DOMINO_ERR_HIP = -5              /* a HIP runtime call failed                    */
