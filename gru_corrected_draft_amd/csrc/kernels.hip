@@ -287,23 +287,10 @@ void launch_gru_table(const Shape& s, const DeviceWeights& w, float* G, hipStrea
 }
 
 // ---------------------------------------------------------------- reset
-__global__ void reset_kernel(uint64_t* slots, int nslots, uint32_t* hist, int nhist,
-                             uint32_t* state, int32_t* bad, int B, int K) {
-  const int stride = gridDim.x * blockDim.x;
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < nhist; j += stride) hist[j] = 0;
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < nslots; j += stride) slots[j] = 0;
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < B; j += stride) {
-    state[8 * j] = 0;  // radix state 0: empty prefix, rank K
-    state[8 * j + 1] = (uint32_t)K;
-    bad[j] = 0;
-  }
-}
-
-void launch_reset(const Workspace& ws, int B, int K, hipStream_t st) {
-  const int nslots = DOMINO_T * B, nhist = B * 3 * 2048;
-  DLAUNCH(reset_kernel, dim3(64), dim3(256), 0, st, ws.slots, nslots, ws.hist, nhist,
-                     ws.state, ws.bad, B, K);
-}
+// There is no reset launch: a run's writeout (the last kernel of every run)
+// clears the argmax words, the bad-token flags and the radix histograms it
+// leaves behind, create() clears them once, and the first selection takes
+// its initial state (empty prefix, rank K) from K itself.
 
 // ------------------------------------------------------- first proposal (p1)
 // argmax over the full vocabulary of base row 0 (t = 0), one word per request
@@ -435,7 +422,7 @@ __device__ __forceinline__ uint2 select_bin(const uint32_t* __restrict__ hh, uin
 template <int PASS, int F>
 __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restrict__ keys, int V,
                                                         uint32_t* __restrict__ state,
-                                                        uint32_t* __restrict__ hist) {
+                                                        uint32_t* __restrict__ hist, int K) {
   constexpr int NBINS = PASS < 2 ? 2048 : 1024;
   __shared__ uint32_t h[NBINS];
   __shared__ int lds[4];
@@ -452,7 +439,9 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
   uint32_t prefix = 0;
   if (PASS > 0) {
     uint32_t* sb = state + 8 * b + 2 * (PASS - 1);
-    const uint2 ns = select_bin<PASS - 1>(hist + ((size_t)b * 3 + PASS - 1) * 2048, sb[0], sb[1],
+    // the state before the first selection is (empty prefix, rank K)
+    const uint32_t p0 = PASS == 1 ? 0u : sb[0], r0 = PASS == 1 ? (uint32_t)K : sb[1];
+    const uint2 ns = select_bin<PASS - 1>(hist + ((size_t)b * 3 + PASS - 1) * 2048, p0, r0,
                                           lds, res);
     prefix = ns.x;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
@@ -712,11 +701,11 @@ static void pool_select_passes(const Shape& s, const Workspace& ws, int B, int K
   const int nch = (s.V + F * kPoolChunk - 1) / (F * kPoolChunk);
   const dim3 grid(nch, B), blk(256);
   if (keys_ready)
-    DLAUNCH((pool_hist_kernel<0, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+    DLAUNCH((pool_hist_kernel<0, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, K);
   else
     DLAUNCH((pool_score_hist_kernel<F>), grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
-  DLAUNCH((pool_hist_kernel<1, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
-  DLAUNCH((pool_hist_kernel<2, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist);
+  DLAUNCH((pool_hist_kernel<1, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, K);
+  DLAUNCH((pool_hist_kernel<2, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, K);
   DLAUNCH((pool_count_kernel<F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, ws.counts,
           nch);
   DLAUNCH((pool_compact_kernel<F>), grid, blk, 0, st, ws.keys, s.V, K, ws.state, ws.counts, nch,
@@ -1187,21 +1176,31 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
 }
 
 // ---------------------------------------------------------------- outputs
-__global__ void writeout_kernel(const uint64_t* __restrict__ slots, const int32_t* __restrict__ bad,
-                                int B, int P, int32_t* __restrict__ out_tokens,
-                                float* __restrict__ out_top1) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * P) return;
-  const int b = idx / P, k = idx % P;
-  const uint64_t key = slots[(size_t)k * B + b];
-  const bool invalid = bad[b] != 0 || key == 0;
-  out_tokens[idx] = invalid ? -1 : key_id(key);
-  if (out_top1) out_top1[idx] = invalid ? __builtin_nanf("") : key_value(key);
+// One workgroup per request: lane k < P writes proposal k, then (after every
+// lane has read them) the request's argmax words, bad flag and, after a pool
+// run, radix histograms are cleared for the next run.
+__global__ __launch_bounds__(64) void writeout_kernel(uint64_t* __restrict__ slots,
+                                                      int32_t* __restrict__ bad,
+                                                      uint32_t* __restrict__ hist, int B, int P,
+                                                      int32_t* __restrict__ out_tokens,
+                                                      float* __restrict__ out_top1) {
+  const int b = blockIdx.x, k = threadIdx.x;
+  const bool flagged = bad[b] != 0;
+  if (k < P) {
+    const uint64_t key = slots[(size_t)k * B + b];
+    const bool invalid = flagged || key == 0;
+    out_tokens[b * P + k] = invalid ? -1 : key_id(key);
+    if (out_top1) out_top1[b * P + k] = invalid ? __builtin_nanf("") : key_value(key);
+  }
+  __syncthreads();  // every lane has read bad[b]
+  if (k < DOMINO_T) slots[(size_t)k * B + b] = 0;
+  if (k == 0) bad[b] = 0;
+  if (hist)
+    for (int i = k; i < 3 * 2048; i += 64) hist[(size_t)b * 3 * 2048 + i] = 0;
 }
 
-void launch_writeout(const Workspace& ws, int B, int P, int32_t* out_tokens, float* out_top1,
-                     hipStream_t st) {
-  const int n = B * P;
-  DLAUNCH(writeout_kernel, dim3((n + 255) / 256), dim3(256), 0, st, ws.slots, ws.bad, B, P,
-          out_tokens, out_top1);
+void launch_writeout(const Workspace& ws, int B, int P, bool pool, int32_t* out_tokens,
+                     float* out_top1, hipStream_t st) {
+  DLAUNCH(writeout_kernel, dim3(B), dim3(64), 0, st, ws.slots, ws.bad, pool ? ws.hist : nullptr,
+          B, P, out_tokens, out_top1);
 }

@@ -222,7 +222,6 @@ bool lmhead_xfrag_used(int B, int H);
 bool lmhead_xfrag_possible(int max_batch, int H);
 size_t lmhead_xfrag_elems(int B, int H);
 
-void launch_reset(const Workspace& ws, int B, int K, hipStream_t st);
 void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int B, hipStream_t st);
 void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st);
 // Whether a pool correction of B requests streams each request group's
@@ -242,6 +241,7 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
 size_t step_offsets_partial_floats(int Bmax, int H, int r);
 void launch_step_offsets(const Shape& s, const DeviceWeights& w, const void* X, const Workspace& ws,
                          int B, hipStream_t st);
-// tokens and top-1 logits of proposals 1..P, [B, P]
-void launch_writeout(const Workspace& ws, int B, int P, int32_t* out_tokens, float* out_top1,
-                     hipStream_t st);
+// tokens and top-1 logits of proposals 1..P, [B, P]; then clears the argmax
+// words, bad flags and (pool runs) radix histograms for the next run
+void launch_writeout(const Workspace& ws, int B, int P, bool pool, int32_t* out_tokens,
+                     float* out_top1, hipStream_t st);

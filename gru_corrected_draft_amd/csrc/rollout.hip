@@ -280,6 +280,10 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   if ((unions && hipMemset(ws.umask, 0, (size_t)ws.ugmax * V * 4) != hipSuccess) ||
       (ws.hp && hipMemset(ws.hp, 0, (Bm + 15) / 16 * 16 * g * 4) != hipSuccess) ||
       hipMemset(ws.pool_ids, 0, Bm * Km * 4) != hipSuccess ||
+      // cleared by every run's writeout from then on
+      hipMemset(ws.slots, 0, DOMINO_T * Bm * 8) != hipSuccess ||
+      hipMemset(ws.bad, 0, Bm * 4) != hipSuccess ||
+      hipMemset(ws.hist, 0, Bm * 3 * 2048 * 4) != hipSuccess ||
       hipMemset(ws.base, 0, DOMINO_T * Bm * V * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
     set_global_err("create: workspace initialisation failed");
     domino_rollout_destroy(h);
@@ -403,7 +407,6 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
   h->last_B = B;
   h->last_K = pool ? K : 0;
   h->last_union = pool && pool_union(sh, ws, B, K);
-  launch_reset(ws, B, pool ? K : 0, st);
   h->last_s_internal = s == nullptr;
   if (!s) {
     // step offsets from the block's hiddens (projector layer 1, backbone half)
@@ -498,7 +501,7 @@ static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, con
         launch_correct_full(sh, h->w, ws, k, B, st);
     }
   }
-  launch_writeout(ws, B, P, out_tokens, out_top1, st);
+  launch_writeout(ws, B, P, pool, out_tokens, out_top1, st);
 }
 
 namespace {
