@@ -381,7 +381,9 @@ __global__ __launch_bounds__(256) void pool_score_hist_kernel(const float* __res
 
 // The radix state of request b after s selections sits at state[8 b + 2 s]
 // (key prefix so far) and state[8 b + 2 s + 1] (rank of the K-th key among
-// the keys with that prefix); s = 0 is (0, K), set by the reset kernel.
+// the keys with that prefix), s = 1..3.  The state s = 0, (empty prefix, K),
+// is never stored: the first selection (inside pool_hist_kernel<1>) starts
+// from the kernel's K argument.
 
 // Block-wide (256 threads): the bin of pass PASS (histogram hh) that holds
 // the need-th largest key with the current prefix; returns the extended

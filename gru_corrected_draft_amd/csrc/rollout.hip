@@ -43,9 +43,17 @@ struct GraphKey {
   }
 };
 
+// A cached graph, with the run shape its capture recorded (what
+// read_workspace reports after a replay of it) and an event recorded after
+// each of its launches, so that an evicted graph is destroyed only once its
+// last replay has finished.
 struct GraphEntry {
   GraphKey key;
   hipGraphExec_t exec;
+  hipEvent_t done;
+  uint64_t used;  // cache clock of the last use (least recently used is evicted)
+  int last_B, last_K;
+  bool last_union, last_s_internal;
 };
 
 constexpr int kPhases = 7;
@@ -60,7 +68,8 @@ struct domino_rollout {
   int device;
   Workspace ws;
   std::vector<void*> allocations;
-  std::vector<GraphEntry> graphs;
+  std::vector<GraphEntry> graphs;  // at most DOMINO_GRAPH_CACHE_MAX
+  uint64_t graph_clock = 0;
   hipStream_t capture_stream = nullptr;
   int last_B = 0, last_K = 0;  // shape of the last enqueued run
   bool last_s_internal = false;  // the last run formed step_s itself
@@ -310,6 +319,16 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   return DOMINO_OK;
 }
 
+// Destroys every cached graph (the device has finished their launches: the
+// callers synchronise first, or the handle is going away with its work done).
+static void drop_graphs(domino_rollout_t* h) {
+  for (auto& g : h->graphs) {
+    (void)hipGraphExecDestroy(g.exec);
+    if (g.done) (void)hipEventDestroy(g.done);
+  }
+  h->graphs.clear();
+}
+
 extern "C" void domino_rollout_destroy(domino_rollout_t* h) {
   if (!h) return;
   for (auto& p : h->pending) {
@@ -317,7 +336,7 @@ extern "C" void domino_rollout_destroy(domino_rollout_t* h) {
     (void)hipEventDestroy(p.b);
   }
   for (auto e : h->free_events) (void)hipEventDestroy(e);
-  for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);
+  drop_graphs(h);
   if (h->capture_stream) (void)hipStreamDestroy(h->capture_stream);
   for (void* p : h->allocations) (void)hipFree(p);
   delete h;
@@ -340,8 +359,9 @@ static domino_status_t check_run_args(domino_rollout_t* h, const void* hidden, c
   if (!s && !h->w.fc1_x)
     return h->fail(DOMINO_ERR_INVALID_ARG,
                    "run: step_s is NULL and the handle holds no fc1_x_w / fc1_b to form it");
-  if (((uintptr_t)hidden & 15) || ((uintptr_t)s & 3))
+  if ((uintptr_t)hidden & 15)
     return h->fail(DOMINO_ERR_INVALID_ARG, "run: base_hidden must be 16-byte aligned");
+  if ((uintptr_t)s & 3) return h->fail(DOMINO_ERR_INVALID_ARG, "run: step_s must be 4-byte aligned");
   if (B < 1 || B > h->cfg.max_batch)
     return h->fail(DOMINO_ERR_INVALID_ARG, "run: batch %d outside [1, %d]", B, h->cfg.max_batch);
   if (K < 0) return h->fail(DOMINO_ERR_INVALID_ARG, "run: K must be >= 0 (got %d)", K);
@@ -559,17 +579,33 @@ static domino_status_t run_graph_common(domino_rollout_t* h, const void* base_hi
   const int kmode = (K > 0 && K < h->cfg.vocab) ? K : 0;
   GraphKey key{batch, kmode, 0, P,
                {base_hidden, step_s, verified_tokens, out_tokens, out_top1_logit, nullptr}};
-  hipGraphExec_t exec = nullptr;
+  GraphEntry* ent = nullptr;
   for (auto& g : h->graphs)
-    if (g.key == key) exec = g.exec;
-  if (!exec) {
+    if (g.key == key) ent = &g;
+  if (!ent) {
+    if (h->graphs.size() >= DOMINO_GRAPH_CACHE_MAX) {
+      // evict the least recently used graph once its last replay has ended
+      auto lru = std::min_element(h->graphs.begin(), h->graphs.end(),
+                                  [](const GraphEntry& a, const GraphEntry& b) { return a.used < b.used; });
+      if (hipEventSynchronize(lru->done) != hipSuccess)
+        return h->fail(DOMINO_ERR_HIP, "run_graph: waiting for an evicted graph failed");
+      (void)hipGraphExecDestroy(lru->exec);
+      (void)hipEventDestroy(lru->done);
+      h->graphs.erase(lru);
+    }
+    hipGraphExec_t exec = nullptr;
+    hipEvent_t done = nullptr;
+    if (hipEventCreateWithFlags(&done, hipEventDisableTiming) != hipSuccess)
+      return h->fail(DOMINO_ERR_HIP, "run_graph: event creation failed");
     if (!h->capture_stream &&
         hipStreamCreateWithFlags(&h->capture_stream, hipStreamNonBlocking) != hipSuccess)
       return h->fail(DOMINO_ERR_HIP, "run_graph: stream creation failed");
     (void)hipGetLastError();
     hipGraph_t graph = nullptr;
-    if (hipStreamBeginCapture(h->capture_stream, hipStreamCaptureModeRelaxed) != hipSuccess)
+    if (hipStreamBeginCapture(h->capture_stream, hipStreamCaptureModeRelaxed) != hipSuccess) {
+      (void)hipEventDestroy(done);
       return h->fail(DOMINO_ERR_HIP, "run_graph: begin capture failed");
+    }
     h->capturing = true;
     enqueue(h, base_hidden, step_s, verified_tokens, nullptr, batch, kmode, P, out_tokens,
             out_top1_logit, h->capture_stream);
@@ -578,17 +614,37 @@ static domino_status_t run_graph_common(domino_rollout_t* h, const void* base_hi
     hipError_t e2 = hipStreamEndCapture(h->capture_stream, &graph);
     if (e1 != hipSuccess || e2 != hipSuccess || !graph) {
       if (graph) (void)hipGraphDestroy(graph);
+      (void)hipEventDestroy(done);
       return h->fail(DOMINO_ERR_HIP, "run_graph: capture failed: %s",
                      hipGetErrorString(e1 != hipSuccess ? e1 : e2));
     }
     hipError_t e3 = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     (void)hipGraphDestroy(graph);
-    if (e3 != hipSuccess) return h->fail(DOMINO_ERR_HIP, "run_graph: instantiate failed: %s", hipGetErrorString(e3));
-    h->graphs.push_back(GraphEntry{key, exec});
+    if (e3 != hipSuccess) {
+      (void)hipEventDestroy(done);
+      return h->fail(DOMINO_ERR_HIP, "run_graph: instantiate failed: %s", hipGetErrorString(e3));
+    }
+    h->graphs.push_back(GraphEntry{key, exec, done, 0, h->last_B, h->last_K, h->last_union,
+                                   h->last_s_internal});
+    ent = &h->graphs.back();
   }
-  hipError_t e = hipGraphLaunch(exec, (hipStream_t)stream);
+  ent->used = ++h->graph_clock;
+  // the workspace now holds this graph's run
+  h->last_B = ent->last_B;
+  h->last_K = ent->last_K;
+  h->last_union = ent->last_union;
+  h->last_s_internal = ent->last_s_internal;
+  hipError_t e = hipGraphLaunch(ent->exec, (hipStream_t)stream);
   if (e != hipSuccess) return h->fail(DOMINO_ERR_HIP, "run_graph: launch failed: %s", hipGetErrorString(e));
+  if (hipEventRecord(ent->done, (hipStream_t)stream) != hipSuccess)
+    return h->fail(DOMINO_ERR_HIP, "run_graph: event record failed");
   h->err.clear();
+  return DOMINO_OK;
+}
+
+extern "C" domino_status_t domino_rollout_cached_graphs(const domino_rollout_t* h, int32_t* count) {
+  if (!h || !count) return DOMINO_ERR_INVALID_ARG;
+  *count = (int32_t)h->graphs.size();
   return DOMINO_OK;
 }
 
@@ -657,8 +713,7 @@ extern "C" domino_status_t domino_rollout_set_pool_strategy(domino_rollout_t* h,
     DeviceGuard dg(h->device);
     if (hipDeviceSynchronize() != hipSuccess)
       return h->fail(DOMINO_ERR_HIP, "set_pool_strategy: synchronize failed");
-    for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);  // captured the old strategy
-    h->graphs.clear();
+    drop_graphs(h);  // captured the old strategy
     h->ws.pool_strategy = strategy;
   }
   return DOMINO_OK;
@@ -672,8 +727,7 @@ extern "C" domino_status_t domino_rollout_set_step_path(domino_rollout_t* h, int
     DeviceGuard dg(h->device);
     if (hipDeviceSynchronize() != hipSuccess)
       return h->fail(DOMINO_ERR_HIP, "set_step_path: synchronize failed");
-    for (auto& g : h->graphs) (void)hipGraphExecDestroy(g.exec);  // captured the old path
-    h->graphs.clear();
+    drop_graphs(h);  // captured the old path
     h->step_path = path;
   }
   return DOMINO_OK;

@@ -31,7 +31,8 @@ EXPORTED = ("domino_rollout_create", "domino_rollout_run", "domino_rollout_run_g
             "domino_rollout_read_workspace", "domino_rollout_destroy",
             "domino_rollout_last_error", "domino_rollout_set_timing",
             "domino_rollout_kernel_times", "domino_rollout_set_pool_strategy",
-            "domino_rollout_set_step_path")
+            "domino_rollout_set_step_path", "domino_rollout_cached_graphs")
+GRAPH_CACHE_MAX = 16  # DOMINO_GRAPH_CACHE_MAX
 # gru: the GRU gates (prefix launch, separate gate kernel); step: projector
 # layer 1 and W_hh of the new state (with the gates where fused)
 PHASES = {"lmhead": 0, "correct": 1, "gru": 2, "step": 3, "pool": 4, "argmax0": 5, "offsets": 6}
@@ -100,6 +101,8 @@ def load_library():
     lib.domino_rollout_kernel_times.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double),
                                                 ctypes.POINTER(ctypes.c_int64)]
     lib.domino_rollout_kernel_times.restype = ctypes.c_int
+    lib.domino_rollout_cached_graphs.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.domino_rollout_cached_graphs.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -118,6 +121,34 @@ def make_config(vocab, hidden, emb_dim, gru_hidden, proj_dim, max_batch, max_k, 
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def check_outputs(out_tokens, out_top1, B, P, device):
+    """The library writes [B, P] int32 tokens and [B, P] float32 logits at
+    the given addresses with row stride P: both must be contiguous tensors of
+    exactly that shape and dtype on the inputs' device (a host tensor would
+    be written through a host address by the device)."""
+    import torch
+    for name, t, dt in (("out_tokens", out_tokens, torch.int32),
+                        ("out_top1", out_top1, torch.float32)):
+        if tuple(t.shape) != (B, P):
+            raise ValueError(f"{name} must be [B, P] = [{B}, {P}], got {list(t.shape)}")
+        if t.dtype != dt:
+            raise ValueError(f"{name} must be {dt}, got {t.dtype}")
+        if t.device != device:
+            raise ValueError(f"{name} must be on {device}, got {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def check_forced(forced, B, device):
+    """Teacher-forced tokens are read as forced[b * 15 + j]: [B, 15] int32,
+    contiguous, on the inputs' device."""
+    import torch
+    if tuple(forced.shape) != (B, N_PROPOSALS) or forced.dtype != torch.int32:
+        raise ValueError("forced must be [B, 15] int32")
+    if forced.device != device or not forced.is_contiguous():
+        raise ValueError(f"forced must be a contiguous tensor on {device}")
 
 
 class DominoRollout:
@@ -176,17 +207,18 @@ class DominoRollout:
             raise ValueError("step_s must be [B, 14, r] float32")
         if verified.shape != (B,) or verified.dtype != torch.int32:
             raise ValueError("verified must be [B] int32")
-        for t in (hidden, verified) + (() if step_s is None else (step_s,)):
-            if not t.is_cuda or not t.is_contiguous():
-                raise ValueError("inputs must be contiguous device tensors")
         dev = hidden.device
+        for t in (hidden, verified) + (() if step_s is None else (step_s,)):
+            if not t.is_cuda or not t.is_contiguous() or t.device != dev:
+                raise ValueError("inputs must be contiguous tensors on one device")
         P = N_PROPOSALS if proposals is None else int(proposals)
         if out_tokens is None:
             out_tokens = torch.empty((B, P), dtype=torch.int32, device=dev)
         if out_top1 is None:
             out_top1 = torch.empty((B, P), dtype=torch.float32, device=dev)
-        if out_tokens.shape != (B, P) or out_top1.shape != (B, P):
-            raise ValueError("out_tokens / out_top1 must be [B, P]")
+        check_outputs(out_tokens, out_top1, B, P, dev)
+        if forced is not None:
+            check_forced(forced, B, dev)
         st_ptr = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream if stream is None
                                  else stream)
         if proposals is not None:
@@ -196,8 +228,6 @@ class DominoRollout:
                                                     _ptr(verified), B, K, P, _ptr(out_tokens),
                                                     _ptr(out_top1), int(bool(graph)), st_ptr)
         elif forced is not None:
-            if forced.shape != (B, N_PROPOSALS) or forced.dtype != torch.int32 or not forced.is_cuda:
-                raise ValueError("forced must be [B, 15] int32 on the device")
             st = self.lib.domino_rollout_run_forced(self.handle, _ptr(hidden), _ptr(step_s),
                                                     _ptr(verified), _ptr(forced), B, K,
                                                     _ptr(out_tokens), _ptr(out_top1), st_ptr)
@@ -232,6 +262,12 @@ class DominoRollout:
     def set_step_path(self, path):
         """0 automatic, 1 fused gates + rows, 2 gate kernel + rows, 3 gate kernel + matrix cores."""
         self._check(self.lib.domino_rollout_set_step_path(self.handle, int(path)))
+
+    def cached_graphs(self):
+        """Number of HIP graphs the handle holds (at most GRAPH_CACHE_MAX)."""
+        n = ctypes.c_int32()
+        self._check(self.lib.domino_rollout_cached_graphs(self.handle, ctypes.byref(n)))
+        return n.value
 
     def set_timing(self, enable):
         self._check(self.lib.domino_rollout_set_timing(self.handle, 1 if enable else 0))

@@ -140,10 +140,20 @@ domino_status_t domino_rollout_run(domino_rollout_t* h, const void* base_hidden,
                                    int32_t batch, int32_t K, int32_t* out_tokens,
                                    float* out_top1_logit, void* stream);
 
+/* Most graphs a handle keeps cached (domino_rollout_run_graph). */
+#define DOMINO_GRAPH_CACHE_MAX 16
+
 /* Same computation as domino_rollout_run, replayed from a HIP graph that the
- * handle captures on first use for each distinct (batch, K mode, pointer
- * set) and keeps until destroy.  The first call for a new key captures and
- * instantiates (host work); later calls are a single hipGraphLaunch. */
+ * handle captures on first use for each distinct (batch, K mode, proposals,
+ * pointer set).  The first call for a new key captures and instantiates
+ * (host work); later calls are a single hipGraphLaunch plus an event record.
+ * The cache holds at most DOMINO_GRAPH_CACHE_MAX graphs: a new key beyond
+ * that evicts the least recently used graph, after a host wait for that
+ * graph's last replay to finish (normally long done), so a caller that
+ * rotates more buffer sets than that pays a capture per rotation but never
+ * grows the cache.  A replay leaves the workspace as its own run does
+ * (domino_rollout_read_workspace reports the replayed run's shape).  Not for
+ * use inside the caller's own stream capture: use domino_rollout_run there. */
 domino_status_t domino_rollout_run_graph(domino_rollout_t* h, const void* base_hidden,
                                          const float* step_s, const int32_t* verified_tokens,
                                          int32_t batch, int32_t K, int32_t* out_tokens,
@@ -232,6 +242,10 @@ domino_status_t domino_rollout_set_step_path(domino_rollout_t* h, int32_t path);
 domino_status_t domino_rollout_set_pool_strategy(domino_rollout_t* h, int32_t strategy);
 domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int32_t which, double* total_ms,
                                             int64_t* launches);
+
+/* Number of graphs the handle has cached (0..DOMINO_GRAPH_CACHE_MAX) in
+ * *count.  INVALID_ARG for a NULL handle or count. */
+domino_status_t domino_rollout_cached_graphs(const domino_rollout_t* h, int32_t* count);
 
 /* Frees the workspace and cached graphs (not the borrowed weights). NULL is a no-op. */
 void domino_rollout_destroy(domino_rollout_t* h);

@@ -98,3 +98,36 @@ def test_null_handle_is_rejected(lib):
     assert lib.domino_rollout_set_pool_strategy(None, 0) == R.DOMINO_ERR_INVALID_ARG
     assert lib.domino_rollout_set_timing(None, 1) == R.DOMINO_ERR_INVALID_ARG
     lib.domino_rollout_destroy(None)   # no-op
+
+
+def test_output_tensors_checked_before_any_launch():
+    """The binding refuses output buffers the library would write with the
+    wrong layout or through a host address (no handle, no launch)."""
+    import torch
+    cpu, gpu = torch.device("cpu"), torch.device("cuda", 0)
+    tok = torch.zeros((3, 15), dtype=torch.int32)
+    top = torch.zeros((3, 15), dtype=torch.float32)
+    R.check_outputs(tok, top, 3, 15, cpu)
+    with pytest.raises(ValueError, match="on cuda"):
+        R.check_outputs(tok, top, 3, 15, gpu)              # host tensors for a device run
+    with pytest.raises(ValueError, match="int32"):
+        R.check_outputs(tok.long(), top, 3, 15, cpu)
+    with pytest.raises(ValueError, match="float32"):
+        R.check_outputs(tok, top.double(), 3, 15, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        R.check_outputs(torch.zeros((15, 3), dtype=torch.int32).t(), top, 3, 15, cpu)
+    with pytest.raises(ValueError, match=r"\[B, P\]"):
+        R.check_outputs(tok[:, :8], top, 3, 15, cpu)
+    forced = torch.zeros((3, 15), dtype=torch.int32)
+    R.check_forced(forced, 3, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        R.check_forced(torch.zeros((15, 3), dtype=torch.int32).t(), 3, cpu)
+    with pytest.raises(ValueError, match="contiguous"):
+        R.check_forced(forced, 3, gpu)
+    with pytest.raises(ValueError, match="int32"):
+        R.check_forced(forced.long(), 3, cpu)
+
+
+def test_graph_cache_query_rejects_null(lib):
+    n = ctypes.c_int32(-1)
+    assert lib.domino_rollout_cached_graphs(None, ctypes.byref(n)) == R.DOMINO_ERR_INVALID_ARG

@@ -621,7 +621,10 @@ def test_truncated_rollout_errors():
 
 # ------------------------------------------------------------ full-size shapes
 
-FULL = [("8b_b1", 0), ("8b_b8", 2048), ("8b_b64", 0), ("8b_b64", 2048), ("27b_b64", 2048)]
+# the five configured workloads plus the other two cells of the 8B matrix
+# (B = 1 with the pool, B = 8 over the full vocabulary)
+FULL = [("8b_b1", 0), ("8b_b8", 2048), ("8b_b64", 0), ("8b_b64", 2048), ("27b_b64", 2048),
+        ("8b_b1", 2048), ("8b_b8", 0)]
 
 
 @pytest.mark.parametrize("name", ["8b_b8", "8b_b64"])
@@ -670,7 +673,8 @@ def test_full_size_rollout(name, K):
     assert checked > 0
 
 
-@pytest.mark.parametrize("name,K", [("8b_b64", 0), ("8b_b64", 2048), ("27b_b64", 2048)])
+@pytest.mark.parametrize("name,K", [("8b_b1", 0), ("8b_b1", 2048), ("8b_b8", 0), ("8b_b8", 2048),
+                                    ("8b_b64", 0), ("8b_b64", 2048), ("27b_b64", 2048)])
 def test_full_size_teacher_forced(name, K):
     """Every step's winning logit at full size, whatever the chain: the GPU
     consumes the oracle's own proposals (teacher forcing), so each step is an
@@ -723,3 +727,36 @@ def _check_full_size_intermediates(h, wl, shape, trial, K, tok, ref):
             cutoff = np.sort(score)[-K]
             diff = np.setxor1d(ids[b], want)
             assert np.all(np.abs(score[diff] - cutoff) < 1e-3), f"pool of request {b}"
+
+
+def test_full_size_graph_equals_eager_20_trials():
+    """Graph replays equal eager runs bit for bit at the 8B shapes: 20 trials
+    at B = 1, 8 and 64 for each K mode, 21,900 proposals per mode (the
+    pages' own check counted proposal mismatches over 20 random trials per
+    batch: "Add correctness-first Domino support to DFlash V2",
+    "Validation").  No oracle: the two GPU paths against each other."""
+    import torch
+    h = G.handle("qwen3-8b", 64, 2048)
+    shape = synth.MODELS["qwen3-8b"]
+    for K in (0, 2048):
+        proposals = 0
+        for B in (1, 8, 64):
+            seed = synth.WORKLOADS[f"8b_b{B}"].input_seed
+            hid = torch.empty((B, 15, shape.hidden), dtype=torch.bfloat16, device="cuda")
+            s = torch.empty((B, 14, shape.proj_dim), dtype=torch.float32, device="cuda")
+            ver = torch.empty((B,), dtype=torch.int32, device="cuda")
+            ot = torch.empty((B, 15), dtype=torch.int32, device="cuda")
+            ol = torch.empty((B, 15), dtype=torch.float32, device="cuda")
+            G.log(f"[gpu-test] 8B graph == eager, K={K} B={B}, 20 trials")
+            for trial in range(20):
+                h_, s_, v_ = R.device_inputs(synth.make_inputs(shape, B, seed, 100 + trial))
+                hid.copy_(h_)
+                s.copy_(s_)
+                ver.copy_(v_)
+                te, le = h.run(hid, s, ver, K)
+                h.run(hid, s, ver, K, out_tokens=ot, out_top1=ol, graph=True)
+                torch.cuda.synchronize()
+                assert torch.equal(ot, te), (K, B, trial)
+                assert torch.equal(ol.view(torch.int32), le.view(torch.int32)), (K, B, trial)
+                proposals += te.numel()
+        assert proposals == 21900

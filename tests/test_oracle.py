@@ -37,12 +37,21 @@ def _rand_inputs(rng, B, V, H, r):
 
 
 def _check_against_brute(out, ref, tol=2e-5, min_margin=1e-3, steps=T):
-    """Tokens equal up to the first step with a near-tie; logits within tol there."""
+    """Tokens equal up to the first step with a near-tie; logits within tol there.
+
+    The top-2 margin (winner minus runner-up over the step's candidates) is
+    compared at every step up to and including that first near-tie step: it
+    decides where the GPU parity rule stops checking a chain, and, unlike the
+    winning id, it is a continuous function of the logits, so the fp32 and
+    float64 values agree within tol even where the two pick different ids."""
     B = len(ref["tokens"])
     checked = 0
     for b in range(B):
         for k in range(steps):
-            if ref["margin"][b][k] < min_margin:
+            mg, mr = float(out["margin"][b, k]), ref["margin"][b][k]
+            assert (math.isinf(mg) and math.isinf(mr)) or abs(mg - mr) <= tol, \
+                ("margin", b, k, mg, mr)
+            if mr < min_margin:
                 break
             assert out["tokens"][b, k] == ref["tokens"][b][k], (b, k)
             assert abs(float(out["top1"][b, k]) - ref["top1"][b][k]) <= tol, (b, k)
@@ -417,6 +426,73 @@ def _mut_cell_z_flipped(x, h, w_ih, w_hh):
     z = od._sigmoid(a[:, g:2 * g] + c[:, g:2 * g])
     n = np.tanh(a[:, 2 * g:] + r * c[:, 2 * g:])
     return z * n + (1 - z) * h                       # interpolation reversed
+
+
+def _margin_over_full_vocabulary(w, X, out, rec):
+    """A plausible mistake in a pool run: the runner-up taken over the whole
+    vocabulary's corrected logits instead of the request's pool."""
+    m = np.array(out["margin"], copy=True)
+    F2, b2 = w["fc2_w"], w["fc2_b"]
+    for k in range(1, T):
+        u = rec["u"][k - 1]
+        for b in range(X.shape[0]):
+            y = rec["base"][k, b] + (u[b] @ F2.T + b2)
+            win = int(out["tokens"][b, k])
+            m[b, k] = out["top1"][b, k] - np.delete(y, win).max()
+    return dict(out, margin=m)
+
+
+def _margin_second_distinct(out, rec):
+    """Another: the runner-up as the second distinct value (a tie then gives
+    a positive margin instead of 0)."""
+    m = np.array(out["margin"], copy=True)
+    for k in range(1, T):
+        for b, y in enumerate(rec["y"][k - 1]):
+            vals = np.unique(y)
+            m[b, k] = vals[-1] - vals[-2] if len(vals) > 1 else np.inf
+    return dict(out, margin=m)
+
+
+@pytest.mark.parametrize("K", [0, 6])
+def test_margin_matches_brute_force_and_catches_mistakes(K):
+    """Oracle margin = float64 brute-force margin at every compared step, for
+    the full vocabulary and a pool, including a planted exact tie (two ids
+    with identical lm_head and fc2 rows and bias), where it must be 0."""
+    rng = np.random.default_rng(33)
+    V, H, e, g, r, B = 40, 8, 4, 4, 4, 3
+    w = _rand_weights(rng, V, H, e, g, r, scale=2.0)
+    X, s, ver = _rand_inputs(rng, B, V, H, r)
+    wd = {k: v.astype(np.float64).tolist() for k, v in w.items()}
+    rec = {}
+    out = oracle.rollout(w, X, s, ver, K, record=rec)
+    ref = brute_rollout(wd, X.astype(np.float64).tolist(), s.astype(np.float64).tolist(), ver, K)
+    assert _check_against_brute(out, ref) >= 5
+    if K:
+        with pytest.raises(AssertionError, match="margin"):
+            _check_against_brute(_margin_over_full_vocabulary(w, X, out, rec), ref)
+    # planted tie: id 30 duplicates id 7 (lm_head, fc2, bias); hidden rows
+    # aligned with that lm_head row make the pair the winner at steps 3 and 9
+    w2 = {k: v.copy() for k, v in w.items()}
+    for n in ("lm_head", "fc2_w", "fc2_b"):
+        w2[n][30] = w2[n][7]
+    X2 = X.copy()
+    X2[:, 3] = 3.0 * w2["lm_head"][7]
+    X2[:, 9] = 3.0 * w2["lm_head"][7]
+    rec2 = {}
+    out2 = oracle.rollout(w2, X2, s, ver, K, record=rec2)
+    ref2 = brute_rollout({k: v.astype(np.float64).tolist() for k, v in w2.items()},
+                         X2.astype(np.float64).tolist(), s.astype(np.float64).tolist(), ver, K)
+    ties = 0
+    for b in range(B):
+        for k in (3, 9):
+            if out2["tokens"][b, k] in (7, 30):
+                assert out2["tokens"][b, k] == 7 and out2["margin"][b, k] == 0.0
+                assert ref2["tokens"][b][k] == 7 and ref2["margin"][b][k] == 0.0
+                ties += 1
+    assert ties >= B
+    _check_against_brute(out2, ref2, steps=3)
+    with pytest.raises(AssertionError, match="margin"):
+        _check_against_brute(_margin_second_distinct(out2, rec2), ref2, steps=4)
 
 
 @pytest.mark.parametrize("mutation", ["swapped_gates", "no_reset", "z_flipped", "s_shift",
