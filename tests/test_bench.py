@@ -88,3 +88,17 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_lower_bound_matches_the_byte_table():
+    """The block's roofline time from the algorithmic bytes: 8B B = 1 K = 0
+    about 0.72 ms (lm_head at HBM speed plus 14 fc2 passes and step
+    products), B = 64 K = 0 about 1.19 ms (the LM-head MFMA-bound)."""
+    import bench
+    from gru_corrected_draft_amd import synth
+    shape = synth.MODELS["qwen3-8b"]
+    lb1 = bench.lower_bound_ms(bench.algorithmic(shape, 1, 0), shape, 1, 0, 15)
+    lb64 = bench.lower_bound_ms(bench.algorithmic(shape, 64, 0), shape, 64, 0, 15)
+    assert 0.70 < lb1 < 0.74, lb1
+    assert 1.10 < lb64 < 1.25, lb64
+    assert bench.MATRIX[0] == ("8b_b1", 0) and len(bench.MATRIX) == 7
