@@ -56,6 +56,42 @@ struct GraphEntry {
   bool last_union, last_s_internal;
 };
 
+// Scratch of the allocation-free runs (domino_rollout_run_static): the
+// per-run buffers of a rollout (argmax words, bad-request flags, radix
+// histograms / state / chunk counts, GRU state and W_hh h ping-pong, u and its
+// bf16 planes, the fragment-ordered state, split partials) carved from one
+// file-scope device array instead of the handle's workspace.  Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in):
+// create() looks up its device address once per device with
+// hipGetSymbolAddress, and the runs use that address.
+constexpr size_t kStaticScratchBytes = (size_t)DOMINO_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, nullptr until looked up
+
+// once per device, with that device current
+bool static_scratch_init(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return false;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return true;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return false;
+  g_scratch_ptr[dev] = p;
+  return true;
+}
+
+void* static_scratch(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  return g_scratch_ptr[dev];
+}
+
+__global__ __launch_bounds__(256) void scratch_clear_kernel(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 constexpr int kPhases = 7;
 enum Phase { kLmHead = 0, kCorrect = 1, kGru = 2, kStep = 3, kPool = 4, kArgmax0 = 5, kOffsets = 6 };
 
@@ -192,6 +228,11 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
     set_global_err(std::string("create: device is ") + prop.gcnArchName + ", the library runs on gfx950 only");
     return DOMINO_ERR_UNSUPPORTED;
+  }
+
+  if (!static_scratch_init(dev)) {
+    set_global_err("create: looking up the static scratch array failed");
+    return DOMINO_ERR_HIP;
   }
 
   domino_rollout* h = new domino_rollout();
@@ -418,11 +459,10 @@ struct PhaseTimer {
 // One rollout producing the first P proposals (P = DOMINO_T: the whole block):
 // base logits, first proposal and pool of the whole block, then P - 1
 // correction steps.
-static void enqueue(domino_rollout_t* h, const void* hidden, const float* s, const int32_t* ver,
-                    const int32_t* forced, int B, int K, int P, int32_t* out_tokens,
-                    float* out_top1, hipStream_t st) {
+static void enqueue(domino_rollout_t* h, const Workspace& ws, const void* hidden, const float* s,
+                    const int32_t* ver, const int32_t* forced, int B, int K, int P,
+                    int32_t* out_tokens, float* out_top1, hipStream_t st) {
   const Shape& sh = h->shape;
-  const Workspace& ws = h->ws;
   const bool pool = K > 0 && K < sh.V;
   h->last_B = B;
   h->last_K = pool ? K : 0;
@@ -543,7 +583,7 @@ static domino_status_t run_common(domino_rollout_t* h, const void* hidden, const
   if (st != DOMINO_OK) return st;
   DeviceGuard dg(h->device);
   (void)hipGetLastError();  // clear a stale error of an unrelated call
-  enqueue(h, hidden, s, ver, forced, B, K, P, out_tokens, out_top1, (hipStream_t)stream);
+  enqueue(h, h->ws, hidden, s, ver, forced, B, K, P, out_tokens, out_top1, (hipStream_t)stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return h->fail(DOMINO_ERR_HIP, "run: kernel launch failed: %s", hipGetErrorString(e));
   h->err.clear();
@@ -567,6 +607,68 @@ extern "C" domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const 
   if (h && !forced_tokens) return h->fail(DOMINO_ERR_INVALID_ARG, "run_forced: forced_tokens is NULL");
   return run_common(h, base_hidden, step_s, verified_tokens, forced_tokens, batch, K, DOMINO_T,
                     out_tokens, out_top1_logit, stream);
+}
+
+// Carves the per-run buffers of a B-request run out of `base` (256-byte
+// aligned pieces) into ws and returns the bytes they take; with base ==
+// nullptr only the size is computed.
+static size_t carve_static(const domino_rollout_t* h, int B, Workspace& ws, unsigned char* base) {
+  const Shape& sh = h->shape;
+  const size_t V = sh.V, g = sh.g, r = sh.r, Bz = B;
+  const size_t nch = (V + kPoolChunk - 1) / kPoolChunk;
+  size_t off = 0;
+  auto take = [&](size_t bytes) -> void* {
+    void* p = base ? (void*)(base + off) : nullptr;
+    off += (bytes + 255) / 256 * 256;
+    return p;
+  };
+  ws.slots = (uint64_t*)take(DOMINO_T * Bz * 8);
+  ws.bad = (int32_t*)take(Bz * 4);
+  ws.hist = (uint32_t*)take(Bz * 3 * 2048 * 4);
+  ws.state = (uint32_t*)take(Bz * 8 * 4);
+  ws.counts = (uint32_t*)take(Bz * nch * 2 * 4);
+  ws.h[0] = (float*)take(Bz * g * 4);
+  ws.h[1] = (float*)take(Bz * g * 4);
+  ws.c[0] = (float*)take(Bz * 3 * g * 4);
+  ws.c[1] = (float*)take(Bz * 3 * g * 4);
+  ws.u = (float*)take(Bz * r * 4);
+  ws.u_hi = (uint16_t*)take(Bz * r * 2);
+  ws.u_lo = (uint16_t*)take(Bz * r * 2);
+  ws.hp = sh.bf16 ? (uint16_t*)take((Bz + 15) / 16 * 16 * g * 4) : nullptr;
+  ws.partial = (float*)take(step_partial_floats((int)g, (int)r) * sizeof(float));
+  return off;
+}
+
+extern "C" domino_status_t domino_rollout_run_static(domino_rollout_t* h, const void* base_hidden,
+                                                     const float* step_s,
+                                                     const int32_t* verified_tokens, int32_t batch,
+                                                     int32_t K, int32_t* out_tokens,
+                                                     float* out_top1_logit, void* stream) {
+  domino_status_t st = check_run_args(h, base_hidden, step_s, verified_tokens, batch, K, out_tokens);
+  if (st != DOMINO_OK) return st;
+  Workspace ws = h->ws;
+  const size_t need = carve_static(h, batch, ws, nullptr);
+  if (need > kStaticScratchBytes)
+    return h->fail(DOMINO_ERR_INVALID_ARG,
+                   "run_static: %d requests need %zu bytes of scratch, more than the %zu of the "
+                   "static array", batch, need, kStaticScratchBytes);
+  DeviceGuard dg(h->device);
+  unsigned char* base = (unsigned char*)static_scratch(h->device);
+  if (!base) return h->fail(DOMINO_ERR_UNSUPPORTED, "run_static: no static scratch on this device");
+  carve_static(h, batch, ws, base);
+  (void)hipGetLastError();
+  // the argmax words, flags and histograms must start at zero, whatever an
+  // earlier call on this device left (a fill kernel, so the call can be captured)
+  const size_t n16 = need / 16;
+  hipLaunchKernelGGL(scratch_clear_kernel, dim3((unsigned)std::min<size_t>((n16 + 255) / 256, 1024)),
+                     dim3(256), 0, (hipStream_t)stream, (uint4*)base, n16);
+  enqueue(h, ws, base_hidden, step_s, verified_tokens, nullptr, batch, K, DOMINO_T, out_tokens,
+          out_top1_logit, (hipStream_t)stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return h->fail(DOMINO_ERR_HIP, "run_static: kernel launch failed: %s", hipGetErrorString(e));
+  h->err.clear();
+  return DOMINO_OK;
 }
 
 static domino_status_t run_graph_common(domino_rollout_t* h, const void* base_hidden,
@@ -607,7 +709,7 @@ static domino_status_t run_graph_common(domino_rollout_t* h, const void* base_hi
       return h->fail(DOMINO_ERR_HIP, "run_graph: begin capture failed");
     }
     h->capturing = true;
-    enqueue(h, base_hidden, step_s, verified_tokens, nullptr, batch, kmode, P, out_tokens,
+    enqueue(h, h->ws, base_hidden, step_s, verified_tokens, nullptr, batch, kmode, P, out_tokens,
             out_top1_logit, h->capture_stream);
     h->capturing = false;
     hipError_t e1 = hipGetLastError();

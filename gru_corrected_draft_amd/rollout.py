@@ -31,7 +31,9 @@ EXPORTED = ("domino_rollout_create", "domino_rollout_run", "domino_rollout_run_g
             "domino_rollout_read_workspace", "domino_rollout_destroy",
             "domino_rollout_last_error", "domino_rollout_set_timing",
             "domino_rollout_kernel_times", "domino_rollout_set_pool_strategy",
-            "domino_rollout_set_step_path", "domino_rollout_cached_graphs")
+            "domino_rollout_set_step_path", "domino_rollout_cached_graphs",
+            "domino_rollout_run_static")
+STATIC_SCRATCH_BYTES = 4 << 20  # DOMINO_STATIC_SCRATCH_BYTES
 GRAPH_CACHE_MAX = 16  # DOMINO_GRAPH_CACHE_MAX
 # gru: the GRU gates (prefix launch, separate gate kernel); step: projector
 # layer 1 and W_hh of the new state (with the gates where fused)
@@ -80,6 +82,8 @@ def load_library():
     lib.domino_rollout_run.restype = ctypes.c_int
     lib.domino_rollout_run_graph.argtypes = run_args
     lib.domino_rollout_run_graph.restype = ctypes.c_int
+    lib.domino_rollout_run_static.argtypes = run_args
+    lib.domino_rollout_run_static.restype = ctypes.c_int
     lib.domino_rollout_run_prefix.argtypes = [vp, vp, f32p, i32p, i32, i32, i32, i32p, f32p, i32,
                                               vp]
     lib.domino_rollout_run_prefix.restype = ctypes.c_int
@@ -192,9 +196,11 @@ class DominoRollout:
             raise DominoError(st, self.lib.domino_rollout_last_error(self.handle).decode())
 
     def run(self, hidden, step_s, verified, K, out_tokens=None, out_top1=None, graph=False,
-            forced=None, stream=None, proposals=None):
+            forced=None, stream=None, proposals=None, static=False):
         """Enqueue one rollout; returns (out_tokens [B,P] int32, out_top1 [B,P] fp32),
-        P = 15, or `proposals` for a truncated rollout (domino_rollout_run_prefix)."""
+        P = 15, or `proposals` for a truncated rollout (domino_rollout_run_prefix).
+        static=True runs domino_rollout_run_static (per-run scratch in the
+        library's static device array)."""
         import torch
         B = hidden.shape[0]
         V, H, e, g, r = self.shape
@@ -221,7 +227,13 @@ class DominoRollout:
             check_forced(forced, B, dev)
         st_ptr = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream if stream is None
                                  else stream)
-        if proposals is not None:
+        if static:
+            if proposals is not None or forced is not None or graph:
+                raise ValueError("the static-scratch run is a plain full-block run")
+            st = self.lib.domino_rollout_run_static(self.handle, _ptr(hidden), _ptr(step_s),
+                                                    _ptr(verified), B, K, _ptr(out_tokens),
+                                                    _ptr(out_top1), st_ptr)
+        elif proposals is not None:
             if forced is not None:
                 raise ValueError("teacher forcing runs the whole block")
             st = self.lib.domino_rollout_run_prefix(self.handle, _ptr(hidden), _ptr(step_s),

@@ -243,6 +243,34 @@ domino_status_t domino_rollout_set_pool_strategy(domino_rollout_t* h, int32_t st
 domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int32_t which, double* total_ms,
                                             int64_t* launches);
 
+/* Size of the library's static scratch array on each device (bytes). */
+#define DOMINO_STATIC_SCRATCH_BYTES (4u << 20)
+
+/* For callers that cannot allocate device memory at run time (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same rollout as domino_rollout_run (same kernels, bit-identical
+ * results), whose per-run scratch -- argmax words, bad-request flags, radix
+ * histograms / state / chunk counts, GRU state and W_hh h, u and its bf16
+ * planes, the fragment-ordered state and split partials -- lives in one
+ * static device array of DOMINO_STATIC_SCRATCH_BYTES that the library holds
+ * on every device it runs on until the process ends, instead of the
+ * handle's workspace.  The call allocates nothing; the handle (created
+ * beforehand, which does allocate) still holds the base logits, pool and
+ * the tables formed at create.  Each call first clears the part of the array
+ * it uses with a fill kernel, then enqueues the rollout on `stream`.  Every
+ * call on one device shares that device's array: calls whose work overlaps
+ * on one device (other streams, other handles, other threads) race and give
+ * undefined results; serialise them.  The scratch needed grows with the
+ * batch (about 70 KB per request plus 1 MB at g = r = 1024, so up to ~44
+ * requests there); a batch whose scratch exceeds the array is
+ * DOMINO_ERR_INVALID_ARG and nothing is launched.  Other arguments and
+ * errors as domino_rollout_run (DOMINO_ERR_UNSUPPORTED if the array's
+ * device address could not be looked up at create). */
+domino_status_t domino_rollout_run_static(domino_rollout_t* h, const void* base_hidden,
+                                          const float* step_s, const int32_t* verified_tokens,
+                                          int32_t batch, int32_t K, int32_t* out_tokens,
+                                          float* out_top1_logit, void* stream);
+
 /* Number of graphs the handle has cached (0..DOMINO_GRAPH_CACHE_MAX) in
  * *count.  INVALID_ARG for a NULL handle or count. */
 domino_status_t domino_rollout_cached_graphs(const domino_rollout_t* h, int32_t* count);
