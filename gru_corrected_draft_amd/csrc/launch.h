@@ -223,6 +223,14 @@ bool lmhead_xfrag_possible(int max_batch, int H);
 size_t lmhead_xfrag_elems(int B, int H);
 
 void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int B, hipStream_t st);
+// One-request LM-head with whole-line lm_head loads (lmhead_one.hip): base
+// logits [15, 1, V], the pool score keys (when keys is not nullptr) and the
+// first-proposal argmax word *slot0; bf16, H a multiple of 1024 up to 5120
+// and V small enough for one CU's share of tiles to stay in LDS.
+bool lmhead_one_supported(int V, int H);
+void lmhead_one_prepare();
+void launch_lmhead_one(const uint16_t* W, const uint16_t* X, float* out, uint32_t* keys,
+                       uint64_t* slot0, int V, int H, hipStream_t st);
 void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st);
 // Whether a pool correction of B requests streams each request group's
 // union of pool rows once (instead of gathering every request's rows).

@@ -343,6 +343,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   std::call_once(once, [] {
     rowstream_prepare();
     lmhead_fused_prepare();
+    lmhead_one_prepare();
     step_prepare();
   });
   // GRU input projection of every id, G[v, :] = W_ih E[v], the stacked step
@@ -475,7 +476,13 @@ static void enqueue(domino_rollout_t* h, const Workspace& ws, const void* hidden
     s = ws.s;
   }
   const bool fused = sh.bf16 && B >= kFusedMinBatch && lmhead_fused_supported(sh.H);
-  if (fused) {
+  const bool one = sh.bf16 && B == 1 && lmhead_one_supported(sh.V, sh.H);
+  if (one) {
+    // base logits, pool-score keys and the first proposal in one pass
+    PhaseTimer t(h, kLmHead, st);
+    launch_lmhead_one((const uint16_t*)h->w.lm_head, (const uint16_t*)hidden, ws.base,
+                      pool ? ws.keys : nullptr, ws.slots, sh.V, sh.H, st);
+  } else if (fused) {
     // base logits, pool-score keys and the first proposal in one pass
     PhaseTimer t(h, kLmHead, st);
     FusedArgs fa{(const uint16_t*)h->w.lm_head, (const uint16_t*)hidden, ws.base,
@@ -491,7 +498,7 @@ static void enqueue(domino_rollout_t* h, const Workspace& ws, const void* hidden
   }
   if (pool) {
     PhaseTimer t(h, kPool, st);
-    launch_pool_build(sh, ws, h->w.fc2_b, B, K, fused, st);
+    launch_pool_build(sh, ws, h->w.fc2_b, B, K, fused || one, st);
   }
   // Prefix: h(1) = GRU(E[verified], 0) and c(1) = W_hh h(1).  It runs for
   // every P: its gates are where an invalid verified token is flagged.

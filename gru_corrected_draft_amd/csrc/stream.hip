@@ -27,6 +27,13 @@ enum { kEpiStore = 0, kEpiArgmax = 1, kEpiUnion = 2 };
 constexpr int kUnionUnitRows = 32;  // rows per unit of the union stream (two 16-row tiles)
 
 constexpr int kSC = 128;  // k per super-chunk (4 MFMA k-slices of 32)
+// Padding (bf16 elements) after each activation-panel row in LDS.  With 16
+// elements (32 B) the rows of a 1024- or 2048-wide panel start 8 banks apart
+// and the 16-byte fragment reads of 16 rows x 4 chunks hit distinct banks; a
+// probe of exactly this read pattern counted half of the LDS-active cycles
+// as bank conflicts with an 8-element pad and none with 16 (30.5 against
+// 32.5 cycles per read at four waves per CU).
+constexpr int kPanelPad = 16;
 constexpr bool kStraightWalk = true;
 
 // Row spreading (SP, the one-request LM-head).  A 16-row tile T normally
@@ -47,7 +54,7 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
   const int N = a.N, K = a.K, KS = a.KS;
-  const int ldsrow = KS + 8;  // 16-byte pad per panel row
+  const int ldsrow = KS + kPanelPad;
   // Column groups of NB*16 activation columns: the a.groups blocks that
   // share one set of weight rows are consecutive on one XCD (blocks j and
   // j + 8 land on the same XCD), so all but the first read their tiles from
@@ -270,7 +277,7 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
   const int lane = threadIdx.x & 63, wave = wave_index();
   const int row = lane & 15, q = lane >> 4;
   const int K = a.K, G = a.groups;
-  const int ldsrow = K + 8;
+  const int ldsrow = K + kPanelPad;
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int grp = local % G;
   const int N = EPI == kEpiUnion ? a.un[grp] : a.N;  // >= 1
@@ -579,7 +586,7 @@ void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
 
 // panel bytes of one group of `cols` columns over all of K
 size_t persist_lds(int K, int cols, bool split) {
-  return (size_t)(split ? 2 : 1) * cols * (K + 8) * sizeof(bf16_t);
+  return (size_t)(split ? 2 : 1) * cols * (K + kPanelPad) * sizeof(bf16_t);
 }
 
 // gcols: activation columns per group (at most NB * 16)
@@ -606,7 +613,7 @@ void launch_t(StreamArgs a, hipStream_t st) {
   const int rowblocks = (waves + 3) / 4;
   const int cols = min(a.ncols, NB * 16);
   a.groups = (a.ncols + NB * 16 - 1) / (NB * 16);
-  const size_t lds = (size_t)(SPLIT ? 2 : 1) * cols * (a.KS + 8) * sizeof(bf16_t);
+  const size_t lds = (size_t)(SPLIT ? 2 : 1) * cols * (a.KS + kPanelPad) * sizeof(bf16_t);
   DLAUNCH((rowstream_kernel<NB, RT, SPLIT, EPI, D, SP>),
                      dim3(8 * a.groups * ((rowblocks + 7) / 8)), dim3(256), lds, st, a);
 }
@@ -615,7 +622,7 @@ void launch_t(StreamArgs a, hipStream_t st) {
 int pick_slice(int K, int ncols, int planes, int budget) {
   int best = 128;
   for (int ks = 128; ks <= K; ks += 128)
-    if (K % ks == 0 && (size_t)planes * ncols * (ks + 8) * 2 <= (size_t)budget) best = ks;
+    if (K % ks == 0 && (size_t)planes * ncols * (ks + kPanelPad) * 2 <= (size_t)budget) best = ks;
   return best;
 }
 

@@ -142,13 +142,14 @@ SMALL = synth.custom_shape(5003, 256, 128, 128, 128, "bf16", 91, name="tie-bf16"
 DEEP = synth.custom_shape(3001, 1024, 256, 256, 256, "bf16", 92, name="tie-bf16-deep")
 TINY = synth.custom_shape(4096, 256, 128, 128, 128, "fp32", 93, name="tie-fp32")
 
-# (shape, batch, pool strategy): every LM-head kernel (row stream at 1, the
-# 32x32 kernel at 8 and 14, line copies at 40, register operands at 64), the
+# (shape, batch, pool strategy): every LM-head kernel (row stream at 1 for
+# H = 256, the whole-line one-request kernel at 1 for H = 1024, the 32x32
+# kernel at 8 and 14, line copies at 40, register operands at 64), the
 # full-vocabulary stream (row-major up to 16, tile order above), and each
 # pool reader (whole-line gather up to 12, split at 14, gather above 16,
 # group unions at r = 256)
 CASES = [(SMALL, 1, 0), (SMALL, 8, 0), (SMALL, 14, 0), (SMALL, 40, 1), (DEEP, 64, 2),
-         (DEEP, 64, 1), (TINY, 1, 0)]
+         (DEEP, 64, 1), (TINY, 1, 0), (DEEP, 1, 0)]
 
 
 def _pairs(shape):
