@@ -228,6 +228,7 @@ void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int
 // first-proposal argmax word *slot0; bf16, H a multiple of 1024 up to 5120
 // and V small enough for one CU's share of tiles to stay in LDS.
 bool lmhead_one_supported(int V, int H);
+int cu_count();
 void lmhead_one_prepare();
 void launch_lmhead_one(const uint16_t* W, const uint16_t* X, float* out, uint32_t* keys,
                        uint64_t* slot0, int V, int H, hipStream_t st);

@@ -332,6 +332,9 @@ __global__ __launch_bounds__(256) void lmhead_lines_kernel(FusedArgs a) {
 }
 
 // ------------------------------------------------- 32x32x16 matrix products
+// 9 to 24 requests (and up to 8 when H is not a multiple of 128, which the
+// vocabulary-range kernel below needs).
+//
 // A workgroup computes 256 vocabulary rows against 8 requests x 16 draft
 // positions (position 15 is padding: its rows repeat position 14 and are
 // dropped).  The activation rows are the A operand and the lm_head rows the
@@ -521,6 +524,230 @@ __global__ __launch_bounds__(256) void lmhead_m32_kernel(FusedArgs a) {
   if (threadIdx.x < kMR && b0 + (int)threadIdx.x < B) {
     const int r = threadIdx.x;
     publish_max(&a.slots[b0 + r], umax64(umax64(wb[0][r], wb[1][r]), umax64(wb[2][r], wb[3][r])));
+  }
+}
+
+// One 64-wide k stage of the m32 products from LDS: per 16-wide k step TV
+// lm_head and 4 activation fragments, read as one stream kMWindow reads
+// ahead of the products (the scheduling barriers keep it).
+template <int TV>
+__device__ __forceinline__ void m32_products(const unsigned char* wsb, const unsigned char* xsb,
+                                             int fhi, int fsw, v16f (&acc)[4][TV]) {
+  constexpr int kPer = TV + 4;
+  constexpr int kF = kPer * (kMK / 16);
+  v8s fr[kF];
+  int issued = 0;
+#pragma unroll
+  for (int k16 = 0; k16 < kMK / 16; ++k16) {
+    const int upto = min(k16 * kPer + kPer - 1 + kMWindow, kF - 1);
+#pragma unroll
+    for (int k = 0; k < kF; ++k)
+      if (k >= issued && k <= upto) {
+        const int kk = k / kPer, idx = k % kPer;
+        const int cofs = ((2 * kk + fhi) ^ fsw) * 16;
+        fr[k] = idx < TV ? *reinterpret_cast<const v8s*>(wsb + idx * 4096 + cofs)
+                         : *reinterpret_cast<const v8s*>(xsb + (idx - TV) * 4096 + cofs);
+      }
+    issued = max(issued, upto + 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+      for (int tv = 0; tv < TV; ++tv)
+        acc[ta][tv] = mfma32(fr[k16 * kPer + TV + ta], fr[k16 * kPer + tv], acc[ta][tv]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Epilogue of one chunk of the range kernel (requests 0..7, the wave's TV
+// tiles from vocabulary row vw): pool score keys, the lane's running
+// position-0 argmax per request and the base logits; clears the
+// accumulators.  A lane holds positions 4 hh + {0, 1, 2, 3, 8, 9, 10, 11} of
+// its (request, id): one guarded run of stores at fixed position strides per
+// request, position 15 (the padding row, hh = 1) never stored.
+template <int TV>
+__device__ __forceinline__ void range_epilogue(const FusedArgs& a, v16f (&acc)[4][TV], int vw,
+                                               int rend, int vl, int hh,
+                                               uint64_t (&best)[kMR]) {
+  // opaque copies, so the store addresses are formed here and not hoisted
+  // out of the stage loop (where they would hold some 200 registers)
+  int V = a.V, B = a.B;
+  asm volatile("" : "+s"(V), "+s"(B));
+  const size_t pstride = (size_t)B * V;  // elements from one position to the next
+#pragma unroll
+  for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+    for (int tv = 0; tv < TV; ++tv) {
+      const int v = vw + tv * 32 + vl;
+      const bool vok = v < rend;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int req = 2 * ta + jj;
+        const bool ok = vok && req < B;
+        if (a.keys) {
+          float m = acc[ta][tv][jj * 8];
+#pragma unroll
+          for (int ii = 1; ii < 7; ++ii) m = fmaxf(m, acc[ta][tv][jj * 8 + ii]);
+          if (hh == 0) m = fmaxf(m, acc[ta][tv][jj * 8 + 7]);
+          m = fmaxf(m, __shfl_xor(m, 32, 64));
+          if (hh == 0 && ok) a.keys[(size_t)req * V + v] = orderable(m);
+        }
+        const uint64_t k0 = pack_key(acc[ta][tv][jj * 8], (uint32_t)v);  // position 0 on hh == 0
+        best[req] = (hh == 0 && vok) ? umax64(best[req], k0) : best[req];
+        if (ok) {
+          float* o = a.base + (size_t)req * V + v + (size_t)(4 * hh) * pstride;
+#pragma unroll
+          for (int ii = 0; ii < 7; ++ii)
+            o[(size_t)(8 * (ii >> 2) + (ii & 3)) * pstride] = acc[ta][tv][jj * 8 + ii];
+          if (hh == 0) o[11 * pstride] = acc[ta][tv][jj * 8 + 7];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[ta][tv][i] = 0.f;
+    }
+}
+
+// Up to 8 requests: vocabulary ranges, producer and consumer waves.
+//
+// One workgroup per compute unit owns a contiguous range of 32-row vocabulary
+// tiles (ranges differ by at most one tile, so every CU streams the same
+// share of lm_head; a grid of 128-row tiles leaves part of the chip idle in
+// its last round) and walks it in chunks of 4 TV tiles with the m32
+// kernel's products, LDS layout and epilogue.  Waves 4..7 produce: they
+// stage both operands through registers (a load-only probe streamed
+// lm_head-shaped rows at 1.8-3.7 TB/s through direct global->LDS copies,
+// 6.1 TB/s through registers) into two LDS slots, two k stages ahead.
+// Waves 0..3 consume: each owns TV tiles of a chunk against all 8 requests
+// and takes one stage's products from LDS per barrier, so the matrix cores
+// work while the producers' loads are in flight.  (With every wave doing
+// both, a stage's products and loads ran one after the other: 8B B = 8
+// 338 against 279 us.)  The chunks form one flat sequence of stages, so the
+// next chunk's first two stages are loading during a chunk's epilogue.
+// Rows past the range (the last chunk's missing tiles) re-read the range's
+// first row, an L2 hit, instead of branching around the load.  Each
+// consumer lane keeps its position-0 maxima across chunks; the workgroup
+// publishes one word per request at the end.
+template <int TV>
+__global__ __launch_bounds__(512) void lmhead_range_kernel(FusedArgs a) {
+  using C = M32<TV>;
+  constexpr int kMV = C::kMV, kMVStage = C::kVStage, kMVCopies = C::kVCopies;
+  const int V = a.V, H = a.H, B = a.B;
+  const int nt = (V + 31) / 32, G = gridDim.x, g = blockIdx.x;
+  const int t0 = (int)((long long)g * nt / G), t1 = (int)((long long)(g + 1) * nt / G);
+  if (t1 <= t0) return;  // uniform per workgroup, before any barrier
+  const int r0 = t0 * 32, rend = min(t1 * 32, V);
+  const int nchunk = (t1 - t0 + 4 * TV - 1) / (4 * TV);
+  const int ns = H / kMK, nq = nchunk * ns;
+  extern __shared__ __align__(1024) unsigned char ring[];
+  unsigned char* const wring = ring;
+  unsigned char* const xring = ring + 2 * kMVStage;
+  const int lane = threadIdx.x & 63, wave = wave_index(), w4 = wave & 3;
+  __shared__ uint64_t wb[4][kMR];  // each consumer wave's position-0 maxima
+
+  if (wave >= 4) {
+    // ---- producer wave w4: lm_head blocks w4 + 4i of 8 chunk rows and
+    // activation blocks w4 + 4i of 8 rows; lane (rr, pp) fetches logical
+    // 16-byte chunk pp ^ ((r >> 1) & 7) of row rr of its block
+    const int rr = lane >> 3, pp = lane & 7;
+    const u32x4* const Wv = reinterpret_cast<const u32x4*>(a.W);
+    const u32x4* const Xv = reinterpret_cast<const u32x4*>(a.X);
+    const uint32_t hrow = (uint32_t)H / 8;  // 16-byte units per row
+    uint32_t wsc[kMVCopies], xoff[kMXCopies];
+#pragma unroll
+    for (int i = 0; i < kMVCopies; ++i) {
+      const int r = ((w4 + 4 * i) & 3) * 8 + rr;
+      wsc[i] = (uint32_t)(pp ^ ((r >> 1) & 7));
+    }
+#pragma unroll
+    for (int i = 0; i < kMXCopies; ++i) {
+      const int R = (w4 + 4 * i) * 8 + rr;  // activation row of the group
+      const int req = min(R >> 4, B - 1);
+      const int pos = min(R & 15, DOMINO_T - 1);
+      xoff[i] = ((uint32_t)req * DOMINO_T + (uint32_t)pos) * hrow + (uint32_t)(pp ^ (((R & 31) >> 1) & 7));
+    }
+    u32x4 AW[kMVCopies], AX[kMXCopies], BW[kMVCopies], BX[kMXCopies];
+    // stage Q (clamped to the last: those loads refill a set nobody reads)
+#define RANGE_LOAD(RW, RX, Q)                                                       \
+  {                                                                                 \
+    const int q_ = min((Q), nq - 1), c_ = q_ / ns, s_ = q_ - c_ * ns;               \
+    const int rc_ = r0 + c_ * kMV + rr;                                             \
+    _Pragma("unroll") for (int i = 0; i < kMVCopies; ++i) {                         \
+      const int v_ = rc_ + (w4 + 4 * i) * 8;                                        \
+      RW[i] = Wv[(uint32_t)(v_ < rend ? v_ : r0) * hrow + wsc[i] + 8u * s_];        \
+    }                                                                               \
+    _Pragma("unroll") for (int i = 0; i < kMXCopies; ++i) RX[i] = Xv[xoff[i] + 8u * s_]; \
+  }
+#define RANGE_PUT(RW, RX, SLOT)                                                     \
+  {                                                                                 \
+    unsigned char* ws_ = wring + (SLOT) * kMVStage + lane * 16;                     \
+    unsigned char* xs_ = xring + (SLOT) * kMXStage + lane * 16;                     \
+    _Pragma("unroll") for (int i = 0; i < kMVCopies; ++i)                           \
+      *reinterpret_cast<u32x4*>(ws_ + (w4 + 4 * i) * 1024) = RW[i];                 \
+    _Pragma("unroll") for (int i = 0; i < kMXCopies; ++i)                           \
+      *reinterpret_cast<u32x4*>(xs_ + (w4 + 4 * i) * 1024) = RX[i];                 \
+  }
+    RANGE_LOAD(AW, AX, 0)
+    RANGE_LOAD(BW, BX, 1)
+    RANGE_PUT(AW, AX, 0)
+    __syncthreads();
+    // in the stage that the consumers take from one slot, stage Q + 1 (set
+    // NW/NX, loaded one stage earlier) goes into the other slot, whose stage
+    // Q - 1 they finished before the last barrier, and stage Q + 2 into set
+    // CW/CX, whose stage Q is in LDS
+    for (int q = 0; q < nq; q += 2) {  // nq is even
+      RANGE_LOAD(AW, AX, q + 2)
+      __builtin_amdgcn_sched_barrier(0);  // the loads go out before the wait for the other set
+      RANGE_PUT(BW, BX, 1)
+      __syncthreads();
+      RANGE_LOAD(BW, BX, q + 3)
+      __builtin_amdgcn_sched_barrier(0);
+      RANGE_PUT(AW, AX, 0)
+      __syncthreads();
+    }
+#undef RANGE_PUT
+#undef RANGE_LOAD
+    wait_vm<0>();  // the clamped loads past the last stage
+    __syncthreads();
+  } else {
+    // ---- consumer wave w4: vocabulary tiles w4 TV .. w4 TV + TV - 1 of each
+    // chunk against all 8 requests
+    uint64_t best[kMR];
+#pragma unroll
+    for (int r = 0; r < kMR; ++r) best[r] = 0;
+    v16f acc[4][TV];
+#pragma unroll
+    for (int ta = 0; ta < 4; ++ta)
+#pragma unroll
+      for (int tv = 0; tv < TV; ++tv)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[ta][tv][i] = 0.f;
+    const int frow = lane & 31, fhi = lane >> 5, fsw = (frow >> 1) & 7;
+    const unsigned char* const wsb = wring + w4 * (TV * 4096) + frow * 128;
+    const unsigned char* const xsb = xring + frow * 128;
+    __syncthreads();
+    for (int c = 0; c < nchunk; ++c) {
+      for (int s = 0; s < ns; s += 2) {  // ns is even: every chunk starts in slot 0
+        m32_products<TV>(wsb, xsb, fhi, fsw, acc);
+        __syncthreads();
+        m32_products<TV>(wsb + kMVStage, xsb + kMXStage, fhi, fsw, acc);
+        __syncthreads();
+      }
+      range_epilogue<TV>(a, acc, r0 + c * kMV + w4 * (TV * 32), rend, lane & 31, lane >> 5, best);
+    }
+#pragma unroll
+    for (int r = 0; r < kMR; ++r) {
+      const uint64_t m = wave_max_u64(best[r]);
+      if (lane == 0) wb[w4][r] = m;
+    }
+    __syncthreads();
+  }
+
+  // one publication per request and workgroup: the words of all workgroups
+  // meet in eight words of memory, and per-chunk publications by every
+  // wave of every CU at nearly the same moment serialise there
+  if (threadIdx.x < kMR && (int)threadIdx.x < B) {
+    const int r = threadIdx.x;
+    publish_max(&a.slots[r], umax64(umax64(wb[0][r], wb[1][r]), umax64(wb[2][r], wb[3][r])));
   }
 }
 
@@ -751,6 +978,18 @@ __global__ __launch_bounds__(64 * 16 / TA) void lmhead_xf_kernel(FusedArgs a) {
 // workgroup count where lm_head streaming, not the products, bounds the time
 constexpr int kM32SmallBatch = 8;
 
+template <int TV>
+constexpr size_t kRangeLds = 2 * ((size_t)M32<TV>::kVStage + kMXStage);  // 64 / 128 KB
+// The range kernel's chunk is 4 TV tiles of 32 rows: one tile per consumer
+// wave (five chunks of an 8B range of 18-19 tiles) up to 4 requests, three
+// from 5 (two chunks: fewer epilogues and activation passes, which cost
+// more than the last chunk's idle tiles once the epilogue stores grow).
+// 8B LM-head us, TV = 1 / 3: B = 2 252 / 256, 3 250 / 256, 4 256 / 257,
+// 5 261 / 260, 6 264 / 261, 7 271 / 263, 8 279 / 267.
+constexpr int kRangeSmallBatch = 4;
+// the stage loops run in pairs of 64-wide k stages
+bool lmhead_range_supported(int H) { return H % (2 * kMK) == 0; }
+
 constexpr size_t kLds = (size_t)kStages * kSliceBytes;
 // line-copy kernel whenever H is a multiple of its 64-wide stage
 
@@ -762,6 +1001,10 @@ void lmhead_fused_prepare() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)M32<2>::kLds);
   (void)hipFuncSetAttribute((const void*)lmhead_m32_kernel<1>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)M32<1>::kLds);
+  (void)hipFuncSetAttribute((const void*)lmhead_range_kernel<1>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRangeLds<1>);
+  (void)hipFuncSetAttribute((const void*)lmhead_range_kernel<3>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRangeLds<3>);
   (void)hipFuncSetAttribute((const void*)lmhead_fused_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
   (void)hipFuncSetAttribute((const void*)lmhead_lines_kernel,
@@ -807,7 +1050,13 @@ void launch_lmhead_fused(const FusedArgs& a, hipStream_t st) {
   }
   if (a.B <= kM32MaxBatch && a.H % kMK == 0 && offsets32) {
     const int ngrp = (a.B + kMR - 1) / kMR;
-    if (a.B <= kM32SmallBatch) {
+    if (a.B <= kMR && lmhead_range_supported(a.H)) {
+      const int grid = min((a.V + 31) / 32, cu_count());
+      if (a.B <= kRangeSmallBatch)
+        DLAUNCH(lmhead_range_kernel<1>, dim3(grid), dim3(512), kRangeLds<1>, st, a);
+      else
+        DLAUNCH(lmhead_range_kernel<3>, dim3(grid), dim3(512), kRangeLds<3>, st, a);
+    } else if (a.B <= kM32SmallBatch) {
       const int nvt = (a.V + M32<1>::kMV - 1) / M32<1>::kMV;
       DLAUNCH(lmhead_m32_kernel<1>, dim3(8 * ((nvt + 7) / 8) * ngrp), dim3(256), M32<1>::kLds, st,
               a);

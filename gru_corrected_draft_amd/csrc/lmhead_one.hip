@@ -201,21 +201,10 @@ size_t one_lds(int wv, int maxt) {
 }
 constexpr size_t kOneLdsLimit = 156 * 1024;  // dynamic LDS (the static part is WV words)
 
-int one_cus() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      cus = 256;
-  }
-  return cus;
-}
-
 // one workgroup per CU, each a contiguous range of at most maxt tiles
 void one_grid(int V, int* grid, int* maxt) {
   const int S = (V + 15) / 16;
-  *grid = min(S, one_cus());
+  *grid = min(S, cu_count());
   *maxt = (S + *grid - 1) / *grid;
 }
 
@@ -229,6 +218,19 @@ void one_launch(const uint16_t* W, const uint16_t* X, float* out, uint32_t* keys
 }
 
 }  // namespace
+
+// compute units of the current device (queried once; the grids sized with it
+// only set how work is divided, never what is computed)
+int cu_count() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 256;
+  }
+  return cus;
+}
 
 // waves per workgroup and k steps per wave for hidden width H (a wave owns
 // 512 of K: 64 VGPRs of activations and 64 of one tile's loads)

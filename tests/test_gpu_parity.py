@@ -112,6 +112,31 @@ def test_lmhead_with_many_activation_slices(B, K):
             assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
 
 
+RANGES = synth.custom_shape(40003, 512, 128, 128, 128, "bf16", 81, name="small-bf16-ranges")
+ODD_K = synth.custom_shape(5003, 576, 128, 128, 128, "bf16", 82, name="small-bf16-odd-k")
+
+
+@pytest.mark.parametrize("shape,B,K", [(RANGES, 2, 0), (RANGES, 4, 300), (RANGES, 5, 0),
+                                       (RANGES, 8, 300), (ODD_K, 3, 0), (ODD_K, 6, 100)])
+def test_lmhead_vocabulary_ranges(shape, B, K):
+    """Up to 8 requests the LM-head gives each CU a contiguous range of
+    32-row vocabulary tiles: 1251 tiles over the CUs (ranges of 4-5 tiles),
+    the last tile 3 rows; chunks of 4 tiles up to 4 requests (a second,
+    partial chunk) and of 12 from 5 (one partial chunk).  H = 576 (nine
+    64-wide stages, an odd count) takes the 128-row tile kernel instead."""
+    G.log(f"[gpu-test] vocabulary ranges {shape.name} B={B} K={K}")
+    tok, top, h = G.gpu_run(shape, B, 900 + B, 0, K, max_batch=8, max_k=2048)
+    ref = G.oracle_run(shape, B, 900 + B, 0, K)
+    compare(tok, top, ref, TOL["bf16"])
+    base = h.read_workspace(0).cpu().numpy().reshape(15, B, -1)
+    want = ref_base(shape, B, 900 + B, 0)
+    assert np.max(np.abs(base - want)) < 1e-4
+    if 0 < K < shape.vocab:
+        ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
+        for b in range(B):
+            assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
+
+
 WIDE = synth.custom_shape(2053, 256, 512, 512, 512, "bf16", 79, name="small-bf16-wide")
 
 
