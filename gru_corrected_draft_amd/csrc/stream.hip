@@ -564,13 +564,11 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
 
 template <int NB, int RT, int D, bool VEC, bool SPLIT, int EPI, int WV, bool PK = false>
 void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
-  static int per_cu = -1, cus = 0;  // resident blocks per CU at this panel size
+  static int per_cu = -1;  // resident blocks per CU at this panel size
   static size_t per_cu_lds = 0;
   if (per_cu < 0 || per_cu_lds != lds) {
     per_cu_lds = lds;
-    int dev = 0, n = 0;
-    (void)hipGetDevice(&dev);
-    (void)hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
             &n, rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI, WV, PK>, WV * 64, lds) != hipSuccess)
       n = 1;
@@ -578,7 +576,7 @@ void launch_persist_t(const StreamArgs& a, size_t lds, hipStream_t st) {
   }
   // a multiple of 8 * groups blocks, about one wave of resident blocks
   const int unit = 8 * a.groups;
-  const int want = (cus > 0 ? cus : 256) * per_cu;
+  const int want = cu_count() * per_cu;
   const int grid = ((want + unit - 1) / unit) * unit;
   DLAUNCH((rowpersist_kernel<NB, RT, D, VEC, SPLIT, EPI, WV, PK>), dim3(grid), dim3(WV * 64), lds,
           st, a);
@@ -689,14 +687,7 @@ void dispatch_argmax(StreamArgs a, hipStream_t st) {
 // launch can choose (one block per CU).
 constexpr size_t kUnionLdsLimit = 156 * 1024;
 int union_units_per_wave(int groups, int ubound) {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus < 1)
-      cus = 256;
-  }
+  const int cus = cu_count();
   const int unit = 8 * groups;
   const int parts = ((cus + unit - 1) / unit) * unit / groups;
   const int units = ((ubound + 15) / 16 + kArgmaxRT - 1) / kArgmaxRT;
