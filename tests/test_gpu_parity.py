@@ -137,6 +137,29 @@ def test_lmhead_vocabulary_ranges(shape, B, K):
             assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
 
 
+TINY_V = synth.custom_shape(37, 256, 128, 128, 128, "bf16", 83, name="bf16-vocab-37")
+
+
+@pytest.mark.parametrize("B", [1, 3, 8, 12, 17, 40, 64])
+def test_tiny_vocabulary(B):
+    """37 ids: fewer rows than one LM-head or correction workgroup covers
+    (one 32-row tile plus 5, three 16-row tiles), so most workgroups and waves
+    of every kernel find no rows of their own; pools of 5 and of all but one
+    id."""
+    for K in (0, 5, 36):
+        G.log(f"[gpu-test] tiny vocabulary B={B} K={K}")
+        tok, top, h = G.gpu_run(TINY_V, B, 950 + B, 0, K, max_batch=64, max_k=64)
+        ref = G.oracle_run(TINY_V, B, 950 + B, 0, K)
+        compare(tok, top, ref, TOL["bf16"])
+        assert np.all((tok >= 0) & (tok < TINY_V.vocab))
+        base = h.read_workspace(0).cpu().numpy().reshape(15, B, -1)
+        assert np.max(np.abs(base - ref_base(TINY_V, B, 950 + B, 0))) < 1e-4
+        if K:
+            ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
+            for b in range(B):
+                assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
+
+
 WIDE = synth.custom_shape(2053, 256, 512, 512, 512, "bf16", 79, name="small-bf16-wide")
 
 
