@@ -330,7 +330,10 @@ def time_cell(h, shape, wl_name, B, K, args, hid, s, ver, digest):
         t_ms /= P - 1
         nbytes = alg["correct_bytes"] + alg["step_bytes"]
         per_step = {"ms": round(t_ms, 5), "alg_gb_s": round(nbytes / (t_ms * 1e-3) / 1e9, 1),
-                    "hbm_frac": round(nbytes / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    "hbm_frac": round(nbytes / (t_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "bytes": "correction + stacked [fc1; W_hh] rows + gate inputs (the W_ih "
+                             "product is read as one row of the per-id table G, 3g floats per "
+                             "request, not as W_ih itself)"}
     lb = lower_bound_ms(alg, shape, B, K, P)
     cell = {"workload": wl_name, "model": shape.name, "batch": B, "K": K, "proposals": P,
             "ms_per_block": round(ms_step, 4), "wall_ms_per_block": round(wall_ms / args.steps, 4),
