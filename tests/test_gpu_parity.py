@@ -137,6 +137,28 @@ def test_lmhead_vocabulary_ranges(shape, B, K):
             assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
 
 
+ONE_WIDTHS = [synth.custom_shape(5003, h, 128, 128, 128, "bf16", 84 + i, name=f"bf16-hidden-{h}")
+              for i, h in enumerate((2048, 3072, 5120))]
+
+
+@pytest.mark.parametrize("shape", ONE_WIDTHS, ids=[s.name for s in ONE_WIDTHS])
+def test_one_request_lmhead_widths(shape):
+    """The one-request LM-head at hidden widths 2048, 3072 and 5120 (4, 6
+    and 10 waves per workgroup, 10 being the largest its LDS allows), the
+    ragged 5003-id vocabulary spread over 313 tiles: base logits, the first
+    proposal, the pool built from its keys and the chain."""
+    for K in (0, 100):
+        G.log(f"[gpu-test] one-request LM-head H={shape.hidden} K={K}")
+        tok, top, h = G.gpu_run(shape, 1, 990, 0, K, max_batch=8, max_k=2048)
+        ref = G.oracle_run(shape, 1, 990, 0, K)
+        compare(tok, top, ref, TOL["bf16"])
+        base = h.read_workspace(0).cpu().numpy().reshape(15, 1, -1)
+        assert np.max(np.abs(base - ref_base(shape, 1, 990, 0))) < 2e-4
+        if K:
+            ids = h.read_workspace(1).cpu().numpy().reshape(1, K)
+            assert np.array_equal(ids[0], ref["pools"][0])
+
+
 TINY_V = synth.custom_shape(37, 256, 128, 128, 128, "bf16", 83, name="bf16-vocab-37")
 
 
