@@ -316,9 +316,10 @@ void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slot
 
 // ---------------------------------------------------------------- pool build
 // Radix select of the K largest per-id scores score[v] = max_t base[t,b,v]
-// (as order-preserving uint32 keys) with 11 + 11 + 10 bit passes, then a
-// stable compaction in id order that takes every key above the threshold and
-// the lowest ids among keys equal to it.
+// (as order-preserving uint32 keys) with 11 + 11 + 10 bit passes; the ids
+// that can still be selected after two passes are collected, and the last
+// pass and the compaction in id order (every key above the threshold and the
+// lowest ids among keys equal to it) run over them alone.
 
 __device__ __forceinline__ int block_excl_scan_256(int v, int* lds, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -381,7 +382,7 @@ __global__ __launch_bounds__(256) void pool_score_hist_kernel(const float* __res
 
 // The radix state of request b after s selections sits at state[8 b + 2 s]
 // (key prefix so far) and state[8 b + 2 s + 1] (rank of the K-th key among
-// the keys with that prefix), s = 1..3.  The state s = 0, (empty prefix, K),
+// the keys with that prefix), s = 1, 2.  The state s = 0, (empty prefix, K),
 // is never stored: the first selection (inside pool_hist_kernel<1>) starts
 // from the kernel's K argument.
 
@@ -390,20 +391,29 @@ __global__ __launch_bounds__(256) void pool_score_hist_kernel(const float* __res
 // prefix and the rank left inside that bin.  Exactly one bin qualifies, so
 // one thread writes res; every thread returns the result.
 template <int PASS>
-__device__ __forceinline__ uint2 select_bin(const uint32_t* __restrict__ hh, uint32_t prefix,
-                                            uint32_t need, int* lds, uint32_t* res) {
-  constexpr int NBINS = PASS < 2 ? 2048 : 1024;
-  constexpr int PER = NBINS / 256;
-  constexpr int BITS = PASS < 2 ? 11 : 10;
-  // thread 0 holds the highest PER bins, thread 255 the lowest
-  const int lo_bin = NBINS - (threadIdx.x + 1) * PER;
+struct SelectBins {
+  static constexpr int NBINS = PASS < 2 ? 2048 : 1024;
+  static constexpr int PER = NBINS / 256;
   uint32_t c[PER];
+  // thread 0 holds the highest PER bins, thread 255 the lowest
+  __device__ __forceinline__ static int lo_bin() { return NBINS - ((int)threadIdx.x + 1) * PER; }
+  __device__ __forceinline__ void load(const uint32_t* __restrict__ hh) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) c[j] = hh[lo_bin() + j];
+  }
+};
+
+// the same with this thread's bins already loaded
+template <int PASS>
+__device__ __forceinline__ uint2 select_bin(const SelectBins<PASS>& bins, uint32_t prefix,
+                                            uint32_t need, int* lds, uint32_t* res) {
+  constexpr int PER = SelectBins<PASS>::PER;
+  constexpr int BITS = PASS < 2 ? 11 : 10;
+  const int lo_bin = SelectBins<PASS>::lo_bin();
+  const uint32_t* const c = bins.c;
   int tot = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    c[j] = hh[lo_bin + j];
-    tot += (int)c[j];
-  }
+  for (int j = 0; j < PER; ++j) tot += (int)c[j];
   uint32_t above = (uint32_t)block_excl_scan_256(tot, lds, nullptr);
 #pragma unroll
   for (int j = PER - 1; j >= 0; --j) {
@@ -417,15 +427,24 @@ __device__ __forceinline__ uint2 select_bin(const uint32_t* __restrict__ hh, uin
   return make_uint2(res[0], res[1]);
 }
 
-// Histogram pass PASS of the keys of request blockIdx.y in one chunk of ids.
-// Passes 1 and 2 first repeat the previous pass's selection in every
-// workgroup (from its finished histogram) instead of in a launch of its own;
-// the chunk-0 workgroup records the new state for the next kernel.
+template <int PASS>
+__device__ __forceinline__ uint2 select_bin(const uint32_t* __restrict__ hh, uint32_t prefix,
+                                            uint32_t need, int* lds, uint32_t* res) {
+  SelectBins<PASS> bins;
+  bins.load(hh);
+  return select_bin<PASS>(bins, prefix, need, lds, res);
+}
+
+// Histogram pass PASS (0 or 1) of the keys of request blockIdx.y in one
+// chunk of ids.  Pass 1 first repeats the first selection in every workgroup
+// (from its finished histogram) instead of in a launch of its own; the
+// chunk-0 workgroup records the new state for the next kernel.
 template <int PASS, int F>
 __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restrict__ keys, int V,
                                                         uint32_t* __restrict__ state,
                                                         uint32_t* __restrict__ hist, int K) {
-  constexpr int NBINS = PASS < 2 ? 2048 : 1024;
+  static_assert(PASS == 0 || PASS == 1, "the last pass runs in pool_collect_kernel");
+  constexpr int NBINS = 2048;
   __shared__ uint32_t h[NBINS];
   __shared__ int lds[4];
   __shared__ uint32_t res[2];
@@ -439,16 +458,13 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
   for (int j = 0; j < NL; ++j) kv[j] = keys[(size_t)b * V + min(v0 + j * 256 + (int)threadIdx.x, V - 1)];
   for (int i = threadIdx.x; i < NBINS; i += 256) h[i] = 0;
   uint32_t prefix = 0;
-  if (PASS > 0) {
-    uint32_t* sb = state + 8 * b + 2 * (PASS - 1);
+  if (PASS == 1) {
     // the state before the first selection is (empty prefix, rank K)
-    const uint32_t p0 = PASS == 1 ? 0u : sb[0], r0 = PASS == 1 ? (uint32_t)K : sb[1];
-    const uint2 ns = select_bin<PASS - 1>(hist + ((size_t)b * 3 + PASS - 1) * 2048, p0, r0,
-                                          lds, res);
+    const uint2 ns = select_bin<0>(hist + (size_t)b * 3 * 2048, 0u, (uint32_t)K, lds, res);
     prefix = ns.x;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-      sb[2] = ns.x;
-      sb[3] = ns.y;
+      state[8 * b + 2] = ns.x;
+      state[8 * b + 3] = ns.y;
     }
   }
   __syncthreads();
@@ -458,10 +474,8 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
     const uint32_t key = kv[j];
     if (PASS == 0) {
       if (ok) atomicAdd(&h[key >> 21], 1u);
-    } else if (PASS == 1) {
-      if (ok && (key >> 21) == prefix) atomicAdd(&h[(key >> 10) & 2047u], 1u);
     } else {
-      if (ok && (key >> 10) == prefix) atomicAdd(&h[key & 1023u], 1u);
+      if (ok && (key >> 21) == prefix) atomicAdd(&h[(key >> 10) & 2047u], 1u);
     }
   }
   __syncthreads();
@@ -470,106 +484,165 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
     if (h[i]) atomicAdd(&hh[i], h[i]);
 }
 
-// Keys above and equal to the threshold per chunk, after the last selection
-// (repeated in every workgroup, recorded by chunk 0's as state 3).
+// Selection after the second radix pass in two launches instead of three
+// passes over the keys.  Every id whose key's top 22 bits are at least the
+// selected prefix is a candidate: K plus the few other ids of that prefix
+// (the first pass's 11-bit bins of float keys are a quarter octave wide and
+// can hold much of the vocabulary; 22-bit ones hold a handful).
+// pool_collect_kernel compacts the candidates of every kPoolChunk ids, as
+// (key, id) pairs in id order, into those ids' own stretch of cand (no counter shared between
+// workgroups: same-line atomics from many workgroups serialise) and adds the
+// candidates of the selected prefix to the last radix histogram;
+// pool_select_kernel, one workgroup per request, takes the threshold from
+// that histogram and writes the pool in id order: every key above the
+// threshold and the lowest ids of those equal to it.  The selected set is the
+// one of the count and compaction kernels, id for id.
 template <int F>
-__global__ __launch_bounds__(256) void pool_count_kernel(const uint32_t* __restrict__ keys, int V,
-                                                         uint32_t* __restrict__ state,
-                                                         const uint32_t* __restrict__ hist,
-                                                         uint32_t* __restrict__ counts, int nch) {
+__global__ __launch_bounds__(256) void pool_collect_kernel(const uint32_t* __restrict__ keys, int V,
+                                                           uint32_t* __restrict__ state,
+                                                           uint32_t* __restrict__ hist,
+                                                           uint2* __restrict__ cand,
+                                                           uint32_t* __restrict__ cand_n, int nch) {
+  constexpr int NL = F * kPoolChunk / 256;
   __shared__ int lds[4];
   __shared__ uint32_t res[2];
-  const int b = blockIdx.y;
-  constexpr int NL = F * kPoolChunk / 256;
+  __shared__ int wcnt[NL][4];  // candidates per (load, wave)
+  const int b = blockIdx.y, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int v0 = blockIdx.x * F * kPoolChunk;
   uint32_t kv[NL];  // issued before the selection, which they do not depend on
 #pragma unroll
   for (int j = 0; j < NL; ++j) kv[j] = keys[(size_t)b * V + min(v0 + j * 256 + (int)threadIdx.x, V - 1)];
-  uint32_t* sb = state + 8 * b + 4;
-  const uint2 ns = select_bin<2>(hist + ((size_t)b * 3 + 2) * 2048, sb[0], sb[1], lds, res);
+  uint32_t* sb = state + 8 * b + 2;
+  const uint2 ns = select_bin<1>(hist + ((size_t)b * 3 + 1) * 2048, sb[0], sb[1], lds, res);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     sb[2] = ns.x;
     sb[3] = ns.y;
   }
-  const uint32_t T = ns.x;
-  int gt = 0, eq = 0;
+  uint64_t mk[NL];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
     const bool ok = v0 + j * 256 + (int)threadIdx.x < V;
-    gt += ok && kv[j] > T;
-    eq += ok && kv[j] == T;
+    mk[j] = __ballot(ok && (kv[j] >> 10) >= ns.x);
+    if (lane == 0) wcnt[j][w] = __popcll(mk[j]);
+    if (ok && (kv[j] >> 10) == ns.x)  // the few ids of the prefix itself
+      atomicAdd(&hist[((size_t)b * 3 + 2) * 2048 + (kv[j] & 1023u)], 1u);
   }
-  gt = block_sum_256(gt, lds);
-  eq = block_sum_256(eq, lds);
-  if (threadIdx.x == 0) {
-    counts[((size_t)b * nch + blockIdx.x) * 2] = (uint32_t)gt;
-    counts[((size_t)b * nch + blockIdx.x) * 2 + 1] = (uint32_t)eq;
+  __syncthreads();
+  // each kPoolChunk ids (four loads) keep their candidates in their own
+  // stretch, in id order, which is (load j, wave, lane)
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int acc = 0;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    constexpr int per = kPoolChunk / 256;
+    if (j % per == 0) acc = 0;
+    int before = acc;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      before += x < w ? wcnt[j][x] : 0;
+      acc += wcnt[j][x];
+    }
+    const int sub = v0 + (j / per) * kPoolChunk;
+    if ((mk[j] >> lane) & 1ull)
+      cand[(size_t)b * V + sub + before + __popcll(mk[j] & lt)] =
+          make_uint2(kv[j], (uint32_t)(v0 + j * 256 + (int)threadIdx.x));
+    if (j % per == per - 1 && threadIdx.x == 0 && sub < V)
+      cand_n[(size_t)b * nch + sub / kPoolChunk] = (uint32_t)acc;
   }
 }
 
-// umask (or nullptr): the selected ids also set their request's bit in the
-// member mask of its group of ug requests (union stream).  A workgroup walks its chunk in
-// sub-chunks of kPoolChunk ids, four consecutive ids per thread, so the scan
-// order is the id order.
-template <int F>
-__global__ __launch_bounds__(256) void pool_compact_kernel(
-    const uint32_t* __restrict__ keys, int V, int K, const uint32_t* __restrict__ state,
-    const uint32_t* __restrict__ counts, int nch, int32_t* __restrict__ pool_ids,
-    uint32_t* __restrict__ umask, int ug) {
-  __shared__ int lds[4];
-  const int b = blockIdx.y, chunk = blockIdx.x;
-  const uint32_t T = state[8 * b + 6];
-  const int need = (int)state[8 * b + 7];
-  int gt_b = 0, eq_b = 0;  // keys above / equal to the threshold before this sub-chunk
-  for (int c = threadIdx.x; c < chunk; c += 256) {
-    gt_b += (int)counts[((size_t)b * nch + c) * 2];
-    eq_b += (int)counts[((size_t)b * nch + c) * 2 + 1];
+// block-wide exclusive scans of two values at once (256 threads)
+__device__ __forceinline__ int2 block_excl_scan2_256(int a, int c, int* lds8) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = a, y = c;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int px = __shfl_up(x, d, 64), py = __shfl_up(y, d, 64);
+    if (lane >= d) {
+      x += px;
+      y += py;
+    }
   }
-  gt_b = block_sum_256(gt_b, lds);
-  eq_b = block_sum_256(eq_b, lds);
-#pragma unroll 1
-  for (int f = 0; f < F; ++f) {
-    const int v0 = (chunk * F + f) * kPoolChunk + threadIdx.x * 4;
-    bool isgt[4], iseq[4];
-    int my_eq = 0, my_gt = 0;
-    uint32_t kv[4];
+  if (lane == 63) {
+    lds8[w] = x;
+    lds8[4 + w] = y;
+  }
+  __syncthreads();
+  int ox = 0, oy = 0;
+  for (int i = 0; i < w; ++i) {
+    ox += lds8[i];
+    oy += lds8[4 + i];
+  }
+  __syncthreads();
+  return make_int2(ox + x - a, oy + y - c);
+}
+
+constexpr int kSelectPre = 24;  // candidates per thread loaded before the selection
+
+// 256 threads (select_bin's scans) per request.  Thread t owns a run of
+// consecutive chunks of kPoolChunk ids, so its candidates, in order, are a
+// run of the ids in order.  Every load of the common case (the first
+// chunk's count and up to kSelectPre candidates, read at clamped places
+// inside that chunk's stretch before their number is known) is issued
+// before the selection; more candidates (many equal scores) and further
+// chunks (vocabularies above 256 chunks) are read in the walks.  With gt and
+// eq the keys above and equal to the threshold before a thread's run, its
+// first selected id goes to place gt + min(eq, need).
+__global__ __launch_bounds__(256) void pool_select_kernel(
+    int K, int nch, const uint32_t* __restrict__ state, const uint32_t* __restrict__ hist,
+    const uint2* __restrict__ cand, const uint32_t* __restrict__ cand_n, int V,
+    int32_t* __restrict__ pool_ids, uint32_t* __restrict__ umask, int ug) {
+  __shared__ int lds[8];
+  __shared__ uint32_t res[2];
+  const int b = blockIdx.x;
+  const uint2* const cb = cand + (size_t)b * V;
+  const uint32_t* const nb = cand_n + (size_t)b * nch;
+  const int cpt = (nch + 255) / 256;
+  const int c0 = min((int)threadIdx.x * cpt, nch), c1 = min(c0 + cpt, nch);
+  const bool any = c0 < c1;
+  // the histogram first: the selection waits for it, not for the candidates
+  SelectBins<2> bins;
+  bins.load(hist + ((size_t)b * 3 + 2) * 2048);
+  const uint2* const src0 = cb + (size_t)min(c0, nch - 1) * kPoolChunk;
+  const int last = min(kPoolChunk, V - min(c0, nch - 1) * kPoolChunk) - 1;  // in the stretch
+  uint2 e[kSelectPre];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) kv[j] = keys[(size_t)b * V + min(v0 + j, V - 1)];
+  for (int j = 0; j < kSelectPre; ++j) e[j] = src0[min(j, last)];
+  const int n0 = any ? (int)nb[c0] : 0;
+  const uint2 s2 = select_bin<2>(bins, state[8 * b + 4], state[8 * b + 5], lds, res);
+  const uint32_t T = s2.x;         // the K-th largest key
+  const int need = (int)s2.y;      // keys equal to T to take, lowest ids first
+  // f on this thread's candidates in id order
+  auto walk = [&](auto&& f) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = v0 + j < V;
-      isgt[j] = ok && kv[j] > T;
-      iseq[j] = ok && kv[j] == T;
-      my_eq += iseq[j];
-      my_gt += isgt[j];
+    for (int j = 0; j < kSelectPre; ++j)
+      if (j < n0) f(e[j]);
+    for (int j = kSelectPre; j < n0; ++j) f(src0[j]);
+    for (int c = c0 + 1; c < c1; ++c) {
+      const int nc = (int)nb[c];
+      const uint2* const src = cb + (size_t)c * kPoolChunk;
+      for (int j = 0; j < nc; ++j) f(src[j]);
     }
-    int eq_sub = 0;
-    const int eq_before = eq_b + block_excl_scan_256(my_eq, lds, &eq_sub);
-    bool sel[4];
-    int my_sel = 0, e = eq_before;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sel[j] = isgt[j] || (iseq[j] && e < need);
-      e += iseq[j];
-      my_sel += sel[j];
-    }
-    int pos = gt_b + min(eq_b, need) + block_excl_scan_256(my_sel, lds, nullptr);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (!sel[j]) continue;
-      const int v = v0 + j;
+  };
+  int my_gt = 0, my_eq = 0;
+  walk([&](uint2 x) {
+    my_gt += x.x > T;
+    my_eq += x.x == T;
+  });
+  const int2 before = block_excl_scan2_256(my_gt, my_eq, lds);
+  int pos = before.x + min(before.y, need), eq = before.y;
+  int32_t* const out = pool_ids + (size_t)b * K;
+  walk([&](uint2 x) {
+    const bool sel = x.x > T || (x.x == T && eq < need);
+    eq += x.x == T;
+    if (sel) {
       if (pos < K) {
-        pool_ids[(size_t)b * K + pos] = v;
-        if (umask)
-          atomicOr(&umask[(size_t)(b / ug) * V + v], 1u << (b % ug));
+        out[pos] = (int32_t)x.y;
+        if (umask) atomicOr(&umask[(size_t)(b / ug) * V + x.y], 1u << (b % ug));
       }
       ++pos;
     }
-    if (F > 1) {
-      gt_b += block_sum_256(my_gt, lds);
-      eq_b += eq_sub;
-    }
-  }
+  });
 }
 
 // ------------------------------------------------------ pool row unions
@@ -707,11 +780,11 @@ static void pool_select_passes(const Shape& s, const Workspace& ws, int B, int K
   else
     DLAUNCH((pool_score_hist_kernel<F>), grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
   DLAUNCH((pool_hist_kernel<1, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, K);
-  DLAUNCH((pool_hist_kernel<2, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, K);
-  DLAUNCH((pool_count_kernel<F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, ws.counts,
-          nch);
-  DLAUNCH((pool_compact_kernel<F>), grid, blk, 0, st, ws.keys, s.V, K, ws.state, ws.counts, nch,
-          ws.pool_ids, uni ? ws.umask : nullptr, ws.ugroup);
+  const int nsub = (s.V + kPoolChunk - 1) / kPoolChunk;
+  DLAUNCH((pool_collect_kernel<F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, ws.cand,
+          ws.cand_n, nsub);
+  DLAUNCH(pool_select_kernel, dim3(B), blk, 0, st, K, nsub, ws.state, ws.hist, ws.cand,
+          ws.cand_n, s.V, ws.pool_ids, uni ? ws.umask : nullptr, ws.ugroup);
 }
 
 void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,

@@ -42,9 +42,10 @@ struct Workspace {
   float* base;         // [15, Bmax, V] step-major base logits
   uint32_t* keys;      // [Bmax, V] orderable pool scores
   uint32_t* hist;      // [Bmax, 3, 2048] radix histograms
-  uint32_t* state;     // [Bmax, 4, 2] radix state (prefix, remaining count) after 0..3 selections
-  uint32_t* counts;    // [Bmax, nchunks, 2] (greater, equal) per chunk
+  uint32_t* state;     // [Bmax, 4, 2] radix state (prefix, remaining count) after 0..2 selections
   int32_t* pool_ids;   // [Bmax, Kmax]
+  uint2* cand;         // [Bmax, V] pool candidates (key, id), compacted per id chunk
+  uint32_t* cand_n;    // [Bmax, nchunks] candidates per chunk of kPoolChunk ids
   float* pool_base;    // [14, Bmax, Kmax]
   float* h[2];         // [Bmax, g] ping-pong GRU state
   float* c[2];         // [Bmax, 3g] W_hh h of the matching state

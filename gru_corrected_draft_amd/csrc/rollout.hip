@@ -58,7 +58,7 @@ struct GraphEntry {
 
 // Scratch of the allocation-free runs (domino_rollout_run_static): the
 // per-run buffers of a rollout (argmax words, bad-request flags, radix
-// histograms / state / chunk counts, GRU state and W_hh h ping-pong, u and its
+// histograms / state, GRU state and W_hh h ping-pong, u and its
 // bf16 planes, the fragment-ordered state, split partials) carved from one
 // file-scope device array instead of the handle's workspace.  Host code never
 // passes the array's name to a kernel (on the host it is only a stand-in):
@@ -257,8 +257,11 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   ws.keys = (uint32_t*)alloc(Bm * V * 4);
   ws.hist = (uint32_t*)alloc(Bm * 3 * 2048 * 4);
   ws.state = (uint32_t*)alloc(Bm * 8 * 4);
-  ws.counts = (uint32_t*)alloc(Bm * nch * 2 * 4);
   ws.pool_ids = (int32_t*)alloc(Bm * Km * 4);
+  if (cfg->max_k > 0) {
+    ws.cand = (uint2*)alloc(Bm * V * 8);
+    ws.cand_n = (uint32_t*)alloc(Bm * nch * 4);
+  }
   ws.pool_base = (float*)alloc(DOMINO_S * Bm * Km * 4);
   ws.h[0] = (float*)alloc(Bm * g * 4);
   ws.h[1] = (float*)alloc(Bm * g * 4);
@@ -311,7 +314,12 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
       return DOMINO_ERR_OUT_OF_MEMORY;
     }
   }
-  for (void* p : {(void*)ws.base, (void*)ws.keys, (void*)ws.hist, (void*)ws.state, (void*)ws.counts,
+  if (cfg->max_k > 0 && (!ws.cand || !ws.cand_n)) {
+    set_global_err("create: workspace allocation failed");
+    domino_rollout_destroy(h);
+    return DOMINO_ERR_OUT_OF_MEMORY;
+  }
+  for (void* p : {(void*)ws.base, (void*)ws.keys, (void*)ws.hist, (void*)ws.state,
                   (void*)ws.pool_ids, (void*)ws.pool_base, (void*)ws.h[0], (void*)ws.h[1],
                   (void*)ws.c[0], (void*)ws.c[1], (void*)ws.G,
                   (void*)ws.u, (void*)ws.u_hi, (void*)ws.u_lo, (void*)ws.slots, (void*)ws.bad,
@@ -621,8 +629,7 @@ extern "C" domino_status_t domino_rollout_run_forced(domino_rollout_t* h, const 
 // nullptr only the size is computed.
 static size_t carve_static(const domino_rollout_t* h, int B, Workspace& ws, unsigned char* base) {
   const Shape& sh = h->shape;
-  const size_t V = sh.V, g = sh.g, r = sh.r, Bz = B;
-  const size_t nch = (V + kPoolChunk - 1) / kPoolChunk;
+  const size_t g = sh.g, r = sh.r, Bz = B;
   size_t off = 0;
   auto take = [&](size_t bytes) -> void* {
     void* p = base ? (void*)(base + off) : nullptr;
@@ -633,7 +640,6 @@ static size_t carve_static(const domino_rollout_t* h, int B, Workspace& ws, unsi
   ws.bad = (int32_t*)take(Bz * 4);
   ws.hist = (uint32_t*)take(Bz * 3 * 2048 * 4);
   ws.state = (uint32_t*)take(Bz * 8 * 4);
-  ws.counts = (uint32_t*)take(Bz * nch * 2 * 4);
   ws.h[0] = (float*)take(Bz * g * 4);
   ws.h[1] = (float*)take(Bz * g * 4);
   ws.c[0] = (float*)take(Bz * 3 * g * 4);

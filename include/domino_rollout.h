@@ -250,7 +250,7 @@ domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int32_t which, 
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
  * the same rollout as domino_rollout_run (same kernels, bit-identical
  * results), whose per-run scratch -- argmax words, bad-request flags, radix
- * histograms / state / chunk counts, GRU state and W_hh h, u and its bf16
+ * histograms / state, GRU state and W_hh h, u and its bf16
  * planes, the fragment-ordered state and split partials -- lives in one
  * static device array of DOMINO_STATIC_SCRATCH_BYTES that the library holds
  * on every device it runs on until the process ends, instead of the

@@ -182,6 +182,39 @@ def test_tiny_vocabulary(B):
                 assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
 
 
+# 300007 ids: 293 chunks of 1024, more than the pool selection workgroup has
+# threads, so some of its threads walk the candidates of two chunks
+LARGE_V = synth.custom_shape(300007, 256, 128, 128, 128, "bf16", 84, name="bf16-vocab-300007")
+
+
+@pytest.mark.parametrize("B", [1, 8, 40])
+def test_large_vocabulary_pools(B):
+    """Pools of 2048 and 9000 ids over 300007.  The selection is exact on
+    the GPU's own base logits: the pool is, id for id and in id order, the K
+    best max-over-steps scores of those logits, lowest id on ties.  Against
+    the oracle's pools, membership may only differ among ids whose scores lie
+    within the LM-head's rounding of the cutoff (at 9000 of 300007 ids the
+    scores there are dense)."""
+    V = LARGE_V.vocab
+    for K in (2048, 9000):
+        G.log(f"[gpu-test] large vocabulary B={B} K={K}")
+        tok, top, h = G.gpu_run(LARGE_V, B, 963 + B, 0, K, max_batch=64, max_k=9000)
+        ref = G.oracle_run(LARGE_V, B, 963 + B, 0, K)
+        c, _ = compare(tok, top, ref, TOL["bf16"])
+        assert c > 0
+        ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
+        base = h.read_workspace(0).cpu().numpy().reshape(15, B, V)
+        obase = ref_base(LARGE_V, B, 963 + B, 0)
+        for b in range(B):
+            score = base[:, b, :].max(axis=0) + np.float32(0.0)
+            order = np.lexsort((np.arange(V), -score))
+            assert np.array_equal(ids[b], np.sort(order[:K])), f"pool of request {b} (own logits)"
+            diff = np.setxor1d(ids[b], ref["pools"][b])
+            oscore = obase[:, b, :].max(axis=0)
+            cutoff = np.sort(oscore)[-K]
+            assert np.all(np.abs(oscore[diff] - cutoff) < 1e-4), f"pool of request {b} (oracle)"
+
+
 WIDE = synth.custom_shape(2053, 256, 512, 512, 512, "bf16", 79, name="small-bf16-wide")
 
 

@@ -199,3 +199,43 @@ def test_exact_ties_lowest_id(shape, B, strategy):
             G.log(f"[gpu-test] ties K={K}: {ties} tie steps, {checked} other steps checked")
     finally:
         h.close()
+
+
+FLAT = synth.custom_shape(5003, 256, 128, 128, 128, "bf16", 94, name="flat-bf16")
+
+
+@pytest.mark.parametrize("B", [3, 40])
+def test_all_scores_equal(B):
+    """Every lm_head row the same: all base logits of a step are equal, so
+    every id's pool score ties.  Every id is then a candidate of the last
+    radix pass (a whole chunk of them, far more than the selection holds in
+    registers), the pool is ids 0..K-1, and the first proposal is id 0."""
+    import oracle
+    import torch
+    w = synth.make_weights(FLAT)
+    f = {n: np.array(w.f32(n), np.float32, copy=True) for n in w.raw}
+    f["lm_head"] = np.broadcast_to(_quant(f["lm_head"][:1], 2.0 ** -6, 0.25), f["lm_head"].shape).copy()
+    raw = {n: _store(FLAT, a) for n, a in f.items()}
+    wq = synth.Weights(FLAT, raw)
+    f32 = {n: wq.f32(n) for n in raw}
+    inp = synth.make_inputs(FLAT, B, 4500 + B, 0)
+    X = _quant(inp.hidden_f32(), 2.0 ** -3, 2.0)
+    inp = synth.Inputs(_store(FLAT, X), inp.step_s, inp.verified)
+    h = R.DominoRollout(R.device_weights(wq), max_batch=64, max_k=5002)
+    try:
+        hid, s, ver = R.device_inputs(inp)
+        for K in (1, 700, 5002):
+            G.log(f"[gpu-test] all scores equal B={B} K={K}")
+            tok, top = h.run(hid, s, ver, K)
+            torch.cuda.synchronize()
+            tok, top = tok.cpu().numpy(), top.cpu().numpy()
+            ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
+            assert np.array_equal(ids, np.broadcast_to(np.arange(K, dtype=ids.dtype), (B, K)))
+            ref = oracle.rollout(f32, X, inp.step_s, inp.verified, K)
+            assert np.array_equal(ref["pools"], ids)
+            assert np.all(tok[:, 0] == 0)
+            checked, ties = compare_with_ties(tok, top, ref, TOL[FLAT.dtype], {0})
+            G.log(f"[gpu-test] all scores equal K={K}: {ties} tie steps, {checked} other steps checked")
+            assert ties >= B
+    finally:
+        h.close()
