@@ -818,6 +818,12 @@ def _check_full_size_intermediates(h, wl, shape, trial, K, tok, ref):
     assert np.all(np.abs(got - exact) <= bound + 1e-6)
     if 0 < K < V:
         ids = h.read_workspace(1).cpu().numpy().reshape(B, K)
+        # the selection is exact on the GPU's own base logits: the K best
+        # max-over-steps scores, lowest id on ties, in id order
+        own = base.max(axis=0) + np.float32(0.0)
+        for b in range(B):
+            order = np.lexsort((np.arange(V), -own[b]))
+            assert np.array_equal(ids[b], np.sort(order[:K])), f"pool of request {b} (own logits)"
         obase = None
         for b in range(B):
             want = ref["pools"][b]
