@@ -129,4 +129,29 @@ __device__ __forceinline__ void publish_max(uint64_t* slot, uint64_t key) {
   if (key > cur) atomicMax((unsigned long long*)slot, (unsigned long long)key);
 }
 
+// An argmax word (one per position and request) is kept as kSlotCopies
+// copies, each alone on a 128-byte line: a workgroup publishes to the copy
+// of its XCD (workgroups are dealt to the eight XCDs in turn), and readers
+// take the largest copy.  Atomics that many workgroups aim at one line
+// serialise (about 10 ns apiece); at 8 requests the 1024 waves of a pool
+// correction published to the one line holding all eight words, which cost
+// more than the correction's loads.  Word w of an array starts at word
+// w * kSlotSpan; an unwritten copy is zero.
+constexpr int kSlotCopies = 8;
+constexpr int kSlotLine = 16;                       // u64 words per 128-byte line
+constexpr int kSlotSpan = kSlotCopies * kSlotLine;  // u64 words per argmax word
+__device__ __forceinline__ void publish_slot(uint64_t* slots, int w, uint64_t key) {
+  const int c = (int)((blockIdx.x + blockIdx.y * gridDim.x) & (kSlotCopies - 1));
+  publish_max(slots + (size_t)w * kSlotSpan + c * kSlotLine, key);
+}
+__device__ __forceinline__ uint64_t read_slot(const uint64_t* slots, int w) {
+  uint64_t v[kSlotCopies];
+#pragma unroll
+  for (int c = 0; c < kSlotCopies; ++c) v[c] = slots[(size_t)w * kSlotSpan + c * kSlotLine];
+  uint64_t m = v[0];
+#pragma unroll
+  for (int c = 1; c < kSlotCopies; ++c) m = m > v[c] ? m : v[c];
+  return m;
+}
+
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }

@@ -51,7 +51,7 @@ __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast
 // token of request b from the argmax word or the int32 source; a token
 // outside [0, V) flags the request (when `flag`) and reads row 0 instead
 __device__ __forceinline__ int step_token(const StepArgs& a, int b, bool flag) {
-  int tok = a.tok_key ? key_id(a.tok_key[b]) : a.tok_i32[(size_t)b * a.tok_stride];
+  int tok = a.tok_key ? key_id(read_slot(a.tok_key, b)) : a.tok_i32[(size_t)b * a.tok_stride];
   if (tok < 0 || tok >= a.V) {
     if (flag) a.bad[b] = 1;
     tok = 0;

@@ -306,7 +306,7 @@ __global__ __launch_bounds__(256) void row0_argmax_kernel(const float* __restric
   __shared__ uint64_t wb[4];
   if ((threadIdx.x & 63) == 0) wb[threadIdx.x >> 6] = best;
   __syncthreads();
-  if (threadIdx.x == 0) publish_max(&slots[b], umax64(umax64(wb[0], wb[1]), umax64(wb[2], wb[3])));
+  if (threadIdx.x == 0) publish_slot(slots, b, umax64(umax64(wb[0], wb[1]), umax64(wb[2], wb[3])));
 }
 
 void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st) {
@@ -910,7 +910,7 @@ __global__ __launch_bounds__(256) void correct_full_kernel(CorrArgs<BF> a) {
     const int b = cb * 16 + n;
     if (b < a.B) {
       const uint64_t m = umax64(umax64(wb[0][cb][n], wb[1][cb][n]), umax64(wb[2][cb][n], wb[3][cb][n]));
-      publish_max(&a.slot_k[b], m);
+      publish_slot(a.slot_k, b, m);
     }
   }
 }
@@ -939,7 +939,7 @@ static void correct_full_dispatch(const CorrArgs<BF>& a, hipStream_t st) {
 void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
                          hipStream_t st) {
   const float* base_k = ws.base + (size_t)k * B * s.V;
-  uint64_t* slot_k = ws.slots + (size_t)k * B;
+  uint64_t* slot_k = ws.slots + (size_t)k * B * kSlotSpan;
   if (s.bf16 && rowstream_supported(s.r, B)) {
     StreamArgs a{(const uint16_t*)w.fc2, s.V, s.r, ws.u_hi, ws.u_lo, B, 0, 0, nullptr,
                  (const uint16_t*)w.fc2_b, base_k, slot_k, kReverseOddSteps ? (k & 1) : 0};
@@ -1027,7 +1027,7 @@ __global__ __launch_bounds__(256) void correct_pool_kernel(PoolArgs<BF> a) {
       }
     }
   best = wave_max_u64(best);
-  if (lane == 0) publish_max(&a.slot_k[b], best);
+  if (lane == 0) publish_slot(a.slot_k, b, best);
 }
 
 // bf16 pool correction with the projector width split over the four waves
@@ -1077,7 +1077,7 @@ __global__ __launch_bounds__(256) void correct_pool_split_kernel(PoolArgs<true> 
     }
   }
   best = wave_max_u64(best);
-  if (lane == 0) publish_max(&a.slot_k[b], best);
+  if (lane == 0) publish_slot(a.slot_k, b, best);
 }
 
 // bf16 pool correction with whole-line loads, for small batches: one wave
@@ -1159,7 +1159,7 @@ __global__ __launch_bounds__(256) void correct_pool_lines_kernel(PoolArgs<true> 
   const float y = rbase + (dot + rbias);
   uint64_t best = (ridx < K) ? pack_key(y, (uint32_t)rid) : 0ull;
   best = wave_max_u64(best);
-  if (lane == 0) publish_max(&a.slot_k[b], best);
+  if (lane == 0) publish_slot(a.slot_k, b, best);
 }
 
 constexpr int kPoolRT = 2;
@@ -1198,7 +1198,7 @@ void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace
   const int units = upr * B;
   const dim3 grid((units + 3) / 4);
   const float* pb = ws.pool_base + (size_t)(k - 1) * B * K;
-  uint64_t* slot_k = ws.slots + (size_t)k * B;
+  uint64_t* slot_k = ws.slots + (size_t)k * B * kSlotSpan;
   if (pool_union(s, ws, B, K)) {
     StreamArgs a{(const uint16_t*)w.fc2, 0, s.r, ws.u_hi, ws.u_lo, B, 0, 0, nullptr,
                  nullptr, nullptr, slot_k, kReverseOddSteps ? (k & 1) : 0};
@@ -1262,13 +1262,14 @@ __global__ __launch_bounds__(64) void writeout_kernel(uint64_t* __restrict__ slo
   const int b = blockIdx.x, k = threadIdx.x;
   const bool flagged = bad[b] != 0;
   if (k < P) {
-    const uint64_t key = slots[(size_t)k * B + b];
+    const uint64_t key = read_slot(slots, k * B + b);
     const bool invalid = flagged || key == 0;
     out_tokens[b * P + k] = invalid ? -1 : key_id(key);
     if (out_top1) out_top1[b * P + k] = invalid ? __builtin_nanf("") : key_value(key);
   }
   __syncthreads();  // every lane has read bad[b]
-  if (k < DOMINO_T) slots[(size_t)k * B + b] = 0;
+  for (int i = k; i < DOMINO_T * kSlotCopies; i += 64)
+    slots[(size_t)((i / kSlotCopies) * B + b) * kSlotSpan + (i % kSlotCopies) * kSlotLine] = 0;
   if (k == 0) bad[b] = 0;
   if (hist)
     for (int i = k; i < 3 * 2048; i += 64) hist[(size_t)b * 3 * 2048 + i] = 0;

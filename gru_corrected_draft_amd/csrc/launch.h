@@ -58,7 +58,7 @@ struct Workspace {
   float* u;            // [Bmax, r]
   uint16_t* u_hi;      // [Bmax, r]
   uint16_t* u_lo;      // [Bmax, r]
-  uint64_t* slots;     // [15, Bmax] argmax words
+  uint64_t* slots;     // [15, Bmax] argmax words, kSlotSpan u64 each (common.h)
   int32_t* bad;        // [Bmax]
   float* partial;      // split partial tiles of the step product
   float* s_tmp;        // k-split partials of the step-offset product

@@ -101,7 +101,7 @@ __device__ __forceinline__ void fused_epilogue(const FusedArgs& a, const v4f (&a
   if (q == 0) wb[wave][row] = best0;
   __syncthreads();
   if (tid < 16 && b0 + tid < B)
-    publish_max(&a.slots[b0 + tid],
+    publish_slot(a.slots, b0 + tid,
                 umax64(umax64(wb[0][tid], wb[1][tid]), umax64(wb[2][tid], wb[3][tid])));
 }
 
@@ -523,7 +523,7 @@ __global__ __launch_bounds__(256) void lmhead_m32_kernel(FusedArgs a) {
   __syncthreads();
   if (threadIdx.x < kMR && b0 + (int)threadIdx.x < B) {
     const int r = threadIdx.x;
-    publish_max(&a.slots[b0 + r], umax64(umax64(wb[0][r], wb[1][r]), umax64(wb[2][r], wb[3][r])));
+    publish_slot(a.slots, b0 + r, umax64(umax64(wb[0][r], wb[1][r]), umax64(wb[2][r], wb[3][r])));
   }
 }
 
@@ -747,7 +747,7 @@ __global__ __launch_bounds__(512) void lmhead_range_kernel(FusedArgs a) {
   // wave of every CU at nearly the same moment serialise there
   if (threadIdx.x < kMR && (int)threadIdx.x < B) {
     const int r = threadIdx.x;
-    publish_max(&a.slots[r], umax64(umax64(wb[0][r], wb[1][r]), umax64(wb[2][r], wb[3][r])));
+    publish_slot(a.slots, r, umax64(umax64(wb[0][r], wb[1][r]), umax64(wb[2][r], wb[3][r])));
   }
 }
 
@@ -970,7 +970,7 @@ __global__ __launch_bounds__(64 * 16 / TA) void lmhead_xf_kernel(FusedArgs a) {
 #pragma unroll
   for (int r = 0; r < 2 * TA; ++r) {
     const uint64_t m = wave_max_u64(best[r]);
-    if (lane == 0 && bw + r < B) publish_max(&a.slots[bw + r], m);
+    if (lane == 0 && bw + r < B) publish_slot(a.slots, bw + r, m);
   }
 }
 

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(WV * 64) void lmhead_one_kernel(const bf16_t* W,
     uint64_t b = wbest[0];
 #pragma unroll
     for (int w = 1; w < WV; ++w) b = umax64(b, wbest[w]);
-    publish_max(slot0, b);
+    publish_slot(slot0, 0, b);
   }
 }
 

@@ -285,7 +285,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
   ws.u = (float*)alloc(Bm * r * 4);
   ws.u_hi = (uint16_t*)alloc(Bm * r * 2);
   ws.u_lo = (uint16_t*)alloc(Bm * r * 2);
-  ws.slots = (uint64_t*)alloc(DOMINO_T * Bm * 8);
+  ws.slots = (uint64_t*)alloc(DOMINO_T * Bm * kSlotSpan * 8);
   ws.bad = (int32_t*)alloc(Bm * 4);
   ws.partial = (float*)alloc(step_partial_floats((int)g, (int)r) * sizeof(float));
   if (h->w.fc1_x) {  // in-library step offsets
@@ -339,7 +339,7 @@ extern "C" domino_status_t domino_rollout_create(const domino_config_t* cfg,
       (ws.hp && hipMemset(ws.hp, 0, (Bm + 15) / 16 * 16 * g * 4) != hipSuccess) ||
       hipMemset(ws.pool_ids, 0, Bm * Km * 4) != hipSuccess ||
       // cleared by every run's writeout from then on
-      hipMemset(ws.slots, 0, DOMINO_T * Bm * 8) != hipSuccess ||
+      hipMemset(ws.slots, 0, DOMINO_T * Bm * kSlotSpan * 8) != hipSuccess ||
       hipMemset(ws.bad, 0, Bm * 4) != hipSuccess ||
       hipMemset(ws.hist, 0, Bm * 3 * 2048 * 4) != hipSuccess ||
       hipMemset(ws.base, 0, DOMINO_T * Bm * V * 4) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
@@ -561,7 +561,7 @@ static void enqueue(domino_rollout_t* h, const Workspace& ws, const void* hidden
       sa.tok_key = nullptr;
     } else {
       sa.tok_i32 = nullptr;
-      sa.tok_key = ws.slots + (size_t)(k - 1) * B;
+      sa.tok_key = ws.slots + (size_t)(k - 1) * B * kSlotSpan;
     }
     sa.step = k - 1;
     sa.row0 = 0;
@@ -636,7 +636,7 @@ static size_t carve_static(const domino_rollout_t* h, int B, Workspace& ws, unsi
     off += (bytes + 255) / 256 * 256;
     return p;
   };
-  ws.slots = (uint64_t*)take(DOMINO_T * Bz * 8);
+  ws.slots = (uint64_t*)take(DOMINO_T * Bz * kSlotSpan * 8);
   ws.bad = (int32_t*)take(Bz * 4);
   ws.hist = (uint32_t*)take(Bz * 3 * 2048 * 4);
   ws.state = (uint32_t*)take(Bz * 8 * 4);

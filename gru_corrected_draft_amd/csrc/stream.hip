@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void rowstream_kernel(StreamArgs a) {
       const int cb = threadIdx.x >> 4, n = threadIdx.x & 15;
       const int b = cb * 16 + n;
       if (b < ncl)
-        publish_max(&a.slot_k[c0 + b], umax64(umax64(wb[0][cb][n], wb[1][cb][n]),
+        publish_slot(a.slot_k, c0 + b, umax64(umax64(wb[0][cb][n], wb[1][cb][n]),
                                          umax64(wb[2][cb][n], wb[3][cb][n])));
     }
   }
@@ -558,7 +558,7 @@ __global__ __launch_bounds__(WV * 64) void rowpersist_kernel(StreamArgs a) {
     uint64_t m = wb[0][cb][n];
 #pragma unroll
     for (int v = 1; v < WV; ++v) m = umax64(m, wb[v][cb][n]);
-    if (b < ncl) publish_max(&a.slot_k[c0 + b], m);
+    if (b < ncl) publish_slot(a.slot_k, c0 + b, m);
   }
 }
 

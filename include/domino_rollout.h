@@ -244,7 +244,7 @@ domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int32_t which, 
                                             int64_t* launches);
 
 /* Size of the library's static scratch array on each device (bytes). */
-#define DOMINO_STATIC_SCRATCH_BYTES (4u << 20)
+#define DOMINO_STATIC_SCRATCH_BYTES (6u << 20)
 
 /* For callers that cannot allocate device memory at run time (code under
  * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
@@ -261,7 +261,7 @@ domino_status_t domino_rollout_kernel_times(domino_rollout_t* h, int32_t which, 
  * call on one device shares that device's array: calls whose work overlaps
  * on one device (other streams, other handles, other threads) race and give
  * undefined results; serialise them.  The scratch needed grows with the
- * batch (about 70 KB per request plus 1 MB at g = r = 1024, so up to ~44
+ * batch (about 85 KB per request plus 1 MB at g = r = 1024, so up to ~58
  * requests there); a batch whose scratch exceeds the array is
  * DOMINO_ERR_INVALID_ARG and nothing is launched.  Other arguments and
  * errors as domino_rollout_run (DOMINO_ERR_UNSUPPORTED if the array's
