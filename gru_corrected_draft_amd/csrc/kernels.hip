@@ -524,8 +524,18 @@ __global__ __launch_bounds__(256) void pool_collect_kernel(const uint32_t* __res
     const bool ok = v0 + j * 256 + (int)threadIdx.x < V;
     mk[j] = __ballot(ok && (kv[j] >> 10) >= ns.x);
     if (lane == 0) wcnt[j][w] = __popcll(mk[j]);
-    if (ok && (kv[j] >> 10) == ns.x)  // the few ids of the prefix itself
-      atomicAdd(&hist[((size_t)b * 3 + 2) * 2048 + (kv[j] & 1023u)], 1u);
+    // the ids of the prefix itself go to the last histogram: few, but when
+    // scores tie many, so a wave adds its lanes of the leader's bin at once
+    const bool pe = ok && (kv[j] >> 10) == ns.x;
+    const uint64_t pm = __ballot(pe);
+    if (pm) {
+      const int leader = __ffsll((unsigned long long)pm) - 1;
+      const uint32_t lb = __shfl(kv[j] & 1023u, leader, 64);
+      const uint64_t same = __ballot(pe && (kv[j] & 1023u) == lb);
+      uint32_t* const h2 = hist + ((size_t)b * 3 + 2) * 2048;
+      if (lane == leader) atomicAdd(&h2[lb], (uint32_t)__popcll(same));
+      if (pe && (kv[j] & 1023u) != lb) atomicAdd(&h2[kv[j] & 1023u], 1u);
+    }
   }
   __syncthreads();
   // each kPoolChunk ids (four loads) keep their candidates in their own
@@ -612,17 +622,25 @@ __global__ __launch_bounds__(256) void pool_select_kernel(
   const uint2 s2 = select_bin<2>(bins, state[8 * b + 4], state[8 * b + 5], lds, res);
   const uint32_t T = s2.x;         // the K-th largest key
   const int need = (int)s2.y;      // keys equal to T to take, lowest ids first
+  // f on candidates j0 .. n - 1 of a chunk's stretch, 4 loads at a time (more code made
+  // the common path, which never gets here, slower)
+  auto tail = [&](const uint2* src, int j0, int n, auto&& f) {
+    for (int j = j0; j < n; j += 4) {
+      uint2 t[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) t[i] = src[min(j + i, n - 1)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (j + i < n) f(t[i]);
+    }
+  };
   // f on this thread's candidates in id order
   auto walk = [&](auto&& f) {
 #pragma unroll
     for (int j = 0; j < kSelectPre; ++j)
       if (j < n0) f(e[j]);
-    for (int j = kSelectPre; j < n0; ++j) f(src0[j]);
-    for (int c = c0 + 1; c < c1; ++c) {
-      const int nc = (int)nb[c];
-      const uint2* const src = cb + (size_t)c * kPoolChunk;
-      for (int j = 0; j < nc; ++j) f(src[j]);
-    }
+    tail(src0, kSelectPre, n0, f);
+    for (int c = c0 + 1; c < c1; ++c) tail(cb + (size_t)c * kPoolChunk, 0, (int)nb[c], f);
   };
   int my_gt = 0, my_eq = 0;
   walk([&](uint2 x) {

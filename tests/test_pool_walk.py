@@ -6,7 +6,8 @@ bits are at least that prefix, compacted per 1024-id chunk in (load, wave,
 lane) order, with a count per chunk, and adds the prefix's own ids to the
 last 10-bit histogram; `pool_select_kernel` gives each of its 256 threads a
 run of consecutive chunks, loads up to 24 candidates of the first one at
-clamped places before the threshold is known, counts the keys above and
+clamped places before the threshold is known (the rest 4 at a time, also
+clamped), counts the keys above and
 equal to the threshold, and writes its selected ids from place
 gt + min(eq, need) on.  A mistake in the ordering, the clamps, the chunk
 ownership or the placement gives a pool out of id order, a wrong member at
@@ -122,9 +123,17 @@ def select(cand, cnt, hist2, p22, r1, V, K, clamp=True, cap=True):
         pre = [rd(src0 + (min(j, last) if clamp else j)) for j in range(PRE)]
         n0 = int(cnt[c0]) if c0 < c1 else 0
         items = [pre[j] for j in range(min(PRE, n0))]
-        items += [rd(src0 + j) for j in range(PRE, n0)]
+
+        def tail(src, j0, n):  # 4 loads at a time, clamped to the chunk's last candidate
+            got = []
+            for j in range(j0, n, 4):
+                batch = [rd(src + min(j + i, n - 1)) for i in range(4)]
+                got += [batch[i] for i in range(4) if j + i < n]
+            return got
+
+        items += tail(src0, PRE, n0)
         for c in range(c0 + 1, c1):
-            items += [rd(c * CHUNK + j) for j in range(int(cnt[c]))]
+            items += tail(c * CHUNK, 0, int(cnt[c]))
         runs.append(items)
     gt = [sum(k > T for k, _ in it) for it in runs]
     eq = [sum(k == T for k, _ in it) for it in runs]
