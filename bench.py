@@ -73,12 +73,20 @@ def algorithmic(shape, B, K, union_sizes=None, proposals=15):
             "step_bytes": step_bytes}
 
 
+def _code_only(text):
+    """Source text without comments, trailing blanks and empty lines, so that
+    a comment edit does not mark recorded counters as stale."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "gru_corrected_draft_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -293,7 +293,7 @@ void launch_gru_table(const Shape& s, const DeviceWeights& w, float* G, hipStrea
 // its initial state (empty prefix, rank K) from K itself.
 
 // ------------------------------------------------------- first proposal (p1)
-// argmax over the full vocabulary of base row 0 (t = 0), one word per request
+// argmax over the full vocabulary of base row 0 (t = 0), one argmax word per request
 __global__ __launch_bounds__(256) void row0_argmax_kernel(const float* __restrict__ base, int V,
                                                           uint64_t* __restrict__ slots) {
   const int b = blockIdx.y;
@@ -484,19 +484,19 @@ __global__ __launch_bounds__(256) void pool_hist_kernel(const uint32_t* __restri
     if (h[i]) atomicAdd(&hh[i], h[i]);
 }
 
-// Selection after the second radix pass in two launches instead of three
-// passes over the keys.  Every id whose key's top 22 bits are at least the
-// selected prefix is a candidate: K plus the few other ids of that prefix
-// (the first pass's 11-bit bins of float keys are a quarter octave wide and
-// can hold much of the vocabulary; 22-bit ones hold a handful).
-// pool_collect_kernel compacts the candidates of every kPoolChunk ids, as
-// (key, id) pairs in id order, into those ids' own stretch of cand (no counter shared between
-// workgroups: same-line atomics from many workgroups serialise) and adds the
-// candidates of the selected prefix to the last radix histogram;
-// pool_select_kernel, one workgroup per request, takes the threshold from
-// that histogram and writes the pool in id order: every key above the
-// threshold and the lowest ids of those equal to it.  The selected set is the
-// one of the count and compaction kernels, id for id.
+// The selection after the second radix pass, in two launches instead of a
+// third pass, a count and a compaction over all the keys.  Every id whose
+// key's top 22 bits are at least the selected prefix is a candidate: K plus
+// the few other ids of that prefix (the first pass's 11-bit bins of float
+// keys are a quarter octave wide and can hold much of the vocabulary; 22-bit
+// ones hold a handful).  pool_collect_kernel compacts the candidates of
+// every kPoolChunk ids, as (key, id) pairs in id order, into those ids' own
+// stretch of cand (no counter shared between workgroups: same-line atomics
+// from many workgroups serialise) and adds the candidates of the selected
+// prefix to the last radix histogram; pool_select_kernel, one workgroup per
+// request, takes the threshold from that histogram and writes the pool in id
+// order: every key above the threshold and the lowest ids of those equal to
+// it.
 template <int F>
 __global__ __launch_bounds__(256) void pool_collect_kernel(const uint32_t* __restrict__ keys, int V,
                                                            uint32_t* __restrict__ state,

@@ -80,7 +80,13 @@ def test_kernel_digest_covers_every_source(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     d2 = bench.kernel_source_digest()
     (csrc / "b.h").write_text("y")
-    assert bench.kernel_source_digest() != d2 != d1
+    d3 = bench.kernel_source_digest()
+    assert d3 != d2 != d1
+    # comments and blank lines do not count; code does, even one character
+    (csrc / "b.h").write_text("// a note\ny  /* and another */\n\n")
+    assert bench.kernel_source_digest() == d3
+    (csrc / "b.h").write_text("y;")
+    assert bench.kernel_source_digest() != d3
 
 
 def test_more_than_one_gpu_is_refused():
