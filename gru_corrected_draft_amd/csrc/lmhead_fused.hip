@@ -594,12 +594,13 @@ __device__ __forceinline__ void range_epilogue(const FusedArgs& a, v16f (&acc)[4
         }
         const uint64_t k0 = pack_key(acc[ta][tv][jj * 8], (uint32_t)v);  // position 0 on hh == 0
         best[req] = (hh == 0 && vok) ? umax64(best[req], k0) : best[req];
-        if (ok) {
+        if (ok) {  // non-temporal: the logits are not read back by this kernel (1-4 us at 8 requests)
           float* o = a.base + (size_t)req * V + v + (size_t)(4 * hh) * pstride;
 #pragma unroll
           for (int ii = 0; ii < 7; ++ii)
-            o[(size_t)(8 * (ii >> 2) + (ii & 3)) * pstride] = acc[ta][tv][jj * 8 + ii];
-          if (hh == 0) o[11 * pstride] = acc[ta][tv][jj * 8 + 7];
+            __builtin_nontemporal_store(acc[ta][tv][jj * 8 + ii],
+                                        &o[(size_t)(8 * (ii >> 2) + (ii & 3)) * pstride]);
+          if (hh == 0) __builtin_nontemporal_store(acc[ta][tv][jj * 8 + 7], &o[11 * pstride]);
         }
       }
 #pragma unroll
