@@ -765,11 +765,14 @@ __global__ __launch_bounds__(256) void union_members_kernel(
   const int b = idx / K;
   const int g = b / ug, bl = b % ug;
   const int v = pool_ids[idx];
-  // the row index and the 14 base values in one round trip, then the record
+  // the row index and the 14 base values in one round trip, then the record;
+  // the values are used once, so their lines are not kept in L2 (45 -> 40 us
+  // at 8B, 64 requests, K = 2048)
   const int ui = uidx[(size_t)g * V + v];
   float vals[DOMINO_S];
 #pragma unroll
-  for (int t = 0; t < DOMINO_S; ++t) vals[t] = base[((size_t)(t + 1) * B + b) * V + v];
+  for (int t = 0; t < DOMINO_S; ++t)
+    vals[t] = __builtin_nontemporal_load(&base[((size_t)(t + 1) * B + b) * V + v]);
   __builtin_amdgcn_sched_barrier(0);
   const uint4 rc = urec[(size_t)g * umax + ui];
   const uint32_t slot = rc.z + __popc(rc.w & ((1u << bl) - 1u));
