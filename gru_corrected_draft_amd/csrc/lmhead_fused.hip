@@ -667,14 +667,18 @@ __global__ __launch_bounds__(512) void lmhead_range_kernel(FusedArgs a) {
       xoff[i] = ((uint32_t)req * DOMINO_T + (uint32_t)pos) * hrow + (uint32_t)(pp ^ (((R & 31) >> 1) & 7));
     }
     u32x4 AW[kMVCopies], AX[kMXCopies], BW[kMVCopies], BX[kMXCopies];
-    // stage Q (clamped to the last: those loads refill a set nobody reads)
+    // stage Q (clamped to the last: those loads refill a set nobody reads);
+    // lm_head non-temporal (read once: 8B B = 8 LM-head 265 -> 258 us, the
+    // pool cell's block 0.554 -> 0.525 ms), the activations cached (re-read
+    // for every chunk)
 #define RANGE_LOAD(RW, RX, Q)                                                       \
   {                                                                                 \
     const int q_ = min((Q), nq - 1), c_ = q_ / ns, s_ = q_ - c_ * ns;               \
     const int rc_ = r0 + c_ * kMV + rr;                                             \
     _Pragma("unroll") for (int i = 0; i < kMVCopies; ++i) {                         \
       const int v_ = rc_ + (w4 + 4 * i) * 8;                                        \
-      RW[i] = Wv[(uint32_t)(v_ < rend ? v_ : r0) * hrow + wsc[i] + 8u * s_];        \
+      RW[i] = __builtin_nontemporal_load(                                           \
+          &Wv[(uint32_t)(v_ < rend ? v_ : r0) * hrow + wsc[i] + 8u * s_]);           \
     }                                                                               \
     _Pragma("unroll") for (int i = 0; i < kMXCopies; ++i) RX[i] = Xv[xoff[i] + 8u * s_]; \
   }

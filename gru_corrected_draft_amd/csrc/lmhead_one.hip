@@ -47,12 +47,16 @@ namespace {
 // 4 i .. 4 i + 3 (i = j % 4) of the j / 4-th 128-k block, lane l row
 // 4 i + l / 16, chunk l % 16 of the block's 256 bytes.  W is deliberately not
 // __restrict__ (with a restrict pointer to read-only data the optimizer
-// moved loads next to their uses).
+// moved loads next to their uses).  The loads are non-temporal: every line is
+// read once, and lm_head lines kept in the L2s would only displace what the
+// rest of the rollout reads (8B: 214 -> 193 us for this kernel, and the pool
+// cell's block 0.410 -> 0.367 ms).
 __device__ __forceinline__ uint4 one_ld(const bf16_t* W, int t, int sub, int j, int S, int V, int H,
                                         int kbase, int row, int q) {
   const int i = j & 3, kb = j >> 2;
-  return *reinterpret_cast<const uint4*>(W + kbase + 256 * sub + 128 * kb + 8 * row +
-                                         (size_t)min((4 * i + q) * S + t, V - 1) * H);
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+      W + kbase + 256 * sub + 128 * kb + 8 * row + (size_t)min((4 * i + q) * S + t, V - 1) * H));
+  return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
 template <int WV, int KS>
