@@ -41,6 +41,13 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                    (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
 }
+// the same for lm_head: non-temporal, since every line is read once (kept in
+// the L2s, it only displaces what later kernels read; 8B K = 2048 blocks at
+// 12 and 16 requests 3% faster)
+__device__ __forceinline__ void dma16_nt(const void* src, void* dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, 0, 2);
+}
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_barrier" ::: "memory"); }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
@@ -138,7 +145,7 @@ __global__ __launch_bounds__(256) void lmhead_fused_kernel(FusedArgs a) {
     unsigned char* slot = ring + (s % kStages) * kSliceBytes;
     const uint32_t kb = (uint32_t)s * 64u;  // 32 bf16 per slice
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(Wb + (aoff[i] + kb), slot + (wave * 4 + i) * 1024);
+    for (int i = 0; i < 4; ++i) dma16_nt(Wb + (aoff[i] + kb), slot + (wave * 4 + i) * 1024);
 #pragma unroll
     for (int i = 0; i < 3; ++i) dma16(Xb + (boff[i] + kb), slot + (16 + wave + 4 * i) * 1024);
     if (four_b) dma16(Xb + (boff[3] + kb), slot + (16 + wave + 12) * 1024);
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(256) void lmhead_lines_kernel(FusedArgs a) {
     unsigned char* slot = aring + (s % kARing) * kAStage;
     const uint32_t kb = (uint32_t)s * (kStageK * 2);
 #pragma unroll
-    for (int i = 0; i < kACopies; ++i) dma16(Wb + (aoff[i] + kb), slot + (wave + 4 * i) * 1024);
+    for (int i = 0; i < kACopies; ++i) dma16_nt(Wb + (aoff[i] + kb), slot + (wave + 4 * i) * 1024);
   };
   auto issue_b = [&](int s) {
     unsigned char* slot = bring + (s % kBRing) * kBStage;
@@ -423,7 +430,7 @@ __global__ __launch_bounds__(256) void lmhead_m32_kernel(FusedArgs a) {
     unsigned char* xs = xring + (s % kMRing) * kMXStage;
     const uint32_t kb = (uint32_t)s * (kMK * 2);
 #pragma unroll
-    for (int i = 0; i < kMVCopies; ++i) dma16(Wb + (woff[i] + kb), ws + (wave + 4 * i) * 1024);
+    for (int i = 0; i < kMVCopies; ++i) dma16_nt(Wb + (woff[i] + kb), ws + (wave + 4 * i) * 1024);
 #pragma unroll
     for (int i = 0; i < kMXCopies; ++i) dma16(Xb + (xoff[i] + kb), xs + (wave + 4 * i) * 1024);
   };
