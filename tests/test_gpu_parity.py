@@ -182,6 +182,25 @@ def test_tiny_vocabulary(B):
                 assert np.array_equal(ids[b], ref["pools"][b]), f"pool of request {b}"
 
 
+# projector width 1024 (the 8B width) on a ragged 5003-id vocabulary: eight
+# 128-wide k chunks per fc2 row in the full-vocabulary stream, and a last
+# 16-row tile with 11 rows past the vocabulary
+R1024 = synth.custom_shape(5003, 256, 128, 128, 1024, "bf16", 85, name="bf16-r1024")
+
+
+@pytest.mark.parametrize("B", [1, 3, 8])
+def test_full_vocabulary_correction_r1024(B):
+    """Tokens and top-1 logits against the oracle, eager and graph (bit for
+    bit between the two), at K = 0."""
+    G.log(f"[gpu-test] r=1024 full-vocabulary correction B={B}")
+    tok, top, h = G.gpu_run(R1024, B, 970 + B, 0, 0, max_batch=8, max_k=1)
+    ref = G.oracle_run(R1024, B, 970 + B, 0, 0)
+    c, _ = compare(tok, top, ref, TOL["bf16"])
+    assert c > 0
+    tok_g, top_g, _ = G.gpu_run(R1024, B, 970 + B, 0, 0, max_batch=8, max_k=1, graph=True)
+    assert np.array_equal(tok, tok_g) and np.array_equal(top.view(np.uint32), top_g.view(np.uint32))
+
+
 # 300007 ids: 293 chunks of 1024, more than the pool selection workgroup has
 # threads, so some of its threads walk the candidates of two chunks
 LARGE_V = synth.custom_shape(300007, 256, 128, 128, 128, "bf16", 84, name="bf16-vocab-300007")
