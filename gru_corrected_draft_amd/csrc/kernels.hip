@@ -793,13 +793,16 @@ static bool pool_lines(const Shape& s, int B) {
 
 template <int F>
 static void pool_select_passes(const Shape& s, const Workspace& ws, int B, int K, bool keys_ready,
-                               bool uni, hipStream_t st) {
+                               bool hist_ready, bool uni, hipStream_t st) {
   const int nch = (s.V + F * kPoolChunk - 1) / (F * kPoolChunk);
   const dim3 grid(nch, B), blk(256);
-  if (keys_ready)
+  if (hist_ready) {
+    // the LM-head counted the keys itself
+  } else if (keys_ready) {
     DLAUNCH((pool_hist_kernel<0, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, K);
-  else
+  } else {
     DLAUNCH((pool_score_hist_kernel<F>), grid, blk, 0, st, ws.base, s.V, B, ws.keys, ws.hist);
+  }
   DLAUNCH((pool_hist_kernel<1, F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, K);
   const int nsub = (s.V + kPoolChunk - 1) / kPoolChunk;
   DLAUNCH((pool_collect_kernel<F>), grid, blk, 0, st, ws.keys, s.V, ws.state, ws.hist, ws.cand,
@@ -809,16 +812,16 @@ static void pool_select_passes(const Shape& s, const Workspace& ws, int B, int K
 }
 
 void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
-                       bool keys_ready, hipStream_t st) {
+                       bool keys_ready, bool hist_ready, hipStream_t st) {
   const int nch = (s.V + kPoolChunk - 1) / kPoolChunk;  // union kernels: kPoolChunk ids per chunk
   const dim3 blk(256);
   const bool uni = pool_union(s, ws, B, K);
   if (B >= kPoolChunk4MinBatch)
-    pool_select_passes<4>(s, ws, B, K, keys_ready, uni, st);
+    pool_select_passes<4>(s, ws, B, K, keys_ready, hist_ready, uni, st);
   else if (B >= kPoolChunk2MinBatch)
-    pool_select_passes<2>(s, ws, B, K, keys_ready, uni, st);
+    pool_select_passes<2>(s, ws, B, K, keys_ready, hist_ready, uni, st);
   else
-    pool_select_passes<1>(s, ws, B, K, keys_ready, uni, st);
+    pool_select_passes<1>(s, ws, B, K, keys_ready, hist_ready, uni, st);
   if (uni) {
     const dim3 ug(nch, (B + ws.ugroup - 1) / ws.ugroup);
     DLAUNCH(union_count_kernel, ug, blk, 0, st, ws.umask, s.V, ws.ucounts, nch);

@@ -225,22 +225,25 @@ size_t lmhead_xfrag_elems(int B, int H);
 
 void launch_lmhead(const Shape& s, const void* W, const void* X, float* out, int B, hipStream_t st);
 // One-request LM-head with whole-line lm_head loads (lmhead_one.hip): base
-// logits [15, 1, V], the pool score keys (when keys is not nullptr) and the
-// first-proposal argmax word *slot0; bf16, H a multiple of 1024 up to 5120
-// and V small enough for one CU's share of tiles to stay in LDS.
+// logits [15, 1, V], the pool score keys (when keys is not nullptr), their
+// first radix histogram added into hist0 [2048] (when not nullptr; zero
+// before) and the first-proposal argmax word *slot0; bf16, H a multiple of
+// 1024 up to 5120 and V small enough for one CU's share of tiles to stay in
+// LDS.
 bool lmhead_one_supported(int V, int H);
 int cu_count();
 void lmhead_one_prepare();
 void launch_lmhead_one(const uint16_t* W, const uint16_t* X, float* out, uint32_t* keys,
-                       uint64_t* slot0, int V, int H, hipStream_t st);
+                       uint32_t* hist0, uint64_t* slot0, int V, int H, hipStream_t st);
 void launch_row0_argmax(const Shape& s, const float* base, int B, uint64_t* slots, hipStream_t st);
 // Whether a pool correction of B requests streams each request group's
 // union of pool rows once (instead of gathering every request's rows).
 bool pool_union(const Shape& s, const Workspace& ws, int B, int K);
 // keys_ready: the per-id scores were already written by the fused LM-head;
+// hist_ready: and their first radix histogram (the one-request LM-head);
 // with pool_union(), also the per-group unions and member base values
 void launch_pool_build(const Shape& s, const Workspace& ws, const void* fc2_b, int B, int K,
-                       bool keys_ready, hipStream_t st);
+                       bool keys_ready, bool hist_ready, hipStream_t st);
 void launch_correct_full(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,
                          hipStream_t st);
 void launch_correct_pool(const Shape& s, const DeviceWeights& w, const Workspace& ws, int k, int B,

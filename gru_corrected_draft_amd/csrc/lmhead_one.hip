@@ -37,6 +37,10 @@
 //    along t.  The workgroup publishes its first-proposal word once.
 //  * A workgroup takes a contiguous range of t (ranges balanced to one tile),
 //    one workgroup per CU.
+//  * With a pool to build, the workgroup also counts its keys by their top
+//    11 bits (the pool selection's first radix histogram) in LDS and adds
+//    the nonzero bins to the histogram in memory, so the selection starts
+//    at its second pass.
 #include "common.h"
 #include "launch.h"
 
@@ -64,6 +68,7 @@ __global__ __launch_bounds__(WV * 64) void lmhead_one_kernel(const bf16_t* W,
                                                              const bf16_t* __restrict__ X,
                                                              float* __restrict__ out,
                                                              uint32_t* __restrict__ keys,
+                                                             uint32_t* __restrict__ hist0,
                                                              uint64_t* __restrict__ slot0, int V,
                                                              int H, int maxt) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -79,6 +84,8 @@ __global__ __launch_bounds__(WV * 64) void lmhead_one_kernel(const bf16_t* W,
   // (maxt tiles at most)
   float* const zout = red + 2 * WV * 256;
   uint32_t* const kout = reinterpret_cast<uint32_t*>(zout + maxt * 256);
+  uint32_t* const hloc = kout + maxt * 16;  // [2048] keys by their top 11 bits
+  for (int i = threadIdx.x; i < 2048; i += WV * 64) hloc[i] = 0;  // ordered by the tile barriers
 
   // this wave's activation fragments: column `row` (draft position; 15 is zero)
   v8s xf[KS];
@@ -181,9 +188,19 @@ __global__ __launch_bounds__(WV * 64) void lmhead_one_kernel(const bf16_t* W,
     const int n = i % ntiles, rc = i / ntiles, col = rc >> 4, r = rc & 15;
     const int v = r * S + t0 + n;
     if (v < V) {
-      if (col < DOMINO_T) out[(size_t)col * V + v] = zout[n * 256 + col * 16 + r];
-      else if (keys) keys[v] = kout[n * 16 + r];
+      if (col < DOMINO_T) {
+        out[(size_t)col * V + v] = zout[n * 256 + col * 16 + r];
+      } else if (keys) {
+        const uint32_t key = kout[n * 16 + r];
+        keys[v] = key;
+        if (hist0) atomicAdd(&hloc[key >> 21], 1u);
+      }
     }
+  }
+  if (hist0) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < 2048; i += WV * 64)
+      if (hloc[i]) atomicAdd(&hist0[i], hloc[i]);
   }
   // first proposal: the workgroup's best (value, lowest id), published once
 #pragma unroll
@@ -201,7 +218,7 @@ __global__ __launch_bounds__(WV * 64) void lmhead_one_kernel(const bf16_t* W,
 
 size_t one_lds(int wv, int maxt) {
   return (size_t)wv * 8192 + 2 * (size_t)wv * 256 * sizeof(float) +
-         (size_t)maxt * (256 + 16) * sizeof(float);
+         (size_t)maxt * (256 + 16) * sizeof(float) + 2048 * sizeof(uint32_t);
 }
 constexpr size_t kOneLdsLimit = 156 * 1024;  // dynamic LDS (the static part is WV words)
 
@@ -213,12 +230,12 @@ void one_grid(int V, int* grid, int* maxt) {
 }
 
 template <int WV, int KS>
-void one_launch(const uint16_t* W, const uint16_t* X, float* out, uint32_t* keys, uint64_t* slot0,
-                int V, int H, hipStream_t st) {
+void one_launch(const uint16_t* W, const uint16_t* X, float* out, uint32_t* keys, uint32_t* hist0,
+                uint64_t* slot0, int V, int H, hipStream_t st) {
   int grid, maxt;
   one_grid(V, &grid, &maxt);
   DLAUNCH((lmhead_one_kernel<WV, KS>), dim3(grid), dim3(WV * 64), one_lds(WV, maxt), st,
-          (const bf16_t*)W, (const bf16_t*)X, out, keys, slot0, V, H, maxt);
+          (const bf16_t*)W, (const bf16_t*)X, out, keys, hist0, slot0, V, H, maxt);
 }
 
 }  // namespace
@@ -264,14 +281,14 @@ void lmhead_one_prepare() {
 }
 
 void launch_lmhead_one(const uint16_t* W, const uint16_t* X, float* out, uint32_t* keys,
-                       uint64_t* slot0, int V, int H, hipStream_t st) {
+                       uint32_t* hist0, uint64_t* slot0, int V, int H, hipStream_t st) {
   int wv, ks;
   one_shape(H, &wv, &ks);
   switch (wv) {
-    case 2: one_launch<2, 16>(W, X, out, keys, slot0, V, H, st); break;
-    case 4: one_launch<4, 16>(W, X, out, keys, slot0, V, H, st); break;
-    case 6: one_launch<6, 16>(W, X, out, keys, slot0, V, H, st); break;
-    case 8: one_launch<8, 16>(W, X, out, keys, slot0, V, H, st); break;
-    default: one_launch<10, 16>(W, X, out, keys, slot0, V, H, st); break;
+    case 2: one_launch<2, 16>(W, X, out, keys, hist0, slot0, V, H, st); break;
+    case 4: one_launch<4, 16>(W, X, out, keys, hist0, slot0, V, H, st); break;
+    case 6: one_launch<6, 16>(W, X, out, keys, hist0, slot0, V, H, st); break;
+    case 8: one_launch<8, 16>(W, X, out, keys, hist0, slot0, V, H, st); break;
+    default: one_launch<10, 16>(W, X, out, keys, hist0, slot0, V, H, st); break;
   }
 }

@@ -489,7 +489,8 @@ static void enqueue(domino_rollout_t* h, const Workspace& ws, const void* hidden
     // base logits, pool-score keys and the first proposal in one pass
     PhaseTimer t(h, kLmHead, st);
     launch_lmhead_one((const uint16_t*)h->w.lm_head, (const uint16_t*)hidden, ws.base,
-                      pool ? ws.keys : nullptr, ws.slots, sh.V, sh.H, st);
+                      pool ? ws.keys : nullptr, pool ? ws.hist : nullptr, ws.slots, sh.V, sh.H,
+                      st);
   } else if (fused) {
     // base logits, pool-score keys and the first proposal in one pass
     PhaseTimer t(h, kLmHead, st);
@@ -506,7 +507,7 @@ static void enqueue(domino_rollout_t* h, const Workspace& ws, const void* hidden
   }
   if (pool) {
     PhaseTimer t(h, kPool, st);
-    launch_pool_build(sh, ws, h->w.fc2_b, B, K, fused || one, st);
+    launch_pool_build(sh, ws, h->w.fc2_b, B, K, fused || one, one, st);
   }
   // Prefix: h(1) = GRU(E[verified], 0) and c(1) = W_hh h(1).  It runs for
   // every P: its gates are where an invalid verified token is flagged.
