@@ -11,16 +11,19 @@
 // weight stream.  On MI355X a load-only probe of a [151936, 4096] bf16
 // matrix streamed 16 rows x 64 B per load instruction (the shape of an MFMA
 // operand fragment) at 4.4 TB/s, but 4 rows x 256 B (whole 128-byte lines)
-// at 5.8 TB/s, and 6.1 TB/s with the 16 rows of a tile spread ceil(V / 16)
-// rows apart; direct global->LDS copies of the same lines reached only
-// 1.8-3.7 TB/s.  This kernel therefore loads lm_head as whole lines into
-// registers and turns them into fragments through LDS:
+// at 5.8 TB/s (cached loads); direct global->LDS copies of the same lines
+// reached only 1.8-3.7 TB/s.  This kernel therefore loads lm_head as whole
+// lines into registers and turns them into fragments through LDS:
 //  * The H/512 waves of a workgroup split K: wave w owns k in
 //    [512 w, 512 w + 512) and keeps its 16 activation fragments (15 rows
 //    plus a zero row, 64 VGPRs) in registers for the whole launch.
-//  * A tile is 16 lm_head rows, row r of tile t being row r S + t
-//    (S = ceil(V / 16)).  A wave streams its K range of a tile in two
-//    stages of 256 k, each eight loads of 4 rows x 256 B, the next stage in
+//  * A tile is 16 consecutive lm_head rows (128 KB at H = 4096).  With
+//    non-temporal loads a probe of this kernel's load pattern streamed
+//    consecutive rows as fast as rows ceil(V / 16) apart (182.8 / 182.7 us
+//    at 8B), and consecutive rows make each workgroup's logits and keys one
+//    contiguous range (whole-line stores: LM-head 192.7 -> 190.2 us, the
+//    K = 2048 block 0.366 -> 0.363 ms).  A wave streams its K range of a
+//    tile in two stages of 256 k, each eight loads of 4 rows x 256 B, the next stage in
 //    flight while one is consumed.  (A deeper ring in registers made the
 //    compiler wait for all but the newest stage at the loop head; with two
 //    stages that wait is exactly the one needed.)  A stage goes through the
@@ -34,7 +37,8 @@
 //    of each row and a running first-proposal maximum are kept; the sums and
 //    keys stay in LDS (a global store inside the loop also made the compiler
 //    over-wait) and are written after the last tile, consecutive threads
-//    along t.  The workgroup publishes its first-proposal word once.
+//    on consecutive ids.  The workgroup publishes its first-proposal word
+//    once.
 //  * A workgroup takes a contiguous range of t (ranges balanced to one tile),
 //    one workgroup per CU.
 //  * With a pool to build, the workgroup also counts its keys by their top
@@ -55,11 +59,11 @@ namespace {
 // read once, and lm_head lines kept in the L2s would only displace what the
 // rest of the rollout reads (8B: 214 -> 193 us for this kernel, and the pool
 // cell's block 0.410 -> 0.367 ms).
-__device__ __forceinline__ uint4 one_ld(const bf16_t* W, int t, int sub, int j, int S, int V, int H,
+__device__ __forceinline__ uint4 one_ld(const bf16_t* W, int t, int sub, int j, int V, int H,
                                         int kbase, int row, int q) {
   const int i = j & 3, kb = j >> 2;
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
-      W + kbase + 256 * sub + 128 * kb + 8 * row + (size_t)min((4 * i + q) * S + t, V - 1) * H));
+      W + kbase + 256 * sub + 128 * kb + 8 * row + (size_t)min(16 * t + 4 * i + q, V - 1) * H));
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
@@ -108,14 +112,14 @@ __global__ __launch_bounds__(WV * 64) void lmhead_one_kernel(const bf16_t* W,
 #define ONE_LOAD8(G, X)                                                                          \
   {                                                                                              \
     const int tt_ = stage_tile(G), ss_ = stage_sub(G);                                           \
-    X##0 = one_ld(W, tt_, ss_, 0, S, V, H, kbase, row, q);                                       \
-    X##1 = one_ld(W, tt_, ss_, 1, S, V, H, kbase, row, q);                                       \
-    X##2 = one_ld(W, tt_, ss_, 2, S, V, H, kbase, row, q);                                       \
-    X##3 = one_ld(W, tt_, ss_, 3, S, V, H, kbase, row, q);                                       \
-    X##4 = one_ld(W, tt_, ss_, 4, S, V, H, kbase, row, q);                                       \
-    X##5 = one_ld(W, tt_, ss_, 5, S, V, H, kbase, row, q);                                       \
-    X##6 = one_ld(W, tt_, ss_, 6, S, V, H, kbase, row, q);                                       \
-    X##7 = one_ld(W, tt_, ss_, 7, S, V, H, kbase, row, q);                                       \
+    X##0 = one_ld(W, tt_, ss_, 0, V, H, kbase, row, q);                                          \
+    X##1 = one_ld(W, tt_, ss_, 1, V, H, kbase, row, q);                                          \
+    X##2 = one_ld(W, tt_, ss_, 2, V, H, kbase, row, q);                                          \
+    X##3 = one_ld(W, tt_, ss_, 3, V, H, kbase, row, q);                                          \
+    X##4 = one_ld(W, tt_, ss_, 4, V, H, kbase, row, q);                                          \
+    X##5 = one_ld(W, tt_, ss_, 5, V, H, kbase, row, q);                                          \
+    X##6 = one_ld(W, tt_, ss_, 6, V, H, kbase, row, q);                                          \
+    X##7 = one_ld(W, tt_, ss_, 7, V, H, kbase, row, q);                                          \
   }
 #define ONE_PUT(J, X)                                                                            \
   {                                                                                              \
@@ -164,7 +168,7 @@ __global__ __launch_bounds__(WV * 64) void lmhead_one_kernel(const bf16_t* W,
 #pragma unroll
       for (int w = 1; w < WV; ++w) z += rp[w * 256 + e];
       const int le = e >> 2, r = 4 * (le >> 4) + (e & 3), col = le & 15;
-      const int v = r * S + t0 + n;
+      const int v = 16 * (t0 + n) + r;
       const bool ok = v < V;
       zout[n * 256 + col * 16 + r] = z;
       // the row's maximum over the 15 positions: lanes (e & 3) + 4 col
@@ -183,10 +187,11 @@ __global__ __launch_bounds__(WV * 64) void lmhead_one_kernel(const bf16_t* W,
 #undef ONE_PUT
 #undef ONE_LOAD8
   __syncthreads();
-  // the workgroup's logits [15, V] and keys, consecutive threads along t
+  // the workgroup's logits [15, V] and keys: for each position one contiguous
+  // range of ids, consecutive threads on consecutive ids
   for (int i = threadIdx.x; i < ntiles * 16 * 16; i += WV * 64) {
-    const int n = i % ntiles, rc = i / ntiles, col = rc >> 4, r = rc & 15;
-    const int v = r * S + t0 + n;
+    const int r = i & 15, nc = i >> 4, n = nc % ntiles, col = nc / ntiles;
+    const int v = 16 * (t0 + n) + r;
     if (v < V) {
       if (col < DOMINO_T) {
         out[(size_t)col * V + v] = zout[n * 256 + col * 16 + r];
