@@ -624,13 +624,13 @@ __device__ __forceinline__ void range_epilogue(const FusedArgs& a, v16f (&acc)[4
 // kernel's products, LDS layout and epilogue.  Waves 4..7 produce: they
 // stage both operands through registers (a load-only probe streamed
 // lm_head-shaped rows at 1.8-3.7 TB/s through direct global->LDS copies,
-// 6.1 TB/s through registers) into two LDS slots, two k stages ahead.
-// Waves 0..3 consume: each owns TV tiles of a chunk against all 8 requests
-// and takes one stage's products from LDS per barrier, so the matrix cores
-// work while the producers' loads are in flight.  (With every wave doing
-// both, a stage's products and loads ran one after the other: 8B B = 8
-// 338 against 279 us.)  The chunks form one flat sequence of stages, so the
-// next chunk's first two stages are loading during a chunk's epilogue.
+// 6.1 TB/s through registers) into two LDS slots.  Waves 0..3 consume: each
+// owns TV tiles of a chunk against all 8 requests and takes one stage's
+// products from LDS per barrier, so the matrix cores work while the
+// producers' loads are in flight.  (With every wave doing both, a stage's products and loads ran one
+// after the other: 8B B = 8 338 against 279 us.)  The chunks form one flat
+// sequence of stages, so the next chunk's first stages are loading during a
+// chunk's epilogue.
 // Rows past the range (the last chunk's missing tiles) re-read the range's
 // first row, an L2 hit, instead of branching around the load.  Each
 // consumer lane keeps its position-0 maxima across chunks; the workgroup
@@ -673,12 +673,11 @@ __global__ __launch_bounds__(512) void lmhead_range_kernel(FusedArgs a) {
       const int pos = min(R & 15, DOMINO_T - 1);
       xoff[i] = ((uint32_t)req * DOMINO_T + (uint32_t)pos) * hrow + (uint32_t)(pp ^ (((R & 31) >> 1) & 7));
     }
-    u32x4 AW[kMVCopies], AX[kMXCopies], BW[kMVCopies], BX[kMXCopies];
     // stage Q (clamped to the last: those loads refill a set nobody reads);
     // lm_head non-temporal (read once: 8B B = 8 LM-head 265 -> 258 us, the
     // pool cell's block 0.554 -> 0.525 ms), the activations cached (re-read
     // for every chunk)
-#define RANGE_LOAD(RW, RX, Q)                                                       \
+#define RANGE_LOAD_W(RW, Q)                                                         \
   {                                                                                 \
     const int q_ = min((Q), nq - 1), c_ = q_ / ns, s_ = q_ - c_ * ns;               \
     const int rc_ = r0 + c_ * kMV + rr;                                             \
@@ -687,6 +686,10 @@ __global__ __launch_bounds__(512) void lmhead_range_kernel(FusedArgs a) {
       RW[i] = __builtin_nontemporal_load(                                           \
           &Wv[(uint32_t)(v_ < rend ? v_ : r0) * hrow + wsc[i] + 8u * s_]);           \
     }                                                                               \
+  }
+#define RANGE_LOAD_X(RX, Q)                                                         \
+  {                                                                                 \
+    const int q_ = min((Q), nq - 1), s_ = q_ % ns;                                  \
     _Pragma("unroll") for (int i = 0; i < kMXCopies; ++i) RX[i] = Xv[xoff[i] + 8u * s_]; \
   }
 #define RANGE_PUT(RW, RX, SLOT)                                                     \
@@ -698,26 +701,70 @@ __global__ __launch_bounds__(512) void lmhead_range_kernel(FusedArgs a) {
     _Pragma("unroll") for (int i = 0; i < kMXCopies; ++i)                           \
       *reinterpret_cast<u32x4*>(xs_ + (w4 + 4 * i) * 1024) = RX[i];                 \
   }
-    RANGE_LOAD(AW, AX, 0)
-    RANGE_LOAD(BW, BX, 1)
-    RANGE_PUT(AW, AX, 0)
-    __syncthreads();
-    // in the stage that the consumers take from one slot, stage Q + 1 (set
-    // NW/NX, loaded one stage earlier) goes into the other slot, whose stage
-    // Q - 1 they finished before the last barrier, and stage Q + 2 into set
-    // CW/CX, whose stage Q is in LDS
-    for (int q = 0; q < nq; q += 2) {  // nq is even
-      RANGE_LOAD(AW, AX, q + 2)
-      __builtin_amdgcn_sched_barrier(0);  // the loads go out before the wait for the other set
-      RANGE_PUT(BW, BX, 1)
+    if constexpr (TV == 1) {
+      // Three lm_head register sets (two activation sets): while the
+      // consumers take stage Q from slot Q % 2, a step loads the activations
+      // of stage Q + 2 and the lm_head rows of stage Q + 3, in that order,
+      // then puts stage Q + 1 into the other slot (its stage Q - 1 was
+      // finished before the last barrier), so the wait for stage Q + 1 leaves
+      // the lm_head loads of stages Q + 2 and Q + 3 in flight.  Six steps
+      // cover both set rotations; a step runs only when every earlier one
+      // did.  8B LM-head us on one box, three / two sets: B = 2 230-247 /
+      // 238-255, 3 234-237 / 243, 4 237-238 / 246.  (At TV = 3 a third set
+      // does not fit the registers: the producers spilled loaded data and
+      // B = 8 took 401 against 266 us.)
+      u32x4 W0[kMVCopies], W1[kMVCopies], W2[kMVCopies], X0[kMXCopies], X1[kMXCopies];
+      RANGE_LOAD_W(W0, 0)
+      RANGE_LOAD_X(X0, 0)
+      RANGE_LOAD_W(W1, 1)
+      RANGE_LOAD_X(X1, 1)
+      RANGE_LOAD_W(W2, 2)
+      RANGE_PUT(W0, X0, 0)
       __syncthreads();
-      RANGE_LOAD(BW, BX, q + 3)
-      __builtin_amdgcn_sched_barrier(0);
+#define RANGE_STEP(I, LX, LW, PW, PX, SLOT)                                         \
+  if (q + (I) >= nq) break;                                                       \
+  RANGE_LOAD_X(LX, q + (I) + 2)                                                   \
+  RANGE_LOAD_W(LW, q + (I) + 3)                                                   \
+  __builtin_amdgcn_sched_barrier(0); /* the loads go out before the wait */       \
+  RANGE_PUT(PW, PX, SLOT)                                                         \
+  __syncthreads();
+      for (int q = 0; q < nq; q += 6) {
+        RANGE_STEP(0, X0, W0, W1, X1, 1)
+        RANGE_STEP(1, X1, W1, W2, X0, 0)
+        RANGE_STEP(2, X0, W2, W0, X1, 1)
+        RANGE_STEP(3, X1, W0, W1, X0, 0)
+        RANGE_STEP(4, X0, W1, W2, X1, 1)
+        RANGE_STEP(5, X1, W2, W0, X0, 0)
+      }
+#undef RANGE_STEP
+    } else {
+      // two register sets: in the stage that the consumers take from one
+      // slot, stage Q + 1 (set B, loaded one stage earlier) goes into the
+      // other slot, whose stage Q - 1 they finished before the last barrier,
+      // and stage Q + 2 into set A, whose stage Q is in LDS
+      u32x4 AW[kMVCopies], AX[kMXCopies], BW[kMVCopies], BX[kMXCopies];
+      RANGE_LOAD_W(AW, 0)
+      RANGE_LOAD_X(AX, 0)
+      RANGE_LOAD_W(BW, 1)
+      RANGE_LOAD_X(BX, 1)
       RANGE_PUT(AW, AX, 0)
       __syncthreads();
+      for (int q = 0; q < nq; q += 2) {  // nq is even
+        RANGE_LOAD_W(AW, q + 2)
+        RANGE_LOAD_X(AX, q + 2)
+        __builtin_amdgcn_sched_barrier(0);  // the loads go out before the wait for the other set
+        RANGE_PUT(BW, BX, 1)
+        __syncthreads();
+        RANGE_LOAD_W(BW, q + 3)
+        RANGE_LOAD_X(BX, q + 3)
+        __builtin_amdgcn_sched_barrier(0);
+        RANGE_PUT(AW, AX, 0)
+        __syncthreads();
+      }
     }
 #undef RANGE_PUT
-#undef RANGE_LOAD
+#undef RANGE_LOAD_X
+#undef RANGE_LOAD_W
     wait_vm<0>();  // the clamped loads past the last stage
     __syncthreads();
   } else {
@@ -994,10 +1041,10 @@ template <int TV>
 constexpr size_t kRangeLds = 2 * ((size_t)M32<TV>::kVStage + kMXStage);  // 64 / 128 KB
 // The range kernel's chunk is 4 TV tiles of 32 rows: one tile per consumer
 // wave (five chunks of an 8B range of 18-19 tiles) up to 4 requests, three
-// from 5 (two chunks: fewer epilogues and activation passes, which cost
-// more than the last chunk's idle tiles once the epilogue stores grow).
-// 8B LM-head us, TV = 1 / 3: B = 2 252 / 256, 3 250 / 256, 4 256 / 257,
-// 5 261 / 260, 6 264 / 261, 7 271 / 263, 8 279 / 267.
+// from 5 (two chunks: fewer epilogues and activation passes).  8B LM-head us
+// on one box, TV = 1 (three register sets) / TV = 3 (two): B = 5 245-256 /
+// 250-260, 6 248 / 255, 7 252 / 257-261, 8 255-258 / 253-261: within the
+// spread between boxes from 5 requests, so those keep TV = 3.
 constexpr int kRangeSmallBatch = 4;
 // the stage loops run in pairs of 64-wide k stages
 bool lmhead_range_supported(int H) { return H % (2 * kMK) == 0; }

@@ -3,9 +3,10 @@
 `lmhead_range_kernel` (csrc/lmhead_fused.hip) gives each workgroup a
 contiguous range of 32-row vocabulary tiles and walks it in chunks of 4 TV
 tiles.  Producer waves 4..7 load 64-wide k stages of the chunk's lm_head rows
-and of the activation rows into two LDS slots, two stages ahead; consumer
-waves 0..3 take one stage per barrier and store each chunk's logits at its
-end.  A mistake in the range split, the clamped rows, the chunk swizzle, the
+and of the activation rows through register sets into two LDS slots (at
+TV = 1 three lm_head sets and two activation sets, loaded three and two
+stages ahead; at TV = 3 two sets of both, two stages ahead); consumer waves
+0..3 take one stage per barrier and store each chunk's logits at its end.  A mistake in the range split, the clamped rows, the chunk swizzle, the
 slot alternation or the epilogue's row mapping gives wrong logits or reads
 outside lm_head.  This replay follows the kernel's index arithmetic and
 checks, for vocabularies, hidden sizes, batches and grid sizes the launcher
@@ -16,6 +17,8 @@ can produce:
 * every fragment a consumer lane reads from LDS holds the lm_head row and
   k piece (or the activation row and k piece) its product needs, from the
   stage of that barrier interval, and no slot is written while it is read;
+* a register set is reloaded only after the stage it held went to LDS,
+  and every put joins the lm_head rows and activations of one stage;
 * every load index stays inside lm_head and the hiddens;
 * producers and consumers pass the same number of barriers;
 * every (position, request, id) of the base logits is stored exactly once
@@ -23,6 +26,7 @@ can produce:
 """
 import os
 import re
+import sys
 
 import numpy as np
 import pytest
@@ -41,6 +45,18 @@ KMK = _constant("kMK")              # k per stage
 KMR = _constant("kMR")              # requests per group
 SMALL_BATCH = _constant("kRangeSmallBatch")
 T = 15                              # draft positions
+
+# The TV = 1 producer's six steps, as (activation set loaded, lm_head set
+# loaded, lm_head set put, activation set put, slot written), read from the
+# kernel's RANGE_STEP lines.
+def _steps_from_source():
+    src = open(SRC).read()
+    rows = re.findall(r"RANGE_STEP\((\d), X(\d), W(\d), W(\d), X(\d), (\d)\)", src)
+    assert [int(r[0]) for r in rows] == list(range(6)), rows
+    return [tuple(int(x) for x in r[1:]) for r in rows]
+
+
+TV1_STEPS = _steps_from_source()
 
 LANE = np.arange(64)
 RR, PP = LANE >> 3, LANE & 7
@@ -121,37 +137,92 @@ def replay(V, H, B, G, workgroups=None):
         nq = nchunk * ns
         stored = np.zeros((T + 1, B, rend - r0), np.int32)
 
-        def load(Q):
-            c_, s_ = divmod(min(Q, nq - 1), ns)
-            return (c_, s_), _stage_lds(V, H, B, TV, r0, rend, c_, s_)
+        # three lm_head register sets, two activation sets (six steps)
+        if TV == 1:
+            # three lm_head register sets, two activation sets (six steps)
+            def load(Q):
+                c_, s_ = divmod(min(Q, nq - 1), ns)
+                return Q, (c_, s_), _stage_lds(V, H, B, TV, r0, rend, c_, s_)
 
-        regs = {"A": load(0), "B": load(1)}
-        slots = [regs["A"], None]
-        bar_p = bar_c = 1
-        for q in range(0, nq, 2):
-            for cur, nxt, rslot in (("A", "B", 0), ("B", "A", 1)):
-                Q = q + (rslot == 1)
+            # register sets: lm_head rows of a stage in W0..W2, its activations in
+            # X0/X1; a set holds (logical stage, stage loaded after the clamp,
+            # its LDS image)
+            W = {0: load(0), 1: load(1), 2: load(2)}
+            X = {0: load(0), 1: load(1)}
+
+            def put(w, x):
+                (qw, sw, dw), (qx, sx, dx) = W[w], X[x]
+                assert qw == qx, f"lm_head of stage {qw} put with activations of stage {qx}"
+                return sw, (dw[0], dx[1])
+
+            slots = [put(0, 0), None]
+            bar_p = bar_c = 1
+            steps = TV1_STEPS
+            Q = 0
+            while Q < nq:
+                lx, lw, pw, px, wslot = steps[Q % 6]
+                # consumers: stage Q from slot Q % 2, then the chunk's epilogue
+                rslot = Q % 2
                 (c_, s_), data = slots[rslot]
                 assert (c_, s_) == divmod(Q, ns), f"slot {rslot} holds stage {(c_, s_)}, not {Q}"
                 _consume(data, V, B, TV, r0, rend, c_, s_)
-                regs[cur] = load(Q + 2)
-                wslot = 1 - rslot
-                assert wslot != rslot
-                slots[wslot] = regs[nxt]
+                if (Q + 1) % ns == 0:
+                    c = Q // ns
+                    for w4 in range(4):
+                        for tv in range(TV):
+                            for hh in range(2):
+                                v = r0 + c * kMV + w4 * TV * 32 + tv * 32 + np.arange(32)
+                                v = v[v < rend]
+                                for req in range(min(B, KMR)):
+                                    for ii in range(7):
+                                        stored[4 * hh + 8 * (ii >> 2) + (ii & 3), req, v - r0] += 1
+                                    if hh == 0:
+                                        stored[11, req, v - r0] += 1
+                # producers: a set is reloaded only once its stage is in LDS
+                # (stage s goes to LDS at step s - 1), never the set put now
+                assert lw != pw and lx != px
+                assert W[lw][0] <= Q and X[lx][0] <= Q, "register set reloaded before its stage was put"
+                X[lx] = load(Q + 2)
+                W[lw] = load(Q + 3)
+                assert W[pw][0] == Q + 1, "wrong stage put"
+                assert wslot != rslot and wslot == (Q + 1) % 2
+                slots[wslot] = put(pw, px)
                 bar_p += 1
                 bar_c += 1
-            if (q + 2) % ns == 0:                     # the chunk's epilogue
-                c = q // ns
-                for w4 in range(4):
-                    for tv in range(TV):
-                        for hh in range(2):
-                            v = r0 + c * kMV + w4 * TV * 32 + tv * 32 + np.arange(32)
-                            v = v[v < rend]
-                            for req in range(min(B, KMR)):
-                                for ii in range(7):
-                                    stored[4 * hh + 8 * (ii >> 2) + (ii & 3), req, v - r0] += 1
-                                if hh == 0:
-                                    stored[11, req, v - r0] += 1
+                Q += 1
+        else:
+            # two register sets
+            def load(Q):
+                c_, s_ = divmod(min(Q, nq - 1), ns)
+                return (c_, s_), _stage_lds(V, H, B, TV, r0, rend, c_, s_)
+
+            regs = {"A": load(0), "B": load(1)}
+            slots = [regs["A"], None]
+            bar_p = bar_c = 1
+            for q in range(0, nq, 2):
+                for cur, nxt, rslot in (("A", "B", 0), ("B", "A", 1)):
+                    Q = q + (rslot == 1)
+                    (c_, s_), data = slots[rslot]
+                    assert (c_, s_) == divmod(Q, ns), f"slot {rslot} holds stage {(c_, s_)}, not {Q}"
+                    _consume(data, V, B, TV, r0, rend, c_, s_)
+                    regs[cur] = load(Q + 2)
+                    wslot = 1 - rslot
+                    assert wslot != rslot
+                    slots[wslot] = regs[nxt]
+                    bar_p += 1
+                    bar_c += 1
+                if (q + 2) % ns == 0:                     # the chunk's epilogue
+                    c = q // ns
+                    for w4 in range(4):
+                        for tv in range(TV):
+                            for hh in range(2):
+                                v = r0 + c * kMV + w4 * TV * 32 + tv * 32 + np.arange(32)
+                                v = v[v < rend]
+                                for req in range(min(B, KMR)):
+                                    for ii in range(7):
+                                        stored[4 * hh + 8 * (ii >> 2) + (ii & 3), req, v - r0] += 1
+                                    if hh == 0:
+                                        stored[11, req, v - r0] += 1
         bar_p += 1
         bar_c += 1
         assert bar_p == bar_c == nq + 2
@@ -190,3 +261,22 @@ def test_replay_catches_a_wrong_swizzle(monkeypatch):
         broken = {k: v for k, v in W.items()}
         broken[(2, 1)] = broken[(2, 0)]   # piece moved to the unswizzled place
         _consume((broken, X), 37, 3, 1, 0, 37, 0, 1)
+
+
+def test_step_table_matches_the_rotation():
+    """The six steps read from the kernel load sets (Q + 2) % 2 and (Q + 3) % 3
+    and put sets (Q + 1) % 3 and (Q + 1) % 2 into slot (Q + 1) % 2."""
+    for i, (lx, lw, pw, px, slot) in enumerate(TV1_STEPS):
+        assert (lx, lw, pw, px, slot) == ((i + 2) % 2, (i + 3) % 3, (i + 1) % 3, (i + 1) % 2, (i + 1) % 2)
+
+
+@pytest.mark.parametrize("broken", [
+    [(0, 1, 1, 1, 1)] + TV1_STEPS[1:],                  # loads the lm_head set it puts
+    TV1_STEPS[:2] + [(0, 2, 1, 1, 1)] + TV1_STEPS[3:],  # puts a set holding another stage
+])
+def test_replay_catches_a_wrong_step_table(monkeypatch, broken):
+    """A step table that reloads a set before its stage reached LDS, or puts
+    the wrong set, fails the replay."""
+    monkeypatch.setattr(sys.modules[__name__], "TV1_STEPS", broken)
+    with pytest.raises(AssertionError):
+        replay(3001, 1024, 2, 94, [0])
