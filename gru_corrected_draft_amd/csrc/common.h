@@ -22,6 +22,7 @@ typedef uint16_t bf16_t;
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 #define DOMINO_T 15   // proposals per block (block size 16)
 #define DOMINO_S 14   // correction steps
