@@ -572,7 +572,7 @@ __device__ __forceinline__ void m32_products(const unsigned char* wsb, const uns
 // accumulators.  A lane holds positions 4 hh + {0, 1, 2, 3, 8, 9, 10, 11} of
 // its (request, id): one guarded run of stores at fixed position strides per
 // request, position 15 (the padding row, hh = 1) never stored.
-template <int TV>
+template <int TV, bool KEEP>
 __device__ __forceinline__ void range_epilogue(const FusedArgs& a, v16f (&acc)[4][TV], int vw,
                                                int rend, int vl, int hh,
                                                uint64_t (&best)[kMR]) {
@@ -601,13 +601,27 @@ __device__ __forceinline__ void range_epilogue(const FusedArgs& a, v16f (&acc)[4
         }
         const uint64_t k0 = pack_key(acc[ta][tv][jj * 8], (uint32_t)v);  // position 0 on hh == 0
         best[req] = (hh == 0 && vok) ? umax64(best[req], k0) : best[req];
-        if (ok) {  // non-temporal: the logits are not read back by this kernel (1-4 us at 8 requests)
+        // Full-vocabulary runs store the logits non-temporally: each
+        // correction step streams one whole row of them, and cached rows
+        // only displace fc2 (8B, 8 requests: LM-head 1-4 us faster, K0 block
+        // 1.131 against 1.145 ms cached).  A pool run (KEEP) reads them back
+        // only at its pool ids, which then hit the caches more often when the
+        // stores are cached (K = 2048 block 0.528 against 0.524 ms cached).
+        // The choice is a template parameter: with a runtime branch the
+        // compiler merged the two stores and dropped the non-temporal hint.
+        if (ok) {
           float* o = a.base + (size_t)req * V + v + (size_t)(4 * hh) * pstride;
+          if constexpr (KEEP) {
 #pragma unroll
-          for (int ii = 0; ii < 7; ++ii)
-            __builtin_nontemporal_store(acc[ta][tv][jj * 8 + ii],
-                                        &o[(size_t)(8 * (ii >> 2) + (ii & 3)) * pstride]);
-          if (hh == 0) __builtin_nontemporal_store(acc[ta][tv][jj * 8 + 7], &o[11 * pstride]);
+            for (int ii = 0; ii < 7; ++ii) o[(size_t)(8 * (ii >> 2) + (ii & 3)) * pstride] = acc[ta][tv][jj * 8 + ii];
+            if (hh == 0) o[11 * pstride] = acc[ta][tv][jj * 8 + 7];
+          } else {
+#pragma unroll
+            for (int ii = 0; ii < 7; ++ii)
+              __builtin_nontemporal_store(acc[ta][tv][jj * 8 + ii],
+                                          &o[(size_t)(8 * (ii >> 2) + (ii & 3)) * pstride]);
+            if (hh == 0) __builtin_nontemporal_store(acc[ta][tv][jj * 8 + 7], &o[11 * pstride]);
+          }
         }
       }
 #pragma unroll
@@ -635,7 +649,7 @@ __device__ __forceinline__ void range_epilogue(const FusedArgs& a, v16f (&acc)[4
 // first row, an L2 hit, instead of branching around the load.  Each
 // consumer lane keeps its position-0 maxima across chunks; the workgroup
 // publishes one word per request at the end.
-template <int TV>
+template <int TV, bool KEEP>
 __global__ __launch_bounds__(512) void lmhead_range_kernel(FusedArgs a) {
   using C = M32<TV>;
   constexpr int kMV = C::kMV, kMVStage = C::kVStage, kMVCopies = C::kVCopies;
@@ -791,7 +805,8 @@ __global__ __launch_bounds__(512) void lmhead_range_kernel(FusedArgs a) {
         m32_products<TV>(wsb + kMVStage, xsb + kMXStage, fhi, fsw, acc);
         __syncthreads();
       }
-      range_epilogue<TV>(a, acc, r0 + c * kMV + w4 * (TV * 32), rend, lane & 31, lane >> 5, best);
+      range_epilogue<TV, KEEP>(a, acc, r0 + c * kMV + w4 * (TV * 32), rend, lane & 31, lane >> 5,
+                               best);
     }
 #pragma unroll
     for (int r = 0; r < kMR; ++r) {
@@ -1060,9 +1075,13 @@ void lmhead_fused_prepare() {
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)M32<2>::kLds);
   (void)hipFuncSetAttribute((const void*)lmhead_m32_kernel<1>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)M32<1>::kLds);
-  (void)hipFuncSetAttribute((const void*)lmhead_range_kernel<1>,
+  (void)hipFuncSetAttribute((const void*)lmhead_range_kernel<1, false>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRangeLds<1>);
-  (void)hipFuncSetAttribute((const void*)lmhead_range_kernel<3>,
+  (void)hipFuncSetAttribute((const void*)lmhead_range_kernel<1, true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRangeLds<1>);
+  (void)hipFuncSetAttribute((const void*)lmhead_range_kernel<3, false>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRangeLds<3>);
+  (void)hipFuncSetAttribute((const void*)lmhead_range_kernel<3, true>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kRangeLds<3>);
   (void)hipFuncSetAttribute((const void*)lmhead_fused_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
@@ -1111,10 +1130,14 @@ void launch_lmhead_fused(const FusedArgs& a, hipStream_t st) {
     const int ngrp = (a.B + kMR - 1) / kMR;
     if (a.B <= kMR && lmhead_range_supported(a.H)) {
       const int grid = min((a.V + 31) / 32, cu_count());
-      if (a.B <= kRangeSmallBatch)
-        DLAUNCH(lmhead_range_kernel<1>, dim3(grid), dim3(512), kRangeLds<1>, st, a);
-      else
-        DLAUNCH(lmhead_range_kernel<3>, dim3(grid), dim3(512), kRangeLds<3>, st, a);
+      // the logits are kept in the caches when a pool reads them back
+      if (a.B <= kRangeSmallBatch) {
+        if (a.keys) DLAUNCH((lmhead_range_kernel<1, true>), dim3(grid), dim3(512), kRangeLds<1>, st, a);
+        else DLAUNCH((lmhead_range_kernel<1, false>), dim3(grid), dim3(512), kRangeLds<1>, st, a);
+      } else {
+        if (a.keys) DLAUNCH((lmhead_range_kernel<3, true>), dim3(grid), dim3(512), kRangeLds<3>, st, a);
+        else DLAUNCH((lmhead_range_kernel<3, false>), dim3(grid), dim3(512), kRangeLds<3>, st, a);
+      }
     } else if (a.B <= kM32SmallBatch) {
       const int nvt = (a.V + M32<1>::kMV - 1) / M32<1>::kMV;
       DLAUNCH(lmhead_m32_kernel<1>, dim3(8 * ((nvt + 7) / 8) * ngrp), dim3(256), M32<1>::kLds, st,
